@@ -1,0 +1,204 @@
+/*
+ * sckv.h -- C ABI of the MI355X (gfx950) compressed sparse attention hot path.
+ *
+ * The operations come from three web pages of a DeepSeek-V4.1-style model:
+ *   "metrale_model_arch/deepseek_v41_ref/compress.rs"  (compress.rs)
+ *   "metrale_model_arch/attn_v41/forward.rs"            (forward.rs)
+ *   "metrale_model_arch/deepseek_v41_layer.rs"          (layer.rs; context only)
+ *
+ * Conventions shared by every call:
+ *   - Tensors are caller-owned, contiguous, row-major DEVICE memory unless a
+ *     stride argument says otherwise.  bf16 tensors are passed as void* and
+ *     hold bf16 bit patterns; indices are int32; f32 is float.
+ *   - B is a leading batch of independent sequences with identical shapes
+ *     (B = 1 is one sequence, as on the pages).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream; none allocates device memory,
+ *     synchronises or keeps state between calls.  Faults inside a kernel show
+ *     up at the caller's next synchronisation.
+ *   - Arguments are checked on the host before anything is enqueued; on a
+ *     failed check nothing is enqueued, the call returns a negative status and
+ *     sckv_last_error() describes it (the pages' ensure!/context checks).
+ *   - Return values: SCKV_OK (0) or one of the negative codes below.
+ */
+#ifndef SCKV_H_
+#define SCKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sckv_status {
+    SCKV_OK = 0,
+    SCKV_EINVAL = -1,       /* bad shape, null pointer, bad mode, misaligned pointer */
+    SCKV_EUNSUPPORTED = -2, /* a valid shape this build has no kernel for (see each call) */
+    SCKV_EHIP = -3,         /* the HIP runtime refused a launch */
+    SCKV_EWORKSPACE = -4    /* workspace pointer NULL or smaller than sckv_workspace_bytes() */
+};
+
+/* fp4 round-trip modes (compress.rs: fp4_quant_e4m3_inplace / fp4_quant_e8m0_inplace). */
+enum sckv_quant_mode {
+    SCKV_FP4_E4M3_B16 = 0, /* compressed KV latent: e4m3 block scales, 16 values a block */
+    SCKV_FP4_E8M0_B32 = 1  /* indexer q and k: power-of-two block scales, 32 values a block */
+};
+
+/* Operations whose workspace size sckv_workspace_bytes() reports. */
+enum sckv_op {
+    SCKV_OP_INDEX_SCORES_TOPK = 0,
+    SCKV_OP_SPARSE_ATTN_SINK = 1
+};
+
+/*
+ * sckv_quant -- the fp4 (e2m1) round trip of a flat bf16 array, in blocks of
+ * 16 (E4M3_B16) or 32 (E8M0_B32) consecutive values (compress.rs:
+ * fp4_quant_e4m3_inplace, fp4_quant_e8m0_inplace; forward.rs: the fp4_quant
+ * call on the new latent groups before the cache copy).
+ * For each block: amax = max |v|, floored at 6*2^-9 (E4M3) or 6*2^-126 (E8M0);
+ * s = e4m3_rne(amax/6) (saturating at 448) or the power-of-two ceiling of
+ * amax/6; every v becomes bf16(e2m1_rne(clamp(v/s, -6, 6)) * s), where v/s is
+ * the correctly rounded binary32 quotient and e2m1_rne rounds to the nearest
+ * of {0,.5,1,1.5,2,3,4,6} with ties to the even code and keeps the sign.
+ *   x, y   [n] bf16 device arrays; x == y (in place) is allowed, any other
+ *          overlap is not.
+ *   n      number of values; must be a multiple of the block (16 or 32), else
+ *          SCKV_EINVAL.  n == 0 is a no-op.
+ *   mode   enum sckv_quant_mode.
+ */
+int sckv_quant(const void* x, void* y, int64_t n, int mode, void* stream);
+
+/*
+ * sckv_quant_rows -- the same round trip over `rows` rows of `cols` values
+ * with row strides ldx / ldy (in elements), e.g. one new cache row in each of
+ * B sequences.  cols must be a multiple of the block; blocks never cross rows.
+ * In place (x == y, ldx == ldy) is allowed.
+ */
+int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols, int mode,
+                    void* stream);
+
+/*
+ * sckv_ring_write -- write this step's m kv rows into the window ring: the row
+ * of position p goes to slot p mod win; only the last min(m, win) positions
+ * are written (forward.rs: the ring's one or two stream-ordered copies at
+ * start_pos 0, the single-row copy at slot start_pos mod win otherwise).
+ *   rows  [B, m, D] bf16 with batch stride rows_bstride (elements)
+ *   ring  [B, win, D] bf16 with batch stride ring_bstride (elements)
+ * The two regions must not overlap (the chunked layout [ring | chunk] in one
+ * buffer, rows = buffer + win*D, satisfies this).
+ */
+int sckv_ring_write(const void* rows, int64_t rows_bstride, void* ring, int64_t ring_bstride, int B, int64_t m,
+                    int64_t start_pos, int win, int D, void* stream);
+
+/*
+ * sckv_rows_a_len -- length of rows_a, the first row base of a step (the
+ * compressed rows' index offset, forward.rs `offset = rows_a_len`):
+ *   start_pos == 0        m        (rows_a = this step's fresh kv rows)
+ *   m == 1, start_pos > 0 win      (rows_a = the ring, after the new row's write)
+ *   m > 1,  start_pos > 0 win + m  (rows_a = the ring before the chunk, then
+ *                                   the m chunk rows; an extension: the pages
+ *                                   copy a single row at start_pos > 0)
+ * Host-only, no device work.  Returns -1 for invalid arguments.
+ */
+int64_t sckv_rows_a_len(int win, int64_t m, int64_t start_pos);
+
+/*
+ * sckv_window_idx -- the window part of every query's index list (forward.rs:
+ * window_topk_idxs, whose body is not printed; the reading used here): for the
+ * query at position p the rows_a indices of positions max(0, p-win+1) .. p,
+ * oldest first, then -1 up to win entries.  rows_a is laid out as
+ * sckv_rows_a_len() describes.
+ *   idx  [B, m, ld] int32; columns 0 .. win-1 are written (same for every b).
+ *   ld >= win.
+ */
+int sckv_window_idx(int B, int64_t m, int64_t start_pos, int win, int32_t* idx, int64_t ld, void* stream);
+
+/*
+ * sckv_visible_idx -- the compressed part of every query's index list when
+ * every causally visible compressed row is attended (a layer without an
+ * indexer): offset + j for j < V_p, then -1 up to K, where compressed row j is
+ * visible to position p iff (j+1)*ratio <= p+1 and j < n_c (forward.rs:
+ * compress_len = (start_pos+m)/ratio).
+ *   idx  [B, m, ld] int32; columns col0 .. col0+K-1 are written.
+ *   K must be >= every V_p of the step (else SCKV_EINVAL).
+ */
+int sckv_visible_idx(int B, int64_t m, int64_t start_pos, int ratio, int64_t n_c, int K, int32_t offset,
+                     int32_t* idx, int64_t ld, int64_t col0, void* stream);
+
+/*
+ * sckv_index_scores_topk -- indexer scores of every query against its visible
+ * compressed rows, then a per-query top-K (forward.rs: the indexer call and
+ * the [window | compressed] merge; compress.rs module doc: q and k go through
+ * the fp4 round trip with power-of-two scales in blocks of 32, and scores are
+ * bf16 values).  The scoring formula is not printed on the pages; the reading
+ * implemented is the lightning-indexer form:
+ *   q_hat[t,h]  = E8M0_B32 round trip of the raw q[t,h,:] (fused; bit-identical
+ *                 to sckv_quant on q),
+ *   d[t,h,s]    = q_hat[t,h,:] . k[s,:], accumulated in binary32 (exact for
+ *                 round-tripped N(0,1)-scale data; see the exactness note),
+ *   r[t,h,s]    = fl32(w[t,h] * (d > 0 ? d : +0)),
+ *   score[t,s]  = bf16_rne of the pairwise head sum, strides Hi/2, .., 1.
+ * Top-K: the K_t = min(K, V_t) visible rows with the largest scores (-0 equals
+ * +0), ties to the lower row; written as offset + s in ascending s into
+ * columns col0 .. col0+K_t-1 of idx, then -1 up to K.  V_t = 0 writes K x -1.
+ *   q        [B, m, Hi, Di] bf16, raw (before the round trip)
+ *   k        [B, n_c, Di] bf16, already round-tripped (E8M0_B32)
+ *   w        [B, m, Hi] f32 per-head weights
+ *   idx      [B, m, ld] int32
+ *   scores   optional [B, m, n_c] bf16 output of the scores (NULL = none);
+ *            entries of invisible rows are left unchanged.
+ *   ws       device workspace of at least
+ *            sckv_workspace_bytes(SCKV_OP_INDEX_SCORES_TOPK, B, m, Hi, Di, n_c).
+ * Supported: Hi a power of two <= 64, Di in {32, 64, 128, 256}, n_c < 2^31.
+ * Exactness note: the binary32 dot equals the exact dot whenever the exact
+ * value is a binary32 value, which holds when the 2*Di products' block scales
+ * lie within a few powers of two of each other (always the case for
+ * round-tripped data of one magnitude); then every bit matches the oracle.
+ */
+int sckv_index_scores_topk(const void* q, const void* k, const float* w, int B, int64_t m, int Hi, int Di,
+                           int64_t n_c, int ratio, int64_t start_pos, int K, int32_t offset, int32_t* idx,
+                           int64_t ld, int64_t col0, void* scores, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sckv_sparse_attn_sink -- sparse MQA attention over the rows named by each
+ * query's index list, with a per-head sink logit (compress.rs attention_any:
+ * the sparse_attn call with scale = head_dim^-1/2, the kv rows being the
+ * window rows followed by the compressed rows; forward.rs attend_and_project:
+ * two row bases rows_a / rows_b addressed through one index list).  For query
+ * t and head h: entry i of idx[t] names rows_a[idx] when idx < ra, else
+ * rows_b[idx - ra]; -1 (and any value outside [0, ra+rb)) is skipped.  Each
+ * row is both key and value.  With l_i = scale * q[t,h,:] . row_i:
+ *   out[t,h,:] = sum_i e^(l_i - M) row_i / (e^(sink_h - M) + sum_i e^(l_i - M)),
+ * M = max(sink_h, max_i l_i); no valid entry gives 0.  f32 accumulation,
+ * bf16 output.
+ *   q      [B, m, H, D] bf16
+ *   rows_a [B, ra, D] bf16     rows_b [B, rb, D] bf16 (NULL allowed when rb == 0)
+ *   idx    [B, m, T] int32     sink [H] f32     out [B, m, H, D] bf16
+ *   ws     device workspace of at least
+ *          sckv_workspace_bytes(SCKV_OP_SPARSE_ATTN_SINK, B, m, H, D, T).
+ * Supported: H <= 64, D in {64, 128, 256, 512}, 1 <= T <= 65536.
+ */
+int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
+                          const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m, int H, int D,
+                          void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sckv_workspace_bytes -- device workspace an operation needs for the given
+ * shape: op = SCKV_OP_INDEX_SCORES_TOPK with (H, D, n) = (Hi, Di, n_c), or
+ * SCKV_OP_SPARSE_ATTN_SINK with (H, D, n) = (H, D, T).  0 means none needed.
+ * Returns (size_t)-1 for invalid arguments.
+ */
+size_t sckv_workspace_bytes(int op, int B, int64_t m, int H, int D, int64_t n);
+
+/* Thread-local description of the last failed call on this thread ("" if none). */
+const char* sckv_last_error(void);
+
+/* ABI version of this header: 1. */
+int sckv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCKV_H_ */

@@ -1,0 +1,172 @@
+"""ctypes binding of libsckv.so: the C ABI's calls under the same names.
+
+Argument marshalling only (torch tensor -> device pointer, current HIP stream,
+status -> exception).  Every step of the computation runs in the library's
+HIP kernels; there is no CPU path.  If the library is missing the import
+fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsckv.so")
+
+SCKV_OK = 0
+SCKV_EINVAL = -1
+SCKV_EUNSUPPORTED = -2
+SCKV_EHIP = -3
+SCKV_EWORKSPACE = -4
+
+SCKV_FP4_E4M3_B16 = 0
+SCKV_FP4_E8M0_B32 = 1
+
+SCKV_OP_INDEX_SCORES_TOPK = 0
+SCKV_OP_SPARSE_ATTN_SINK = 1
+
+
+class SckvError(RuntimeError):
+    def __init__(self, call: str, code: int, msg: str):
+        super().__init__(f"{call} failed ({code}): {msg}")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.sckv_quant.argtypes = [vp, vp, i64, i32, vp]
+    L.sckv_quant_rows.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]
+    L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
+    L.sckv_rows_a_len.argtypes = [i32, i64, i64]
+    L.sckv_rows_a_len.restype = i64
+    L.sckv_window_idx.argtypes = [i32, i64, i64, i32, vp, i64, vp]
+    L.sckv_visible_idx.argtypes = [i32, i64, i64, i32, i64, i32, ctypes.c_int32, vp, i64, i64, vp]
+    L.sckv_index_scores_topk.argtypes = [vp, vp, vp, i32, i64, i32, i32, i64, i32, i64, i32, ctypes.c_int32, vp,
+                                         i64, i64, vp, vp, sz, vp]
+    L.sckv_sparse_attn_sink.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32, vp,
+                                        vp, sz, vp]
+    L.sckv_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i64]
+    L.sckv_workspace_bytes.restype = sz
+    L.sckv_last_error.argtypes = []
+    L.sckv_last_error.restype = ctypes.c_char_p
+    L.sckv_abi_version.argtypes = []
+    for name in ("sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_window_idx", "sckv_visible_idx",
+                 "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_abi_version"):
+        getattr(L, name).restype = ctypes.c_int
+    return L
+
+
+lib = _load()
+
+
+def _check(call: str, rc: int):
+    if rc != SCKV_OK:
+        raise SckvError(call, rc, sckv_last_error())
+
+
+def _ptr(t: torch.Tensor | None, dtype=None, name: str = "") -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def sckv_last_error() -> str:
+    return lib.sckv_last_error().decode()
+
+
+def sckv_abi_version() -> int:
+    return lib.sckv_abi_version()
+
+
+def sckv_workspace_bytes(op: int, B: int, m: int, H: int, D: int, n: int) -> int:
+    return lib.sckv_workspace_bytes(op, B, m, H, D, n)
+
+
+def workspace(op: int, B: int, m: int, H: int, D: int, n: int, device="cuda") -> torch.Tensor:
+    """A device byte buffer of the size the library asks for (plumbing only)."""
+    nbytes = sckv_workspace_bytes(op, B, m, H, D, n)
+    if nbytes == ctypes.c_size_t(-1).value:
+        raise SckvError("sckv_workspace_bytes", SCKV_EINVAL, "invalid arguments")
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def sckv_quant(x: torch.Tensor, y: torch.Tensor, mode: int, stream=None):
+    if x.numel() != y.numel():
+        raise ValueError("sckv_quant: x and y sizes differ")
+    _check("sckv_quant", lib.sckv_quant(_ptr(x, torch.bfloat16, "x"), _ptr(y, torch.bfloat16, "y"), x.numel(), mode,
+                                        _stream(stream)))
+
+
+def sckv_quant_rows(x: torch.Tensor, ldx: int, y: torch.Tensor, ldy: int, rows: int, cols: int, mode: int,
+                    stream=None):
+    """x / y: any bf16 device tensors whose data pointers start the first row."""
+    for t, n in ((x, "x"), (y, "y")):
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n}: expected a bf16 device tensor")
+    _check("sckv_quant_rows", lib.sckv_quant_rows(x.data_ptr(), ldx, y.data_ptr(), ldy, rows, cols, mode,
+                                                  _stream(stream)))
+
+
+def sckv_ring_write(rows: torch.Tensor, rows_bstride: int, ring: torch.Tensor, ring_bstride: int, B: int, m: int,
+                    start_pos: int, win: int, D: int, stream=None):
+    for t, n in ((rows, "rows"), (ring, "ring")):
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n}: expected a bf16 device tensor")
+    _check("sckv_ring_write", lib.sckv_ring_write(rows.data_ptr(), rows_bstride, ring.data_ptr(), ring_bstride, B, m,
+                                                  start_pos, win, D, _stream(stream)))
+
+
+def sckv_rows_a_len(win: int, m: int, start_pos: int) -> int:
+    return lib.sckv_rows_a_len(win, m, start_pos)
+
+
+def sckv_window_idx(B: int, m: int, start_pos: int, win: int, idx: torch.Tensor, ld: int, stream=None):
+    _check("sckv_window_idx", lib.sckv_window_idx(B, m, start_pos, win, _ptr(idx, torch.int32, "idx"), ld,
+                                                  _stream(stream)))
+
+
+def sckv_visible_idx(B: int, m: int, start_pos: int, ratio: int, n_c: int, K: int, offset: int, idx: torch.Tensor,
+                     ld: int, col0: int, stream=None):
+    _check("sckv_visible_idx", lib.sckv_visible_idx(B, m, start_pos, ratio, n_c, K, offset,
+                                                    _ptr(idx, torch.int32, "idx"), ld, col0, _stream(stream)))
+
+
+def sckv_index_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, B: int, m: int, Hi: int, Di: int,
+                           n_c: int, ratio: int, start_pos: int, K: int, offset: int, idx: torch.Tensor, ld: int,
+                           col0: int, scores: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                           stream=None):
+    if ws is None:
+        ws = workspace(SCKV_OP_INDEX_SCORES_TOPK, B, m, Hi, Di, n_c, device=idx.device)
+    _check("sckv_index_scores_topk", lib.sckv_index_scores_topk(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(w, torch.float32, "w"), B, m, Hi, Di, n_c,
+        ratio, start_pos, K, offset, _ptr(idx, torch.int32, "idx"), ld, col0, _ptr(scores, torch.bfloat16, "scores"),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sckv_sparse_attn_sink(q: torch.Tensor, rows_a: torch.Tensor, ra: int, rows_b: torch.Tensor | None, rb: int,
+                          idx: torch.Tensor, T: int, sink: torch.Tensor, scale: float, B: int, m: int, H: int, D: int,
+                          out: torch.Tensor, ws: torch.Tensor | None = None, stream=None):
+    if ws is None:
+        ws = workspace(SCKV_OP_SPARSE_ATTN_SINK, B, m, H, D, T, device=out.device)
+    _check("sckv_sparse_attn_sink", lib.sckv_sparse_attn_sink(
+        _ptr(q, torch.bfloat16, "q"), _ptr(rows_a, torch.bfloat16, "rows_a"), ra,
+        _ptr(rows_b, torch.bfloat16, "rows_b"), rb, _ptr(idx, torch.int32, "idx"), T,
+        _ptr(sink, torch.float32, "sink"), float(scale), B, m, H, D, _ptr(out, torch.bfloat16, "out"),
+        _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))

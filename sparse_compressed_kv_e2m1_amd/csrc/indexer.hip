@@ -1,0 +1,359 @@
+// indexer.hip -- indexer scores of every query against its visible compressed
+// rows (MFMA contraction, fused q round trip, fixed pairwise head sum) and the
+// per-query top-K (two-pass byte radix select, then an ordered compaction).
+//
+// Pages: "metrale_model_arch/deepseek_v41_ref/compress.rs" (module doc: q and
+// k through the e2m1 round trip with power-of-two scales in blocks of 32,
+// scores are bf16 values) and "metrale_model_arch/attn_v41/forward.rs" (the
+// indexer call with offset = rows_a's length, compress_len, the merge of the
+// window and compressed lists).  The head combination is the lightning-indexer
+// reading: score = bf16(pairwise sum over h of fl32(w[t,h] * relu(q_hat.k))).
+//
+// Score kernel.  One wave = one query x tiles of 32 compressed rows; heads are
+// the MFMA M dimension (32 or 64 rows of A), rows the N dimension, the
+// indexer head dim the K dimension.  q_hat lives in registers in A layout;
+// k rows are read straight from HBM in B layout (16 bytes per lane per
+// k-step).  All products are exact and, for round-tripped data, every partial
+// sum is a binary32 value, so the MFMA accumulation order does not matter.
+// The head sum follows the fixed pairwise order (stride Hi/2 first): in the D
+// tile layout strides 32, 16, 8, 2 and 1 stay inside a lane and stride 4 is
+// the lane^32 exchange.
+#include "mfma.h"
+#include "sckv_device.h"
+
+namespace sckv {
+namespace {
+
+constexpr int SCORE_WAVES = 4;
+constexpr int TOPK_THREADS = 512;
+
+// Ordered 16-bit key of a bf16 score: -0 counts as +0; a larger key is a
+// larger score.
+__device__ __forceinline__ uint32_t score_key(uint32_t b) {
+    if (b == 0x8000u) b = 0u;
+    return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
+}
+
+template <int MT, int DI>
+__global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w, int64_t m, int Hi,
+    int64_t n_c, int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys,
+    uint16_t* __restrict__ scores) {
+    constexpr int KS = DI / 16;  // k-steps
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t qi = blockIdx.x / nsplit;
+    const int split = (int)(blockIdx.x - qi * nsplit);
+    const int64_t b = qi / m;
+    const int64_t t = qi - b * m;
+
+    int64_t vis = (start_pos + t + 1) / ratio;
+    vis = vis < n_c ? vis : n_c;
+    const int64_t row0 = (int64_t)split * rows_per_wg;
+    if (row0 >= vis) return;
+    int64_t row_end = row0 + rows_per_wg;
+    row_end = row_end < vis ? row_end : vis;
+
+    // ---- q_hat in A layout: head mt*32 + lane%32, dims ks*16 + (lane/32)*8 + 0..7
+    const uint16_t* qrow = q + qi * (int64_t)Hi * DI;
+    bf16x8 qa[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int h = mt * 32 + (lane & 31);
+        u32x4 raw[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            raw[ks] = (h < Hi) ? load16(qrow + (int64_t)h * DI + ks * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+        }
+        // E8M0_B32 blocks: dims [32c, 32c+32) = k-steps 2c and 2c+1 of this lane
+        // and of lane^32.
+#pragma unroll
+        for (int c = 0; c < KS / 2; ++c) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t v = raw[2 * c + kk][e];
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v & 0xffffu)));
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v >> 16)));
+                }
+            amax = fmaxf(amax, shfl_xor32(amax));
+            const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    uint32_t v = raw[2 * c + kk][e];
+                    uint32_t lo = fp4_value_bits(bf16_bits_to_f32(v & 0xffffu), s);
+                    uint32_t hi = fp4_value_bits(bf16_bits_to_f32(v >> 16), s);
+                    raw[2 * c + kk][e] = lo | (hi << 16);
+                }
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[mt][ks] = as_bf16x8(raw[ks]);
+    }
+
+    // ---- head weights in D layout: head mt*32 + d_row(i, lane)
+    float wd[MT][16];
+    const float* wrow = w + qi * (int64_t)Hi;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = mt * 32 + d_row(i, lane);
+            wd[mt][i] = (h < Hi) ? wrow[h] : 0.0f;
+        }
+
+    const uint16_t* kb = k + b * n_c * DI;
+    uint16_t* kout = keys + qi * n_c;
+    uint16_t* sout = scores ? scores + qi * n_c : nullptr;
+
+    for (int64_t s0 = row0 + (int64_t)wave * 32; s0 < row_end; s0 += SCORE_WAVES * 32) {
+        const int64_t s = s0 + (lane & 31);
+        u32x4 kr[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            kr[ks] = (s < n_c) ? load16(kb + s * DI + ks * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+        f32x16 acc[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            acc[mt] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma32x32x16(qa[mt][ks], as_bf16x8(kr[ks]), acc[mt]);
+        }
+        // r_h = fl32(w_h * relu(d_h)); relu maps every d <= 0 (and -0) to +0
+        float v[MT * 16];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float d = acc[mt][i];
+                v[mt * 16 + i] = wd[mt][i] * ((d > 0.0f) ? d : 0.0f);
+            }
+        // pairwise head sum, stride Hi/2 first (h and h + stride)
+        if (MT == 2 && Hi > 32) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = v[i] + v[16 + i];
+        }
+        if (Hi > 16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = v[i] + v[i + 8];
+        }
+        if (Hi > 8) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = v[i] + v[i + 4];
+        }
+        if (Hi > 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = v[i] + shfl_xor32(v[i]);
+        }
+        if (Hi > 2) {
+            v[0] = v[0] + v[2];
+            v[1] = v[1] + v[3];
+        }
+        if (Hi > 1) v[0] = v[0] + v[1];
+        if (lane < 32 && s < row_end) {
+            const uint32_t bits = f32_to_bf16_bits(v[0]);
+            kout[s] = (uint16_t)score_key(bits);
+            if (sout) sout[s] = (uint16_t)bits;
+        }
+    }
+}
+
+// ---- block-wide scans (LDS, Hillis-Steele), all threads of the block call them
+
+// Inclusive prefix sum over the block's threads of `x`; `buf` holds blockDim.x words.
+__device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* buf) {
+    const int tid = threadIdx.x;
+    buf[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+        uint32_t add = (tid >= off) ? buf[tid - off] : 0u;
+        __syncthreads();
+        buf[tid] += add;
+        __syncthreads();
+    }
+    uint32_t r = buf[tid];
+    __syncthreads();
+    return r;
+}
+
+// Given a 256-bin histogram in hist and a target count `need` (>= 1, <= total),
+// find the bin b such that (# in bins > b) < need <= (# in bins >= b).  Returns
+// b and writes the count strictly above b into *above.  Uses threads 0..255 of
+// the block for the scan; every thread calls it.
+__device__ int find_threshold_bin(const uint32_t* hist, uint32_t need, uint32_t* buf, uint32_t* shared_out,
+                                  uint32_t* above) {
+    const int tid = threadIdx.x;
+    // reversed so the prefix over i is the suffix over bins 255 - i .. 255
+    uint32_t x = (tid < 256) ? hist[255 - tid] : 0u;
+    uint32_t incl = block_inclusive_scan(x, buf);
+    uint32_t excl = incl - x;
+    if (tid < 256 && incl >= need && excl < need) {
+        shared_out[0] = 255 - tid;
+        shared_out[1] = excl;
+    }
+    __syncthreads();
+    int bin = (int)shared_out[0];
+    *above = shared_out[1];
+    __syncthreads();
+    return bin;
+}
+
+// One block per query: select the K largest keys among rows 0 .. vis-1 (ties
+// to the lower row) and write offset + row in ascending row order.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const uint16_t* __restrict__ keys, int64_t n_c,
+                                                            int64_t m, int ratio, int64_t start_pos, int K,
+                                                            int32_t offset, int32_t* __restrict__ idx, int64_t ld,
+                                                            int64_t col0) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t buf[TOPK_THREADS];
+    __shared__ uint32_t sh[2];
+    const int tid = threadIdx.x;
+    const int64_t qi = blockIdx.x;
+    const int64_t t = qi % m;
+    int64_t vis = (start_pos + t + 1) / ratio;
+    vis = vis < n_c ? vis : n_c;
+    int32_t* out = idx + qi * ld + col0;
+    const uint16_t* kp = keys + qi * n_c;
+
+    if (tid < 2) sh[tid] = 0u;
+    if (vis <= K) {
+        for (int j = tid; j < K; j += TOPK_THREADS) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
+        return;
+    }
+    // pass 1: high byte
+    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t s = tid; s < vis; s += TOPK_THREADS) atomicAdd(&hist[kp[s] >> 8], 1u);
+    __syncthreads();
+    uint32_t above1;
+    const int b1 = find_threshold_bin(hist, (uint32_t)K, buf, sh, &above1);
+    // pass 2: low byte among keys with high byte b1
+    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0u;
+    __syncthreads();
+    for (int64_t s = tid; s < vis; s += TOPK_THREADS) {
+        uint32_t key = kp[s];
+        if ((int)(key >> 8) == b1) atomicAdd(&hist[key & 0xffu], 1u);
+    }
+    __syncthreads();
+    uint32_t above0;
+    const int b0 = find_threshold_bin(hist, (uint32_t)K - above1, buf, sh, &above0);
+    const uint32_t tau = ((uint32_t)b1 << 8) | (uint32_t)b0;
+    const uint32_t need_eq = (uint32_t)K - above1 - above0;  // >= 1
+
+    // ordered compaction: thread tid owns rows [tid*seg, (tid+1)*seg)
+    const int64_t seg = (vis + TOPK_THREADS - 1) / TOPK_THREADS;
+    const int64_t lo = (int64_t)tid * seg;
+    const int64_t hi = (lo + seg < vis) ? lo + seg : vis;
+    uint32_t gt = 0, eq = 0;
+    for (int64_t s = lo; s < hi; ++s) {
+        uint32_t key = kp[s];
+        gt += key > tau;
+        eq += key == tau;
+    }
+    const uint32_t eq_incl = block_inclusive_scan(eq, buf);
+    const uint32_t eq_base = eq_incl - eq;
+    uint32_t take_eq = (need_eq > eq_base) ? (need_eq - eq_base) : 0u;
+    take_eq = take_eq < eq ? take_eq : eq;
+    const uint32_t sel = gt + take_eq;
+    const uint32_t sel_incl = block_inclusive_scan(sel, buf);
+    uint32_t pos = sel_incl - sel;
+    uint32_t eq_seen = 0;
+    for (int64_t s = lo; s < hi; ++s) {
+        uint32_t key = kp[s];
+        bool take = key > tau;
+        if (key == tau) {
+            take = eq_seen < take_eq;
+            ++eq_seen;
+        }
+        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s);
+    }
+}
+
+template <int MT, int DI>
+void launch_scores(const uint16_t* q, const uint16_t* k, const float* w, int64_t nq, int64_t m, int Hi, int64_t n_c,
+                   int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* keys, uint16_t* scores,
+                   hipStream_t stream) {
+    index_score_kernel<MT, DI><<<dim3((unsigned)(nq * nsplit)), dim3(SCORE_WAVES * 64), 0, stream>>>(
+        q, k, w, m, Hi, n_c, ratio, start_pos, rows_per_wg, nsplit, keys, scores);
+}
+
+// Rows per workgroup: a multiple of 128 (4 waves x 32 rows), small enough
+// that the launch has about 1024 workgroups when the queries alone do not.
+int score_rows_per_wg(int64_t nq, int64_t n_c) {
+    int64_t tiles = (n_c + 127) / 128;  // 128-row tiles of one query
+    int64_t want_splits = (1024 + nq - 1) / nq;
+    if (want_splits > tiles) want_splits = tiles;
+    if (want_splits < 1) want_splits = 1;
+    int64_t tiles_per = (tiles + want_splits - 1) / want_splits;
+    return (int)(tiles_per * 128);
+}
+
+}  // namespace
+
+size_t index_workspace_bytes(int B, int64_t m, int64_t n_c) {
+    // one 16-bit key per (query, compressed row), 256-byte aligned
+    const size_t bytes = (size_t)B * (size_t)m * (size_t)n_c * 2u;
+    return (bytes + 255u) & ~(size_t)255u;
+}
+
+}  // namespace sckv
+
+extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float* w, int B, int64_t m, int Hi, int Di,
+                                      int64_t n_c, int ratio, int64_t start_pos, int K, int32_t offset,
+                                      int32_t* idx, int64_t ld, int64_t col0, void* scores, void* ws,
+                                      size_t ws_bytes, void* stream) {
+    using namespace sckv;
+    if (B < 0 || m < 0 || n_c < 0 || ratio <= 0 || start_pos < 0 || K < 0 || col0 < 0 || offset < 0)
+        return fail(SCKV_EINVAL, "sckv_index_scores_topk: bad sizes");
+    if (Hi <= 0 || (Hi & (Hi - 1)) != 0) return fail(SCKV_EINVAL, "sckv_index_scores_topk: Hi must be a power of two");
+    if (Hi > 64) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: Hi > 64");
+    if (Di != 32 && Di != 64 && Di != 128 && Di != 256)
+        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: Di not in {32, 64, 128, 256}");
+    if (B == 0 || m == 0 || K == 0) return SCKV_OK;
+    if (!idx) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null idx");
+    if (ld < col0 + K) return fail(SCKV_EINVAL, "sckv_index_scores_topk: ld < col0 + K");
+    if (n_c >= 0x7fffffffLL || (int64_t)offset + n_c > 0x7fffffffLL)
+        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: offset + n_c >= 2^31");
+    const int64_t nq = (int64_t)B * m;
+    hipStream_t s = (hipStream_t)stream;
+    // no compressed row is visible to any query: every list is K x -1 (the pages' empty selection)
+    int64_t vmax = (start_pos + m) / ratio;
+    vmax = vmax < n_c ? vmax : n_c;
+    if (vmax == 0) {
+        topk_kernel<<<dim3((unsigned)nq), dim3(TOPK_THREADS), 0, s>>>(nullptr, 0, m, ratio, start_pos, K, offset, idx,
+                                                                      ld, col0);
+        return check_launch("sckv_index_scores_topk");
+    }
+    if (!q || !k || !w) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null input");
+    if ((uintptr_t)q % 16 || (uintptr_t)k % 16)
+        return fail(SCKV_EINVAL, "sckv_index_scores_topk: q and k must be 16-byte aligned");
+    if ((uintptr_t)w % 4 || (uintptr_t)idx % 4) return fail(SCKV_EINVAL, "sckv_index_scores_topk: misaligned w/idx");
+    if (scores && (uintptr_t)scores % 2) return fail(SCKV_EINVAL, "sckv_index_scores_topk: misaligned scores");
+    const size_t need = index_workspace_bytes(B, m, n_c);
+    if (!ws || ws_bytes < need) return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk: workspace too small");
+    if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: too many queries");
+    const int rpw = score_rows_per_wg(nq, n_c);
+    const int nsplit = (int)((n_c + rpw - 1) / rpw);
+    if (nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: grid too large");
+    uint16_t* keys = (uint16_t*)ws;
+    const uint16_t* qq = (const uint16_t*)q;
+    const uint16_t* kk = (const uint16_t*)k;
+    uint16_t* sc = (uint16_t*)scores;
+    const bool two = Hi > 32;
+#define SCKV_SCORES(MT, DI) launch_scores<MT, DI>(qq, kk, w, nq, m, Hi, n_c, ratio, start_pos, rpw, nsplit, keys, sc, s)
+    switch (Di) {
+        case 32: two ? SCKV_SCORES(2, 32) : SCKV_SCORES(1, 32); break;
+        case 64: two ? SCKV_SCORES(2, 64) : SCKV_SCORES(1, 64); break;
+        case 128: two ? SCKV_SCORES(2, 128) : SCKV_SCORES(1, 128); break;
+        default: two ? SCKV_SCORES(2, 256) : SCKV_SCORES(1, 256); break;
+    }
+#undef SCKV_SCORES
+    int rc = check_launch("sckv_index_scores_topk (scores)");
+    if (rc) return rc;
+    topk_kernel<<<dim3((unsigned)nq), dim3(TOPK_THREADS), 0, s>>>(keys, n_c, m, ratio, start_pos, K, offset, idx, ld,
+                                                                  col0);
+    return check_launch("sckv_index_scores_topk (top-k)");
+}

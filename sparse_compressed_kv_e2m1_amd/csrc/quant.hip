@@ -1,0 +1,130 @@
+// quant.hip -- the fp4 (e2m1) round trip over bf16 rows (page
+// "metrale_model_arch/deepseek_v41_ref/compress.rs": fp4_quant_e8m0_inplace,
+// fp4_quant_e4m3_inplace; page "metrale_model_arch/attn_v41/forward.rs": the
+// fp4_quant of the new latent groups before the cache copy).
+//
+// HBM-bound: one lane owns one block (16 or 32 values = 32 or 64 bytes), reads
+// it with 16-byte loads, and writes it back with 16-byte stores; neighbouring
+// lanes own neighbouring blocks, so a wave streams 2 or 4 KiB contiguously.
+#include "sckv_device.h"
+
+namespace sckv {
+namespace {
+
+constexpr int QUANT_THREADS = 256;
+
+// rows x cols values, row strides ldx / ldy (elements); cols % BLOCK == 0.
+// VEC: every block is 16-byte aligned in x and y (checked on the host).
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                    uint16_t* __restrict__ y, int64_t ldy,
+                                                                    int64_t blocks_per_row, int64_t nblocks) {
+    constexpr int BLOCK = QuantMode<MODE>::BLOCK;
+    const int64_t gid = (int64_t)blockIdx.x * QUANT_THREADS + threadIdx.x;
+    if (gid >= nblocks) return;
+    const int64_t row = gid / blocks_per_row;
+    const int64_t col = (gid - row * blocks_per_row) * BLOCK;
+    const uint16_t* src = x + row * ldx + col;
+    uint16_t* dst = y + row * ldy + col;
+
+    uint32_t w[BLOCK / 2];  // bf16 pairs, low half = lower index
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 8; ++i) {
+            uint4 v = reinterpret_cast<const uint4*>(src)[i];
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+    const float s = block_scale<MODE>(amax);
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        uint32_t lo = fp4_value_bits(bf16_bits_to_f32(w[i] & 0xffffu), s);
+        uint32_t hi = fp4_value_bits(bf16_bits_to_f32(w[i] >> 16), s);
+        w[i] = lo | (hi << 16);
+    }
+    if (VEC) {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 8; ++i)
+            reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 2; ++i) {
+            dst[2 * i] = (uint16_t)(w[i] & 0xffffu);
+            dst[2 * i + 1] = (uint16_t)(w[i] >> 16);
+        }
+    }
+}
+
+template <int MODE>
+int launch_quant(const uint16_t* x, int64_t ldx, uint16_t* y, int64_t ldy, int64_t rows, int64_t cols,
+                 hipStream_t stream) {
+    constexpr int BLOCK = QuantMode<MODE>::BLOCK;
+    const int64_t bpr = cols / BLOCK;
+    const int64_t nblocks = rows * bpr;
+    if (nblocks == 0) return SCKV_OK;
+    const int64_t grid = (nblocks + QUANT_THREADS - 1) / QUANT_THREADS;
+    if (grid > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_quant: too many blocks for one launch");
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) && (ldx % 8 == 0) && (ldy % 8 == 0);
+    if (vec)
+        quant_rows_kernel<MODE, true><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, stream>>>(x, ldx, y, ldy, bpr,
+                                                                                                  nblocks);
+    else
+        quant_rows_kernel<MODE, false><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, stream>>>(x, ldx, y, ldy,
+                                                                                                   bpr, nblocks);
+    return check_launch("sckv_quant");
+}
+
+int quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols, int mode,
+                    void* stream) {
+    if (mode != SCKV_FP4_E4M3_B16 && mode != SCKV_FP4_E8M0_B32) return fail(SCKV_EINVAL, "sckv_quant: bad mode");
+    const int block = (mode == SCKV_FP4_E4M3_B16) ? 16 : 32;
+    if (rows < 0 || cols < 0) return fail(SCKV_EINVAL, "sckv_quant: negative size");
+    if (cols % block != 0) return fail(SCKV_EINVAL, "sckv_quant: row length is not a multiple of the block");
+    if (rows == 0 || cols == 0) return SCKV_OK;
+    if (!x || !y) return fail(SCKV_EINVAL, "sckv_quant: null pointer");
+    if (ldx < cols || ldy < cols) return fail(SCKV_EINVAL, "sckv_quant: row stride shorter than the row");
+    if ((uintptr_t)x % 2 || (uintptr_t)y % 2) return fail(SCKV_EINVAL, "sckv_quant: pointer not 2-byte aligned");
+    if (x != y) {
+        // ranges [x, x + span) and [y, y + span) must not overlap
+        const uintptr_t xs = (uintptr_t)x, ys = (uintptr_t)y;
+        const uintptr_t xe = xs + (uintptr_t)(((rows - 1) * ldx + cols) * 2);
+        const uintptr_t ye = ys + (uintptr_t)(((rows - 1) * ldy + cols) * 2);
+        if (xs < ye && ys < xe) return fail(SCKV_EINVAL, "sckv_quant: x and y overlap without being equal");
+    } else if (ldx != ldy) {
+        return fail(SCKV_EINVAL, "sckv_quant: in place needs ldx == ldy");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == SCKV_FP4_E4M3_B16)
+        return launch_quant<SCKV_FP4_E4M3_B16>((const uint16_t*)x, ldx, (uint16_t*)y, ldy, rows, cols, s);
+    return launch_quant<SCKV_FP4_E8M0_B32>((const uint16_t*)x, ldx, (uint16_t*)y, ldy, rows, cols, s);
+}
+
+}  // namespace
+}  // namespace sckv
+
+extern "C" int sckv_quant(const void* x, void* y, int64_t n, int mode, void* stream) {
+    if (n < 0) return sckv::fail(SCKV_EINVAL, "sckv_quant: negative n");
+    if (mode != SCKV_FP4_E4M3_B16 && mode != SCKV_FP4_E8M0_B32)
+        return sckv::fail(SCKV_EINVAL, "sckv_quant: bad mode");
+    const int block = (mode == SCKV_FP4_E4M3_B16) ? 16 : 32;
+    if (n % block != 0) return sckv::fail(SCKV_EINVAL, "sckv_quant: n is not a multiple of the block");
+    // a flat array is one row of n values
+    return sckv::quant_rows_impl(x, n, y, n, n ? 1 : 0, n, mode, stream);
+}
+
+extern "C" int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                               int mode, void* stream) {
+    return sckv::quant_rows_impl(x, ldx, y, ldy, rows, cols, mode, stream);
+}

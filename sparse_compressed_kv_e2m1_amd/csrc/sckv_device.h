@@ -1,0 +1,120 @@
+// sckv_device.h -- device helpers of the gfx950 kernels: bf16 bits, the e2m1
+// grid, the two block-scale rules, and the ABI's host-side error plumbing.
+//
+// Rules (page "metrale_model_arch/deepseek_v41_ref/compress.rs": E2M1,
+// FP4_MAX, to_e2m1_rne, fp4_quant_e8m0_inplace, fp4_quant_e4m3_inplace).
+// Every function here is bit-exact by construction: integer bit work, or one
+// correctly rounded binary32 operation per step.  The library is compiled
+// with -ffp-contract=off so no multiply-add is fused behind our back.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/sckv.h"
+
+namespace sckv {
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// binary32 -> bf16 bits, round to nearest, ties to even (finite inputs; NaN
+// stays a quiet NaN).  Adding 0x7fff plus the kept LSB and truncating rounds
+// the dropped 16 bits half-to-even.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ---------------------------------------------------------------- e2m1 grid
+
+// Nearest point of {0, .5, 1, 1.5, 2, 3, 4, 6} to |y| with exact ties going to
+// the even code (codes 0..7 in grid order), sign of y kept.  The tie points
+// are the midpoints .25 .75 1.25 1.75 2.5 3.5 5: the even neighbour is 0, 1,
+// 1, 2, 2, 4, 4, which decides whether each comparison is strict.
+__device__ __forceinline__ float e2m1_round(float y) {
+    float a = fabsf(y);
+    float r = 6.0f;
+    r = (a <= 5.0f) ? 4.0f : r;
+    r = (a < 3.5f) ? 3.0f : r;
+    r = (a <= 2.5f) ? 2.0f : r;
+    r = (a < 1.75f) ? 1.5f : r;
+    r = (a <= 1.25f) ? 1.0f : r;
+    r = (a < 0.75f) ? 0.5f : r;
+    r = (a <= 0.25f) ? 0.0f : r;
+    return copysignf(r, y);
+}
+
+// ---------------------------------------------------------------- scale rules
+
+// Power-of-two ceiling of a normal positive binary32 x (x >= 2^-126 here
+// thanks to the amax floor, and x < 2^126 for any finite bf16 amax / 6).
+__device__ __forceinline__ float pow2_ceil_normal(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x007fffffu) == 0u) return x;
+    return __uint_as_float((u & 0x7f800000u) + 0x00800000u);
+}
+
+// x >= 0 rounded to the nearest OCP E4M3FN value (ties to the even code),
+// saturating at 448.  Subnormal range (x < 2^-6): multiples of 2^-9, rounded
+// with rintf (half-to-even) on the exactly scaled value.  Normal range: keep
+// 3 mantissa bits with half-to-even on the binary32 bits (a carry moves to the
+// next binade, which is the correct rounding).
+__device__ __forceinline__ float e4m3_round_nonneg(float x) {
+    if (x < 0.015625f) {
+        float q = rintf(x * 512.0f);
+        return q * 0.001953125f;
+    }
+    uint32_t u = __float_as_uint(x);
+    u += 0x7ffffu + ((u >> 20) & 1u);
+    u &= 0xfff00000u;
+    float r = __uint_as_float(u);
+    return fminf(r, 448.0f);
+}
+
+// Block scale for the two modes from the block's amax (binary32).
+template <int MODE>
+__device__ __forceinline__ float block_scale(float amax) {
+    if (MODE == SCKV_FP4_E8M0_B32) {
+        const float floor_amax = 0x1.8p-124f;  // 6 * 2^-126
+        amax = fmaxf(amax, floor_amax);
+        return pow2_ceil_normal(__fdiv_rn(amax, 6.0f));
+    } else {
+        const float floor_amax = 0x1.8p-7f;  // 6 * 2^-9
+        amax = fmaxf(amax, floor_amax);
+        return e4m3_round_nonneg(__fdiv_rn(amax, 6.0f));
+    }
+}
+
+// One value of a block: bf16 bits of e2m1(clamp(v / s, -6, 6)) * s.  The
+// quotient is the correctly rounded binary32 division (true division, not a
+// reciprocal multiply: the two differ on some exact e2m1 midpoints).
+__device__ __forceinline__ uint32_t fp4_value_bits(float v, float s) {
+    float y = __fdiv_rn(v, s);
+    y = fminf(fmaxf(y, -6.0f), 6.0f);
+    return f32_to_bf16_bits(e2m1_round(y) * s);
+}
+
+template <int MODE>
+struct QuantMode;
+template <>
+struct QuantMode<SCKV_FP4_E4M3_B16> {
+    static constexpr int BLOCK = 16;
+};
+template <>
+struct QuantMode<SCKV_FP4_E8M0_B32> {
+    static constexpr int BLOCK = 32;
+};
+
+// ---------------------------------------------------------------- host side
+
+void set_error(const std::string& msg);
+int fail(int code, const std::string& msg);
+int check_launch(const char* what);
+
+}  // namespace sckv

@@ -1,0 +1,129 @@
+"""One step of the compressed sparse attention hot path for B independent
+sequences, as a sequence of C-ABI calls on one HIP stream (no host round
+trip, no CPU compute).
+
+Order of a step (page "metrale_model_arch/attn_v41/forward.rs",
+AttnV41::forward; page "metrale_model_arch/deepseek_v41_ref/compress.rs",
+attention_any):
+  1. fp4 round trip of the step's new compressed latent rows into the latent
+     cache (e4m3 scales, block 16) and of the new indexer k rows into the k
+     cache (power-of-two scales, block 32);
+  2. decode (m == 1, start_pos > 0): the new kv row goes into its ring slot
+     before attention;
+  3. window columns of every query's index list;
+  4. compressed columns: indexer scores + top-K, or every visible row on a
+     layer without an indexer;
+  5. sparse attention with the sink over [rows_a | latent cache];
+  6. start_pos == 0 or a chunk: the step's last rows go into the ring after
+     attention (a chunk reads the ring as it was before the chunk).
+
+Device memory layout (per sequence b; all bf16 unless noted):
+  q [B, m, H, D]; rows_a: the fresh kv [B, m, D] (start_pos 0), the ring
+  [B, win, D] (decode), or [B, win + m, D] = ring then chunk (chunked
+  prefill); latent cache [B, n_c, D]; indexer k cache [B, n_c, Di];
+  indexer q [B, m, Hi, Di]; w f32 [B, m, Hi]; sink f32 [H];
+  idx int32 [B, m, win + K]; out [B, m, H, D].
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _binding as sk
+
+
+class PathState:
+    """Device buffers of one step for B sequences of a workload, built from
+    raw CPU inputs (see sckv_synth.make_inputs).  setup() round-trips the cache
+    rows that existed before this step; step() runs the hot path."""
+
+    def __init__(self, w, inputs: dict, B: int = 1, device="cuda"):
+        self.w, self.B, self.device = w, B, device
+        dev = lambda t: t.to(device).contiguous()  # noqa: E731
+        self.q = dev(inputs["q"])
+        self.sink = dev(inputs["sink"])
+        m, win, D = w.m, w.win, w.D
+        if w.start_pos == 0:
+            self.mode = "fresh"
+            self.rows_a = dev(inputs["kv_new"])
+            self.ring = torch.zeros((B, win, D), dtype=torch.bfloat16, device=device)
+        elif m == 1:
+            self.mode = "ring"
+            self.rows_a = dev(inputs["ring"])  # the ring itself; the new row is written in step()
+            self.ring = self.rows_a
+            self.kv_new = dev(inputs["kv_new"])
+        else:
+            self.mode = "chunk"
+            buf = torch.empty((B, win + m, D), dtype=torch.bfloat16, device=device)
+            buf[:, :win] = inputs["ring"].to(device)
+            buf[:, win:] = inputs["kv_new"].to(device)
+            self.rows_a = buf
+        self.ra = sk.sckv_rows_a_len(win, m, w.start_pos)
+        assert self.ra == self.rows_a.shape[1]
+        self.first_new = w.first_new_row
+        self.n_new = w.n_c - self.first_new
+        lat = inputs["latent_raw"]
+        self.latent = dev(lat)
+        self.latent_new = dev(lat[:, self.first_new:])
+        if w.Hi:
+            self.iq = dev(inputs["iq"])
+            self.iw = dev(inputs["iw"])
+            self.ik = dev(inputs["ik_raw"])
+            self.ik_new = dev(inputs["ik_raw"][:, self.first_new:])
+            self.ws_index = sk.workspace(sk.SCKV_OP_INDEX_SCORES_TOPK, B, m, w.Hi, w.Di, w.n_c, device=device)
+        self.T = w.T
+        self.idx = torch.empty((B, m, self.T), dtype=torch.int32, device=device)
+        self.out = torch.empty((B, m, w.H, D), dtype=torch.bfloat16, device=device)
+        self.ws_attn = sk.workspace(sk.SCKV_OP_SPARSE_ATTN_SINK, B, m, w.H, D, self.T, device=device)
+
+    def setup(self):
+        """Round-trip the compressed rows that precede this step (the caches
+        as earlier steps left them)."""
+        w, B = self.w, self.B
+        if self.first_new > 0:
+            sk.sckv_quant_rows(self.latent, w.n_c * w.D, self.latent, w.n_c * w.D, B, self.first_new * w.D,
+                               sk.SCKV_FP4_E4M3_B16)
+            if w.Hi:
+                sk.sckv_quant_rows(self.ik, w.n_c * w.Di, self.ik, w.n_c * w.Di, B, self.first_new * w.Di,
+                                   sk.SCKV_FP4_E8M0_B32)
+
+    def _quant_new(self, src, dst, width, mode):
+        w, B = self.w, self.B
+        if self.n_new == 0:
+            return
+        if self.n_new == 1 or B == 1:
+            # B x n_new rows: either one row per sequence, or one sequence
+            rows, ldx, ldy, cols = (B, width, w.n_c * width, width) if self.n_new == 1 else (self.n_new, width, width,
+                                                                                               width)
+            sk.sckv_quant_rows(src, ldx, dst[:, self.first_new:], ldy, rows, cols, mode)
+        else:
+            for b in range(B):
+                sk.sckv_quant_rows(src[b], width, dst[b, self.first_new:], width, self.n_new, width, mode)
+
+    def step(self):
+        w, B = self.w, self.B
+        m, win, D = w.m, w.win, w.D
+        # 1. the step's new compressed rows
+        self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16)
+        if w.Hi:
+            self._quant_new(self.ik_new, self.ik, w.Di, sk.SCKV_FP4_E8M0_B32)
+        # 2. decode: ring write before attention
+        if self.mode == "ring":
+            sk.sckv_ring_write(self.kv_new, D, self.ring, win * D, B, 1, w.start_pos, win, D)
+        # 3. window columns
+        sk.sckv_window_idx(B, m, w.start_pos, win, self.idx, self.T)
+        # 4. compressed columns
+        if w.Hi:
+            sk.sckv_index_scores_topk(self.iq, self.ik, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K,
+                                      self.ra, self.idx, self.T, win, ws=self.ws_index)
+        else:
+            sk.sckv_visible_idx(B, m, w.start_pos, w.ratio, w.n_c, w.K, self.ra, self.idx, self.T, win)
+        # 5. attention
+        sk.sckv_sparse_attn_sink(self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink,
+                                 w.scale, B, m, w.H, D, self.out, ws=self.ws_attn)
+        # 6. ring after attention (fresh prefill, chunk)
+        if self.mode == "fresh":
+            sk.sckv_ring_write(self.rows_a, m * D, self.ring, win * D, B, m, w.start_pos, win, D)
+        elif self.mode == "chunk":
+            rows = self.rows_a[:, win:]
+            sk.sckv_ring_write(rows, (win + m) * D, self.rows_a, (win + m) * D, B, m, w.start_pos, win, D)
+        return self.out

@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+call include/sckv.h declares, and rejects invalid arguments before enqueuing
+anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_calls():
+    src = open(os.path.join(ROOT, "include", "sckv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sckv_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_calls():
+    names = declared_calls()
+    for n in ["sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_rows_a_len", "sckv_window_idx",
+              "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
+              "sckv_last_error", "sckv_abi_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_call():
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    lib = ctypes.CDLL(sk.LIB_PATH)
+    for n in declared_calls():
+        assert hasattr(lib, n), n
+    assert sk.sckv_abi_version() == 1
+
+
+def test_header_compiles_as_c():
+    """The header is plain C (no HIP or torch types)."""
+    import subprocess
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write('#include "sckv.h"\nint main(void){return sckv_abi_version() == 1 ? 0 : 1;}\n')
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
+                        c], check=True)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    return sk.lib
+
+
+def test_error_paths(L):
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails its host checks
+    # quant: n not a multiple of the block, bad mode, null pointers
+    assert L.sckv_quant(fake, fake, 17, sk.SCKV_FP4_E4M3_B16, None) == sk.SCKV_EINVAL
+    assert "multiple" in sk.sckv_last_error()
+    assert L.sckv_quant(fake, fake, 32, 7, None) == sk.SCKV_EINVAL
+    assert L.sckv_quant(None, fake, 32, sk.SCKV_FP4_E8M0_B32, None) == sk.SCKV_EINVAL
+    assert L.sckv_quant(fake, fake, 0, sk.SCKV_FP4_E8M0_B32, None) == sk.SCKV_OK  # empty is a no-op
+    assert L.sckv_quant_rows(fake, 8, fake, 8, 2, 16, sk.SCKV_FP4_E4M3_B16, None) == sk.SCKV_EINVAL  # ld < cols
+    assert L.sckv_quant_rows(fake, 16, ctypes.c_void_p(0x1010), 16, 2, 16, sk.SCKV_FP4_E4M3_B16,
+                             None) == sk.SCKV_EINVAL  # overlap
+    # ring
+    assert L.sckv_ring_write(fake, 64, fake, 64, 1, 1, 5, 0, 64, None) == sk.SCKV_EINVAL
+    assert L.sckv_ring_write(fake, 64, fake, 64 * 16, 1, 1, 5, 16, 64, None) == sk.SCKV_EINVAL  # overlap
+    # window / visible
+    assert L.sckv_window_idx(1, 4, 0, 16, None, 16, None) == sk.SCKV_EINVAL
+    assert L.sckv_window_idx(1, 4, 0, 16, fake, 8, None) == sk.SCKV_EINVAL
+    assert L.sckv_visible_idx(1, 1, 1000, 4, 1000, 16, 0, fake, 32, 16, None) == sk.SCKV_EINVAL  # V > K
+    # indexer
+    args = dict(B=1, m=1, Hi=64, Di=128, n_c=8192, ratio=4, start_pos=32767, K=512, offset=128, ld=640, col0=128)
+
+    def ix(**kw):
+        a = {**args, **kw}
+        return L.sckv_index_scores_topk(fake, fake, fake, a["B"], a["m"], a["Hi"], a["Di"], a["n_c"], a["ratio"],
+                                        a["start_pos"], a["K"], a["offset"], kw.get("idx", fake), a["ld"], a["col0"],
+                                        None, kw.get("ws", fake), kw.get("ws_bytes", 1 << 30), None)
+
+    assert ix(Hi=48) == sk.SCKV_EINVAL
+    assert ix(Hi=128) == sk.SCKV_EUNSUPPORTED
+    assert ix(Di=96) == sk.SCKV_EUNSUPPORTED
+    assert ix(ld=600) == sk.SCKV_EINVAL
+    assert ix(idx=None) == sk.SCKV_EINVAL
+    assert ix(ws=None) == sk.SCKV_EWORKSPACE
+    assert ix(ws_bytes=100) == sk.SCKV_EWORKSPACE
+    assert ix(ratio=0) == sk.SCKV_EINVAL
+
+    # attention
+    def at(**kw):
+        a = dict(ra=128, rb=8192, T=640, B=1, m=1, H=64, D=512, scale=0.044, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.sckv_sparse_attn_sink(fake, fake, a["ra"], fake, a["rb"], fake, a["T"], fake,
+                                       ctypes.c_float(a["scale"]), a["B"], a["m"], a["H"], a["D"],
+                                       kw.get("out", fake), kw.get("ws", fake), a["ws_bytes"], None)
+
+    assert at(H=65) == sk.SCKV_EUNSUPPORTED
+    assert at(D=96) == sk.SCKV_EUNSUPPORTED
+    assert at(T=0) == sk.SCKV_EINVAL
+    assert at(T=70000) == sk.SCKV_EUNSUPPORTED
+    assert at(out=None) == sk.SCKV_EINVAL
+    assert at(scale=0.0) == sk.SCKV_EINVAL
+    assert at(ws=None) == sk.SCKV_EWORKSPACE  # decode at B = 1 splits rows over workgroups
+    assert at(B=0) == sk.SCKV_OK
+
+
+def test_workspace_sizes(L):
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    assert sk.sckv_workspace_bytes(sk.SCKV_OP_INDEX_SCORES_TOPK, 1, 4096, 64, 128, 1024) == 4096 * 1024 * 2
+    assert sk.sckv_workspace_bytes(sk.SCKV_OP_SPARSE_ATTN_SINK, 1, 4096, 64, 512, 640) == 0  # no split at m = 4096
+    assert sk.sckv_workspace_bytes(sk.SCKV_OP_SPARSE_ATTN_SINK, 1, 1, 64, 512, 640) > 0
+    assert sk.sckv_workspace_bytes(9, 1, 1, 1, 1, 1) == ctypes.c_size_t(-1).value
+    assert sk.sckv_rows_a_len(128, 4096, 0) == 4096
+    assert sk.sckv_rows_a_len(128, 1, 32767) == 128
+    assert sk.sckv_rows_a_len(128, 2048, 63488) == 2176
+    assert sk.sckv_rows_a_len(0, 1, 1) == -1
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    """The package never imports the oracle and has no CPU compute path."""
+    pkg = os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                for bad in ("import oracle", "from oracle", "libsckv_oracle", "sckvo_", "oracle.py"):
+                    assert bad not in text, (f, bad)

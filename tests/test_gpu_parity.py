@@ -1,0 +1,331 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by
+element, on seeded inputs.
+
+Bars: quantised bf16 bits, index lists and indexer scores bit-exact;
+attention |gpu - oracle| <= 1e-2 * max|oracle| + 1e-3.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import sckv_synth as synth
+from oracle import oracle
+from tests.helpers import attn_tolerance_ok, bits, from_bits, oracle_step, sample_queries, vals
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sk():
+    assert torch.cuda.is_available(), "the gpu tests need a GPU"
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    return sk
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_of(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------- quant
+
+def _scale_sweep_blocks(mode):
+    """Blocks that pin the scale at every reachable value s and put every bf16
+    magnitude of [s/8, 6s] (both signs) through the rounding: the block's
+    first value is 6s (so amax / 6 = s exactly) and the rest are the probes."""
+    block = 16 if mode == oracle.E4M3_B16 else 32
+    if mode == oracle.E4M3_B16:
+        scales = sorted({oracle.e4m3_to_f32(c) for c in range(1, 0x7F)})
+    else:
+        scales = [2.0**e for e in list(range(-126, -110)) + list(range(-12, 13)) + list(range(110, 126))]
+    allpos = vals(np.arange(1, 0x7F80, dtype=np.uint16))
+    blocks = []
+    for s in scales:
+        top = np.float32(6.0) * np.float32(s)
+        if not np.isfinite(top) or float(bf16_of([top]).float()[0]) != float(top):
+            continue
+        probes = allpos[(allpos >= s / 8) & (allpos <= top)]
+        probes = np.concatenate([probes, -probes, [0.0, -0.0, float(top), -float(top)]]).astype(np.float32)
+        per = block - 1
+        n = (len(probes) + per - 1) // per
+        pad = np.zeros(n * per, np.float32)
+        pad[: len(probes)] = probes
+        blk = np.concatenate([np.full((n, 1), top, np.float32), pad.reshape(n, per)], axis=1)
+        blocks.append(blk)
+    x = np.concatenate(blocks).reshape(-1)
+    return bits(bf16_of(x))
+
+
+@pytest.mark.parametrize("mode_name", ["e4m3_b16", "e8m0_b32"])
+def test_quant_scale_sweep_bit_exact(sk, mode_name):
+    mode = oracle.E4M3_B16 if mode_name == "e4m3_b16" else oracle.E8M0_B32
+    gmode = sk.SCKV_FP4_E4M3_B16 if mode_name == "e4m3_b16" else sk.SCKV_FP4_E8M0_B32
+    xb = _scale_sweep_blocks(mode)
+    say(f"quant scale sweep {mode_name}: {xb.size} values")
+    want = oracle.quant(xb, mode)
+    x = from_bits(xb, "cuda")
+    y = torch.empty_like(x)
+    sk.sckv_quant(x, y, gmode)
+    got = bits(y)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (bad.size, vals(xb[bad[:8]]), vals(got[bad[:8]]), vals(want[bad[:8]]))
+    # in place gives the same bits
+    sk.sckv_quant(x, x, gmode)
+    assert np.array_equal(bits(x), want)
+
+
+@pytest.mark.parametrize("mode_name,n", [("e4m3_b16", 16), ("e4m3_b16", 1024 * 512 + 48), ("e8m0_b32", 32),
+                                         ("e8m0_b32", 8192 * 128 + 96)])
+def test_quant_random_bit_exact(sk, mode_name, n):
+    mode = oracle.E4M3_B16 if mode_name == "e4m3_b16" else oracle.E8M0_B32
+    gmode = sk.SCKV_FP4_E4M3_B16 if mode_name == "e4m3_b16" else sk.SCKV_FP4_E8M0_B32
+    rng = np.random.default_rng(n)
+    blk = 16 if mode == oracle.E4M3_B16 else 32
+    sig = np.exp(rng.uniform(-20, 20, size=(n // blk, 1)))
+    x = bits(bf16_of((rng.standard_normal((n // blk, blk)) * sig).reshape(-1)))
+    say(f"quant random {mode_name} n={n}")
+    want = oracle.quant(x, mode)
+    xd = from_bits(x, "cuda")
+    yd = torch.empty_like(xd)
+    sk.sckv_quant(xd, yd, gmode)
+    assert np.array_equal(bits(yd), want)
+
+
+def test_quant_rows_strided(sk):
+    """One new row in each of B caches (row stride n_c * D), unaligned pointers too."""
+    B, n_c, D = 5, 7, 512
+    rng = np.random.default_rng(4)
+    cache = bits(bf16_of(rng.standard_normal((B, n_c, D))))
+    new = bits(bf16_of(rng.standard_normal((B, D))))
+    cd = from_bits(cache, "cuda")
+    nd = from_bits(new, "cuda")
+    say("quant_rows strided")
+    sk.sckv_quant_rows(nd, D, cd[:, 3], n_c * D, B, D, sk.SCKV_FP4_E4M3_B16)
+    want = cache.copy()
+    for b in range(B):
+        want[b, 3] = oracle.quant(new[b], oracle.E4M3_B16)
+    assert np.array_equal(bits(cd), want)
+    # unaligned (2-byte offset) source and destination
+    x = torch.zeros(1 + 64, dtype=torch.bfloat16, device="cuda")
+    x[1:] = from_bits(new[0, :64], "cuda")
+    yv = torch.zeros(1 + 64, dtype=torch.bfloat16, device="cuda")
+    sk.sckv_quant_rows(x[1:], 64, yv[1:], 64, 1, 64, sk.SCKV_FP4_E8M0_B32)
+    assert np.array_equal(bits(yv[1:]), oracle.quant(new[0, :64], oracle.E8M0_B32))
+
+
+# --------------------------------------------------------------------- window, visible, ring
+
+@pytest.mark.parametrize("win,m,start_pos", [(16, 1, 255), (128, 1, 32767), (128, 4096, 0), (128, 2048, 63488),
+                                             (16, 1, 3), (8, 20, 0), (8, 5, 0), (8, 12, 40), (8, 1, 0)])
+def test_window_idx_bit_exact(sk, win, m, start_pos):
+    B = 2
+    ld = win + 3
+    idx = torch.full((B, m, ld), 77, dtype=torch.int32, device="cuda")
+    say(f"window idx win={win} m={m} start_pos={start_pos}")
+    sk.sckv_window_idx(B, m, start_pos, win, idx, ld)
+    want, _ = oracle.window_idx(win, m, start_pos)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b, :, :win], want)
+        assert np.all(got[b, :, win:] == 77)
+
+
+@pytest.mark.parametrize("m,start_pos,ratio,n_c,K", [(2048, 63488, 128, 512, 512), (7, 60, 8, 8, 10),
+                                                     (1, 32767, 4, 8192, 8192), (300, 0, 4, 75, 80)])
+def test_visible_idx_bit_exact(sk, m, start_pos, ratio, n_c, K):
+    B, col0, off = 2, 5, 2176
+    ld = col0 + K
+    idx = torch.full((B, m, ld), 77, dtype=torch.int32, device="cuda")
+    say(f"visible idx m={m} start_pos={start_pos}")
+    sk.sckv_visible_idx(B, m, start_pos, ratio, n_c, K, off, idx, ld, col0)
+    want = oracle.visible_idx(m, start_pos, ratio, n_c, K, off)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b, :, col0:], want) and np.all(got[b, :, :col0] == 77)
+
+
+@pytest.mark.parametrize("win,m,start_pos,D", [(16, 1, 255, 64), (128, 4096, 0, 512), (128, 2048, 63488, 512),
+                                               (8, 20, 5, 64), (8, 3, 0, 64)])
+def test_ring_write_bit_exact(sk, win, m, start_pos, D):
+    B = 2
+    rng = np.random.default_rng(m)
+    ring = rng.integers(0, 65535, size=(B, win, D)).astype(np.uint16)
+    rows = rng.integers(0, 65535, size=(B, m, D)).astype(np.uint16)
+    rd, gd = from_bits(rows, "cuda"), from_bits(ring, "cuda")
+    say(f"ring write win={win} m={m}")
+    sk.sckv_ring_write(rd, m * D, gd, win * D, B, m, start_pos, win, D)
+    got = bits(gd)
+    for b in range(B):
+        assert np.array_equal(got[b], oracle.ring_write(ring[b], rows[b], start_pos))
+    # chunk layout: [ring | chunk] in one buffer
+    buf = np.concatenate([ring, rows], axis=1)
+    bd = from_bits(buf, "cuda")
+    sk.sckv_ring_write(bd[:, win:], (win + m) * D, bd, (win + m) * D, B, m, start_pos, win, D)
+    got = bits(bd)
+    for b in range(B):
+        assert np.array_equal(got[b, :win], oracle.ring_write(ring[b], rows[b], start_pos))
+        assert np.array_equal(got[b, win:], rows[b])
+
+
+# --------------------------------------------------------------------- indexer
+
+INDEXER_CASES = [
+    # B, m, Hi, Di, n_c, ratio, start_pos, K
+    (1, 1, 4, 32, 64, 4, 255, 16),
+    (2, 1, 64, 128, 8192, 4, 32767, 512),
+    (1, 3, 64, 128, 1000, 4, 3997, 100),     # ragged row tail, several queries
+    (2, 5, 32, 64, 300, 1, 295, 37),
+    (1, 4, 16, 256, 129, 2, 254, 128),
+    (1, 2, 8, 128, 77, 3, 230, 76),
+    (1, 2, 2, 32, 40, 1, 38, 39),
+    (1, 1, 1, 32, 40, 1, 39, 5),
+    (1, 6, 64, 128, 20, 4, 0, 8),            # early positions: 0, 1, 2 see nothing
+    (3, 1, 64, 128, 3000, 4, 11999, 3000),   # K >= visible: all visible rows
+]
+
+
+@pytest.mark.parametrize("case", INDEXER_CASES, ids=lambda c: "B{}m{}Hi{}Di{}nc{}K{}".format(*c[:5], c[7]))
+def test_index_scores_topk_bit_exact(sk, case):
+    B, m, Hi, Di, n_c, ratio, start_pos, K = case
+    rng = np.random.default_rng(sum(case))
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di))))
+    k = np.stack([oracle.quant(bits(bf16_of(rng.standard_normal((n_c, Di)))).reshape(-1), oracle.E8M0_B32)
+                  .reshape(n_c, Di) for _ in range(B)])
+    w = (rng.standard_normal((B, m, Hi)) * (Hi * Di) ** -0.5).astype(np.float32)
+    col0, off = 3, 1234
+    ld = col0 + K + 2
+    idx = torch.full((B, m, ld), 77, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, m, n_c), dtype=torch.bfloat16, device="cuda")
+    say(f"indexer case {case}")
+    sk.sckv_index_scores_topk(from_bits(q, "cuda"), from_bits(k, "cuda"), torch.from_numpy(w).cuda(), B, m, Hi, Di,
+                              n_c, ratio, start_pos, K, off, idx, ld, col0, scores=scores)
+    got_idx = idx.cpu().numpy()
+    got_sc = bits(scores)
+    for b in range(B):
+        sc, bad = oracle.index_scores(q[b], k[b], w[b], start_pos, ratio)
+        assert bad == 0
+        for t in range(m):
+            v = oracle.visible(start_pos + t, ratio, n_c)
+            assert np.array_equal(got_sc[b, t, :v], sc[t, :v]), (b, t)
+            want = oracle.topk(sc[t], v, K, off)
+            assert np.array_equal(got_idx[b, t, col0:col0 + K], want), (b, t)
+        assert np.all(got_idx[b, :, :col0] == 77) and np.all(got_idx[b, :, col0 + K:] == 77)
+
+
+def test_index_topk_ties(sk):
+    """Many equal scores at the K-th place: w = 0 for all but one head and a k
+    cache of repeated rows forces ties; the lower rows must win."""
+    B, m, Hi, Di, n_c, K = 1, 2, 4, 32, 500, 64
+    rng = np.random.default_rng(99)
+    base = bits(bf16_of(rng.standard_normal((8, Di))))
+    kraw = base[rng.integers(0, 8, size=n_c)]
+    k = oracle.quant(kraw.reshape(-1), oracle.E8M0_B32).reshape(n_c, Di)
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di))))
+    w = np.zeros((B, m, Hi), np.float32)
+    w[:, :, 0] = 1.0
+    w[:, 1, 1] = -0.5
+    idx = torch.empty((B, m, K), dtype=torch.int32, device="cuda")
+    say("indexer ties")
+    sk.sckv_index_scores_topk(from_bits(q, "cuda"), from_bits(k[None], "cuda"), torch.from_numpy(w).cuda(), B, m, Hi,
+                              Di, n_c, 1, n_c - 1, K, 0, idx, K, 0)
+    sc, _ = oracle.index_scores(q[0], k, w[0], n_c - 1, 1)
+    for t in range(m):
+        assert np.array_equal(idx[0, t].cpu().numpy(), oracle.topk(sc[t], n_c, K, 0))
+
+
+# --------------------------------------------------------------------- attention
+
+ATTN_CASES = [
+    # B, m, H, D, ra, rb, T, frac_invalid
+    (1, 1, 8, 64, 16, 64, 32, 0.0),
+    (1, 1, 64, 512, 128, 8192, 640, 0.05),
+    (2, 3, 64, 512, 50, 300, 100, 0.3),      # ragged T (not a multiple of 32)
+    (1, 2, 48, 256, 40, 40, 70, 0.2),
+    (1, 4, 16, 128, 33, 0, 33, 0.1),         # rows_b empty
+    (1, 1, 64, 512, 128, 1024, 2176, 0.5),
+    (1, 3, 1, 64, 10, 10, 5, 0.0),
+    (300, 1, 64, 512, 128, 200, 64, 0.1),    # many queries: no split
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "B{}m{}H{}D{}T{}".format(c[0], c[1], c[2], c[3], c[6]))
+def test_sparse_attn_sink_tolerance(sk, case):
+    B, m, H, D, ra, rb, T, frac = case
+    rng = np.random.default_rng(ra * 7 + T)
+    q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, ra, D))))
+    Rb = bits(bf16_of(rng.standard_normal((B, max(rb, 1), D))))[:, :rb]
+    idx = rng.integers(0, ra + rb, size=(B, m, T)).astype(np.int32)
+    idx[rng.random((B, m, T)) < frac] = -1
+    if T > 3:
+        idx[:, :, 1] = idx[:, :, 0]  # a duplicate counts twice
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(D ** -0.5))
+    out = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    say(f"attention case {case}")
+    sk.sckv_sparse_attn_sink(from_bits(q, "cuda"), from_bits(A, "cuda"), ra,
+                             from_bits(Rb, "cuda") if rb else None, rb, torch.from_numpy(idx).cuda(), T,
+                             torch.from_numpy(sink).cuda(), scale, B, m, H, D, out)
+    got = vals(bits(out))
+    bsel = range(B) if B <= 4 else [0, B // 2, B - 1]
+    for b in bsel:
+        ref = oracle.sparse_attn(q[b], A[b], Rb[b] if rb else None, idx[b], sink, scale)
+        ok, worst = attn_tolerance_ok(got[b], ref)
+        assert ok, (b, worst)
+
+
+def test_sparse_attn_edge_rows(sk):
+    """All -1 gives 0; out-of-range indices are skipped like -1."""
+    B, m, H, D, ra, T = 1, 3, 64, 512, 40, 64
+    rng = np.random.default_rng(5)
+    q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, ra, D))))
+    idx = rng.integers(0, ra, size=(B, m, T)).astype(np.int32)
+    idx[0, 0] = -1
+    idx[0, 1, ::3] = ra + 1000   # outside rows_a + rows_b
+    sink = rng.standard_normal(H).astype(np.float32)
+    out = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    say("attention edge rows")
+    sk.sckv_sparse_attn_sink(from_bits(q, "cuda"), from_bits(A, "cuda"), ra, None, 0, torch.from_numpy(idx).cuda(), T,
+                             torch.from_numpy(sink).cuda(), 0.05, B, m, H, D, out)
+    got = vals(bits(out))[0]
+    assert np.all(got[0] == 0)
+    idx_ref = idx[0].copy()
+    idx_ref[idx_ref >= ra] = -1
+    ref = oracle.sparse_attn(q[0], A[0], None, idx_ref, sink, 0.05)
+    ok, worst = attn_tolerance_ok(got, ref)
+    assert ok, worst
+
+
+# --------------------------------------------------------------------- the whole step per workload
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_step_matches_oracle(sk, name):
+    from sparse_compressed_kv_e2m1_amd.step import PathState
+
+    w = synth.WORKLOADS[name]
+    B = 2 if w.m == 1 else 1
+    say(f"step {name} B={B}: generating inputs")
+    x = synth.make_inputs(w, B)
+    st = PathState(w, x, B)
+    st.setup()
+    say(f"step {name}: running the HIP path")
+    st.step()
+    torch.cuda.synchronize()
+    idx = st.idx.cpu().numpy()
+    out = vals(bits(st.out))
+    qsel = None if w.m <= 16 else sample_queries(w)
+    for b in range(B):
+        say(f"step {name}: oracle for instance {b}")
+        ref_idx, ref_out = oracle_step(w, x, b, qsel)
+        sel = np.arange(w.m) if qsel is None else qsel
+        assert np.array_equal(idx[b, sel], ref_idx), f"index lists differ ({name}, b={b})"
+        ok, worst = attn_tolerance_ok(out[b, sel], ref_out)
+        assert ok, (name, b, worst)
+    del st
