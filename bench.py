@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Throughput of the compressed sparse attention hot path on one MI355X.
+
+A step is one pass of the whole hot path (fp4 round trip of the step's new
+latent and indexer-k rows, ring write, window columns, indexer scores + top-k,
+sparse attention with the sink) over one batch: B independent sequences of a
+workload, every input resident in HBM before the timed region.
+
+Default workload: decode, m = 1 at start_pos = 32767, 64 heads x 512, window
+128, ratio 4 (8192 compressed rows), indexer 64 x 128 with top-512, batched
+over B = 128 independent sequences so that one step streams ~350 MB, past the
+256 MB last-level cache.
+
+Prints ONE JSON line (stdout): metric tokens/s, roofline of the dominant
+kernel (HIP-event time on the library's stream), and the oracle timed on the
+host cores as a CPU baseline.  Everything else goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, datasheet
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
+
+DEFAULT_B = {"tiny_decode": 1, "decode": 128, "long_decode": 32, "causal_prefill": 1, "chunked_prefill": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def describe(w):
+    s = (f"{w.name}: m={w.m} start_pos={w.start_pos} H={w.H} D={w.D} win={w.win} ratio={w.ratio} "
+         f"n_c={w.n_c}")
+    if w.Hi:
+        s += f" indexer {w.Hi}x{w.Di} top-{w.K}"
+    else:
+        s += f" all visible compressed rows (<= {w.K})"
+    return s
+
+
+def counts(w, B, call):
+    """Algorithmic bytes and flops of one library call for one step of B
+    sequences: what the method must read and write (bf16 storage, each needed
+    row once, valid (query, row) pairs only).  The implementation's workspace
+    traffic is not counted.  bound: the roofline the call is judged against."""
+    m, win, D = w.m, w.win, w.D
+    V = [min(w.n_c, (w.start_pos + t + 1) // w.ratio) for t in range(m)]
+    Wv = [min(win, w.start_pos + t + 1) for t in range(m)]
+    C = [min(w.K, v) for v in V]
+    pairs = sum(Wv) + sum(C)
+    n_new = w.n_c - w.first_new_row
+    dense = m > 1
+    if call == "quant_latent":
+        return {"bytes": B * n_new * D * 4, "flops": 0, "bound": "hbm"}
+    if call == "quant_index_k":
+        return {"bytes": B * n_new * w.Di * 4, "flops": 0, "bound": "hbm"}
+    if call == "ring_write":
+        return {"bytes": B * min(m, win) * D * 4, "flops": 0, "bound": "hbm"}
+    if call == "window_idx":
+        return {"bytes": B * m * win * 4, "flops": 0, "bound": "hbm"}
+    if call == "visible_idx":
+        return {"bytes": B * m * w.K * 4, "flops": 0, "bound": "hbm"}
+    if call == "index_scores_topk":
+        by = B * (max(V) * w.Di * 2 + m * w.Hi * w.Di * 2 + m * w.Hi * 4 + m * w.K * 4)
+        fl = B * sum(V) * w.Hi * w.Di * 2
+        return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm"}
+    if call == "sparse_attn_sink":
+        rows = (w.m if w.start_pos == 0 else (win + m if m > 1 else None))
+        row_bytes = (rows + w.n_c) * D * 2 if rows is not None else pairs * D * 2
+        by = B * (row_bytes + 2 * m * w.H * D * 2 + m * w.T * 4 + w.H * 4)
+        fl = B * pairs * w.H * D * 4
+        return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm"}
+    raise KeyError(call)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(workload, B, call):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = rec.get("entries", {}).get(f"{workload}/B{B}/{call}")
+    return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds):
+    """The oracle as it stands, single-threaded, on a bounded sample of the same
+    workload (one sequence; decode: whole steps, prefill: sampled queries)."""
+    import numpy as np  # noqa: PLC0415
+
+    import sckv_synth as synth  # noqa: PLC0415
+    from tests.helpers import oracle_step, sample_queries  # noqa: PLC0415
+
+    x = synth.make_inputs(w, 1)
+    tokens, t0 = 0, time.perf_counter()
+    if w.m == 1:
+        while True:
+            oracle_step(w, x, 0)
+            tokens += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        sample = f"{tokens} whole decode step(s) of one sequence"
+    else:
+        qs = sample_queries(w, extra=64, seed=1)
+        for t in qs:
+            oracle_step(w, x, 0, np.array([t]))
+            tokens += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        sample = f"{tokens} query token(s) of one {w.m}-token step (index lists + attention per query)"
+    el = time.perf_counter() - t0
+    return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample,
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode")
+    ap.add_argument("--instances", type=int, default=None, help="B independent sequences per step")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single", action="store_true", help="skip the B = 1 latency run (for profiling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); the multi-GPU "
+              "sharding of this path is a design note, not an implementation.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch  # noqa: PLC0415
+
+    import sckv_synth as synth  # noqa: PLC0415
+    from sparse_compressed_kv_e2m1_amd.step import PathState  # noqa: PLC0415
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    B = args.instances or DEFAULT_B[args.workload]
+    log(f"bench: workload {w.name} B={B}: generating inputs on the device")
+    x = synth.make_inputs(w, B, device="cuda")
+    st = PathState(w, x, B)
+    del x
+    st.setup()
+    calls = st.calls()
+    st._calls = calls
+    torch.cuda.synchronize()
+
+    log(f"bench: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        st.step()
+    torch.cuda.synchronize()
+
+    # whole steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        st.step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"bench: {args.steps} steps, {ms:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
+
+    # per call, events on the same stream around each library call
+    per = {name: [] for name, _ in calls}
+    for _ in range(args.steps):
+        for name, f in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            per[name].append((a, b))
+    torch.cuda.synchronize()
+    per_ms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in per.items()}
+    log("bench: per call ms " + json.dumps({k: round(v, 5) for k, v in per_ms.items()}))
+
+    # single sequence latency (B = 1) on the same workload
+    single = None
+    if B > 1 and not args.no_single:
+        x1 = synth.make_inputs(w, 1, device="cuda")
+        s1 = PathState(w, x1, 1)
+        s1.setup()
+        for _ in range(args.warmup):
+            s1.step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            s1.step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms1 = a.elapsed_time(b) / args.steps
+        single = {"instances": 1, "ms_per_step": round(ms1, 5), "tokens_per_s": round(w.m / (ms1 / 1e3), 1)}
+        del s1, x1
+
+    tokens = B * w.m
+    value = tokens / (ms / 1e3)
+    dom = max(per_ms, key=per_ms.get)
+    cnt = counts(w, B, dom)
+    if cnt["bound"] == "hbm":
+        achieved = cnt["bytes"] / (per_ms[dom] / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = cnt["flops"] / (per_ms[dom] / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
+    roof["kernel"] = dom
+    roof["ms_per_launch"] = round(per_ms[dom], 5)
+    roof["algorithmic_bytes"] = cnt["bytes"]
+    roof["algorithmic_flops"] = cnt["flops"]
+    roof["traffic"] = traffic_for(w.name, B, dom)
+
+    line = {
+        "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), device generator)",
+        "config": {"workload": describe(w), "instances": B, "tokens_per_step": tokens},
+        "roofline": roof,
+        "per_call_ms": {k: round(v, 5) for k, v in per_ms.items()},
+        "single_instance": single,
+    }
+    if not args.no_cpu_baseline:
+        log(f"bench: timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,41 +70,46 @@ WORKLOADS = {
 }
 
 
-def _gen(seed: int, workload: str, tensor: str) -> torch.Generator:
+def _gen(seed: int, workload: str, tensor: str, device: str = "cpu") -> torch.Generator:
     key = zlib.crc32(f"{seed}/{workload}/{tensor}".encode())
-    g = torch.Generator(device="cpu")
+    g = torch.Generator(device=device)
     g.manual_seed(key)
     return g
 
 
-def normal_f32(shape, seed: int, workload: str, tensor: str) -> torch.Tensor:
-    return torch.randn(tuple(shape), generator=_gen(seed, workload, tensor), dtype=torch.float32)
+def normal_f32(shape, seed: int, workload: str, tensor: str, device: str = "cpu") -> torch.Tensor:
+    return torch.randn(tuple(shape), generator=_gen(seed, workload, tensor, device), dtype=torch.float32,
+                       device=device)
 
 
-def normal_bf16(shape, seed: int, workload: str, tensor: str) -> torch.Tensor:
-    return normal_f32(shape, seed, workload, tensor).to(torch.bfloat16)
+def normal_bf16(shape, seed: int, workload: str, tensor: str, device: str = "cpu") -> torch.Tensor:
+    return normal_f32(shape, seed, workload, tensor, device).to(torch.bfloat16)
 
 
-def make_inputs(w: Workload, B: int = 1) -> dict:
+def make_inputs(w: Workload, B: int = 1, device: str = "cpu") -> dict:
     """Raw inputs of one step for B independent sequences of workload w (CPU tensors).
 
     Keys: q [B,m,H,D] bf16; sink [H] f32; kv_new [B,m,D] bf16 (this step's kv
     rows); ring [B,win,D] bf16 (the ring before the step; unused at
     start_pos 0); latent_raw [B,n_c,D] bf16 (compressed rows before the fp4
     round trip); and, when the workload has an indexer, iq [B,m,Hi,Di] bf16,
-    ik_raw [B,n_c,Di] bf16, iw [B,m,Hi] f32."""
-    s, n = w.seed, w.name
+    ik_raw [B,n_c,Di] bf16, iw [B,m,Hi] f32.
+
+    device="cpu" (the tests, the oracle) draws from torch's CPU generator;
+    device="cuda" draws the same distributions from the device generator
+    (different numbers; used for large bench batches)."""
+    s, n, d = w.seed, w.name, device
     out = {
-        "q": normal_bf16((B, w.m, w.H, w.D), s, n, "q"),
-        "sink": normal_f32((w.H,), s, n, "sink"),
-        "kv_new": normal_bf16((B, w.m, w.D), s, n, "kv_new"),
-        "ring": normal_bf16((B, w.win, w.D), s, n, "ring"),
-        "latent_raw": normal_bf16((B, w.n_c, w.D), s, n, "latent_raw"),
+        "q": normal_bf16((B, w.m, w.H, w.D), s, n, "q", d),
+        "sink": normal_f32((w.H,), s, n, "sink", d),
+        "kv_new": normal_bf16((B, w.m, w.D), s, n, "kv_new", d),
+        "ring": normal_bf16((B, w.win, w.D), s, n, "ring", d),
+        "latent_raw": normal_bf16((B, w.n_c, w.D), s, n, "latent_raw", d),
     }
     if w.Hi:
-        out["iq"] = normal_bf16((B, w.m, w.Hi, w.Di), s, n, "iq")
-        out["ik_raw"] = normal_bf16((B, w.n_c, w.Di), s, n, "ik_raw")
-        out["iw"] = normal_f32((B, w.m, w.Hi), s, n, "iw") * float((w.Hi * w.Di) ** -0.5)
+        out["iq"] = normal_bf16((B, w.m, w.Hi, w.Di), s, n, "iq", d)
+        out["ik_raw"] = normal_bf16((B, w.n_c, w.Di), s, n, "ik_raw", d)
+        out["iw"] = normal_f32((B, w.m, w.Hi), s, n, "iw", d) * float((w.Hi * w.Di) ** -0.5)
     return out
 
 

@@ -63,12 +63,12 @@ class PathState:
         self.n_new = w.n_c - self.first_new
         lat = inputs["latent_raw"]
         self.latent = dev(lat)
-        self.latent_new = dev(lat[:, self.first_new:])
+        self.latent_new = lat[:, self.first_new:].to(device).clone()  # a buffer of its own, never a view
         if w.Hi:
             self.iq = dev(inputs["iq"])
             self.iw = dev(inputs["iw"])
             self.ik = dev(inputs["ik_raw"])
-            self.ik_new = dev(inputs["ik_raw"][:, self.first_new:])
+            self.ik_new = inputs["ik_raw"][:, self.first_new:].to(device).clone()
             self.ws_index = sk.workspace(sk.SCKV_OP_INDEX_SCORES_TOPK, B, m, w.Hi, w.Di, w.n_c, device=device)
         self.T = w.T
         self.idx = torch.empty((B, m, self.T), dtype=torch.int32, device=device)
@@ -99,31 +99,39 @@ class PathState:
             for b in range(B):
                 sk.sckv_quant_rows(src[b], width, dst[b, self.first_new:], width, self.n_new, width, mode)
 
-    def step(self):
+    def calls(self):
+        """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
         m, win, D = w.m, w.win, w.D
-        # 1. the step's new compressed rows
-        self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16)
+        out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
         if w.Hi:
-            self._quant_new(self.ik_new, self.ik, w.Di, sk.SCKV_FP4_E8M0_B32)
-        # 2. decode: ring write before attention
+            out.append(("quant_index_k", lambda: self._quant_new(self.ik_new, self.ik, w.Di, sk.SCKV_FP4_E8M0_B32)))
         if self.mode == "ring":
-            sk.sckv_ring_write(self.kv_new, D, self.ring, win * D, B, 1, w.start_pos, win, D)
-        # 3. window columns
-        sk.sckv_window_idx(B, m, w.start_pos, win, self.idx, self.T)
-        # 4. compressed columns
+            out.append(("ring_write", lambda: sk.sckv_ring_write(self.kv_new, D, self.ring, win * D, B, 1,
+                                                                 w.start_pos, win, D)))
+        out.append(("window_idx", lambda: sk.sckv_window_idx(B, m, w.start_pos, win, self.idx, self.T)))
         if w.Hi:
-            sk.sckv_index_scores_topk(self.iq, self.ik, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K,
-                                      self.ra, self.idx, self.T, win, ws=self.ws_index)
+            out.append(("index_scores_topk", lambda: sk.sckv_index_scores_topk(
+                self.iq, self.ik, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K, self.ra, self.idx,
+                self.T, win, ws=self.ws_index)))
         else:
-            sk.sckv_visible_idx(B, m, w.start_pos, w.ratio, w.n_c, w.K, self.ra, self.idx, self.T, win)
-        # 5. attention
-        sk.sckv_sparse_attn_sink(self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink,
-                                 w.scale, B, m, w.H, D, self.out, ws=self.ws_attn)
-        # 6. ring after attention (fresh prefill, chunk)
+            out.append(("visible_idx", lambda: sk.sckv_visible_idx(B, m, w.start_pos, w.ratio, w.n_c, w.K, self.ra,
+                                                                   self.idx, self.T, win)))
+        out.append(("sparse_attn_sink", lambda: sk.sckv_sparse_attn_sink(
+            self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink, w.scale, B, m, w.H, D,
+            self.out, ws=self.ws_attn)))
         if self.mode == "fresh":
-            sk.sckv_ring_write(self.rows_a, m * D, self.ring, win * D, B, m, w.start_pos, win, D)
+            out.append(("ring_write", lambda: sk.sckv_ring_write(self.rows_a, m * D, self.ring, win * D, B, m,
+                                                                 w.start_pos, win, D)))
         elif self.mode == "chunk":
-            rows = self.rows_a[:, win:]
-            sk.sckv_ring_write(rows, (win + m) * D, self.rows_a, (win + m) * D, B, m, w.start_pos, win, D)
+            out.append(("ring_write", lambda: sk.sckv_ring_write(self.rows_a[:, win:], (win + m) * D, self.rows_a,
+                                                                 (win + m) * D, B, m, w.start_pos, win, D)))
+        return out
+
+    def step(self):
+        """One pass of the hot path (steps 1-6 of the module doc)."""
+        if not hasattr(self, "_calls"):
+            self._calls = self.calls()
+        for _, f in self._calls:
+            f()
         return self.out
