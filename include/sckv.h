@@ -150,7 +150,7 @@ int sckv_visible_idx(int B, int64_t m, int64_t start_pos, int ratio, int64_t n_c
  *            entries of invisible rows are left unchanged.
  *   ws       device workspace of at least
  *            sckv_workspace_bytes(SCKV_OP_INDEX_SCORES_TOPK, B, m, Hi, Di, n_c).
- * Supported: Hi a power of two <= 64, Di in {32, 64, 128, 256}, n_c < 2^31.
+ * Supported: Hi a power of two <= 64, Di in {32, 64, 128, 256}, n_c <= 65536.
  * Exactness note: the binary32 dot equals the exact dot whenever the exact
  * value is a binary32 value, which holds when the 2*Di products' block scales
  * lie within a few powers of two of each other (always the case for

@@ -10,20 +10,22 @@
 //
 // Design (gfx950).  One workgroup = one query x a range of 32-row chunks of
 // its index list.  All heads (padded to 32 or 64) form the MFMA M dimension,
-// so every gathered row byte feeds every head.  The NW waves split the head
-// dimension D: wave w owns dims [w*DW, (w+1)*DW) of Q, of every row and of O.
-// Per chunk:
-//   1. each lane resolves one row pointer (row = lane % 32) and loads its wave's
-//      dims of that row straight from HBM in MFMA B layout (16 B per lane per
-//      k-step);
-//   2. S_w = Q[:, dims_w] . R[:, dims_w]^T on the matrix cores;
-//   3. the NW partial S tiles meet in LDS; every wave sums them in the same
-//      order, so all waves hold bit-identical logits, and reads them back in
-//      MFMA A layout (head = lane % 32);
-//   4. online softmax per head (running max starts at the sink logit), P in
-//      bf16;
-//   5. the wave's row slice goes to wave-private LDS transposed (rows along
-//      the contraction) and O[:, dims_w] += P . R[:, dims_w] on the matrix cores.
+// so every gathered row byte feeds every head.  NW waves split the head
+// dimension D: wave w owns dims [w*DW, (w+1)*DW) of Q (in registers) and of O
+// (in accumulators).  Per chunk:
+//   1. rows arrive by asynchronous global->LDS copies (global_load_lds_dwordx4:
+//      one instruction moves one whole 1 KiB row, fully coalesced), issued two
+//      chunks ahead into a 3-stage ring; each wave brings in 32/NW rows;
+//   2. S_w = Q[:, dims_w] . R[:, dims_w]^T on the matrix cores (B operand read
+//      from the row-major stage);
+//   3. the NW partial logit tiles meet in LDS; wave w sums the tiles of its own
+//      HP/NW heads (fixed order) and runs the online softmax for them in base 2
+//      (the running max starts at the sink logit and only moves when a logit
+//      exceeds it by more than 2^8, so rescaling is rare); P goes back to LDS
+//      in bf16;
+//   4. every wave reads all of P (A layout) and O[:, dims_w] += P . R[:, dims_w],
+//      the B operand coming from the same row-major stage through the
+//      transposing LDS read (ds_read_b64_tr_b16), so no second copy of the rows.
 // A query's chunks may be split over several workgroups; their partial
 // (max, sum, O) are merged by a small combine kernel that adds the sink once.
 #include "mfma.h"
@@ -33,20 +35,46 @@ namespace sckv {
 namespace {
 
 constexpr int CHUNK = 32;
-constexpr int SX_STRIDE = 36;  // floats per head row of a partial S tile (32 + pad, 16-byte aligned)
-constexpr int RT_STRIDE = 40;  // bf16 per dim row of a transposed chunk (32 + pad, 16-byte aligned)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float STALE_MAX = 8.0f;  // base-2 slack before the running max moves
+constexpr int MAX_CPS = 64;        // chunks one workgroup handles at most (its index range sits in LDS)
 
 template <int MT, int DW, int NW>
 struct AttnShape {
-    static constexpr int HP = MT * 32;           // padded heads
+    static constexpr int HP = MT * 32;             // padded heads
     static constexpr int D = DW * NW;
-    static constexpr int KS = DW / 16;           // k-steps of Q.R^T per wave
-    static constexpr int NT = DW / 32;           // 32-wide output tiles per wave
-    static constexpr int SX_FLOATS = 2 * NW * HP * SX_STRIDE;  // double-buffered partial S
-    static constexpr int RT_HALVES = NW * DW * RT_STRIDE;      // transposed chunk, per wave
-    static constexpr size_t LDS_BYTES = (size_t)SX_FLOATS * 4 + (size_t)RT_HALVES * 2;
+    static constexpr int KS = DW / 16;             // k-steps of Q.R^T per wave
+    static constexpr int NT = DW / 32;             // 32-wide output tiles per wave
+    static constexpr int RPW = CHUNK / NW;         // rows each wave copies in per chunk
+    static constexpr int PD = (RPW <= 16) ? 2 : 1; // chunks in flight ahead of the one computed
+    static constexpr int NST = PD + 1;             // stages in the ring
+    static constexpr int RS = 2 * D + 32;          // bytes per row in a stage (32-byte pad: no bank conflicts)
+    static constexpr int STAGE = CHUNK * RS;
+    static constexpr int HW = HP / NW;             // heads whose softmax one wave owns
+    static constexpr int LPH = 64 / HW;            // lanes per owned head
+    static constexpr int VPL = CHUNK / LPH;        // logits per lane in the softmax
+    static constexpr int SXS = CHUNK + 4;          // floats per head row of a partial-logit tile
+    static constexpr int PS = CHUNK + 8;           // bf16 per head row of P
+    static constexpr int OFF_SX = NST * STAGE;
+    static constexpr int OFF_P = OFF_SX + NW * HP * SXS * 4;
+    static constexpr int OFF_ALPHA = OFF_P + HP * PS * 2;
+    static constexpr int OFF_L = OFF_ALPHA + HP * 4;
+    static constexpr int OFF_FLAG = OFF_L + HP * 4;
+    static constexpr int OFF_IDX = OFF_FLAG + 16;
+    static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
+    static_assert(VPL % 4 == 0 && LPH >= 1 && LPH <= 64, "softmax split");
 };
+
+// Wait until at most n of this wave's row copies are in flight (n uniform, one of 0, RPW, 2*RPW).
+template <int RPW>
+__device__ __forceinline__ void wait_rows(int n) {
+    if (n == 0)
+        wait_vmcnt<0>();
+    else if (n == RPW)
+        wait_vmcnt<RPW>();
+    else
+        wait_vmcnt<(2 * RPW < 64 ? 2 * RPW : 63)>();
+}
 
 template <int MT, int DW, int NW>
 __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
@@ -56,26 +84,28 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
     using S = AttnShape<MT, DW, NW>;
     constexpr int D = S::D;
-    extern __shared__ __align__(16) unsigned char lds_raw[];
-    float* sx = reinterpret_cast<float*>(lds_raw);
-    uint16_t* rt_all = reinterpret_cast<uint16_t*>(lds_raw + (size_t)S::SX_FLOATS * 4);
+    extern __shared__ __align__(16) unsigned char lds[];
+    float* sx = reinterpret_cast<float*>(lds + S::OFF_SX);
+    uint16_t* pl = reinterpret_cast<uint16_t*>(lds + S::OFF_P);
+    float* alpha_l = reinterpret_cast<float*>(lds + S::OFF_ALPHA);
+    float* lsum_l = reinterpret_cast<float*>(lds + S::OFF_L);
+    int* flags = reinterpret_cast<int*>(lds + S::OFF_FLAG);
+    const uint32_t lds0 = lds_offset(lds);
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r_lane = lane & 31;   // row of this lane in B layout / head in A layout
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r_lane = lane & 31;  // row of this lane in B layout / head in A layout
     const int half = lane >> 5;
     const int64_t qi = blockIdx.x / nsplit;
     const int split = (int)(blockIdx.x - qi * nsplit);
     const int64_t b = qi / m;
     const int dim0 = wave * DW;
-    uint16_t* rt = rt_all + wave * DW * RT_STRIDE;
-
     const uint16_t* rows_a_b = rows_a + b * ra * D;
     const uint16_t* rows_b_b = rows_b ? rows_b + b * rb * D : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
+    const uint16_t* qrow = q + qi * (int64_t)H * D;
 
     // ---- Q slice in A layout: head mt*32 + r_lane, dims dim0 + ks*16 + half*8 + 0..7
-    const uint16_t* qrow = q + qi * (int64_t)H * D;
     bf16x8 qa[MT][S::KS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -86,14 +116,12 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
                                            : u32x4{0, 0, 0, 0});
     }
 
-    // ---- running softmax state per head (A layout: head mt*32 + r_lane)
-    float m_run[MT], l_run[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int h = mt * 32 + r_lane;
-        m_run[mt] = (h < H) ? sink[h] * LOG2E : 0.0f;
-        l_run[mt] = (nsplit == 1) ? 1.0f : 0.0f;  // e^(sink - M) at M = sink; splits add the sink when merged
-    }
+    // ---- softmax state of the head this lane helps own: hr, rows r0 .. r0+VPL-1
+    const int hr = S::HW * wave + lane / S::LPH;
+    const int r0 = (lane % S::LPH) * S::VPL;
+    float m_run = (hr < H) ? sink[hr] * LOG2E : 0.0f;  // base-2 running max, starting at the sink
+    float l_run = (nsplit == 1) ? 1.0f : 0.0f;          // e^(sink - M) at M = sink; splits add it when merged
+
     f32x16 o[MT][S::NT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
@@ -104,154 +132,196 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     const int c_begin = split * chunks_per_split;
     int c_end = c_begin + chunks_per_split;
     c_end = c_end < nchunks ? c_end : nchunks;
-    int buf = 0;
+
+    // Copy chunk c's rows (this wave's share) into its stage; returns the chunk's
+    // valid-row mask (identical in every wave).  Invalid rows of a partly valid
+    // chunk copy this query's first q row instead (finite data; masked later).
+    // This workgroup's slice of the index list, staged once in LDS.
+    int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
+    {
+        const int e0 = c_begin * CHUNK;
+        const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
+        for (int i = threadIdx.x; i < (c_end - c_begin) * CHUNK; i += NW * 64) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
+        __syncthreads();
+    }
+    auto row_src = [&](int32_t iv) -> const uint16_t* {
+        const bool valid = (iv >= 0) && ((int64_t)iv < ra + rb);
+        return !valid ? qrow : (((int64_t)iv < ra) ? rows_a_b + (int64_t)iv * D : rows_b_b + ((int64_t)iv - ra) * D);
+    };
+    // Copy chunk c's rows (this wave's share) into its stage; returns the chunk's
+    // valid-row mask (identical in every wave).  Invalid rows of a partly valid
+    // chunk copy this query's first q row instead (finite data; masked later).
+    auto issue = [&](int c) -> uint32_t {
+        const int32_t* ic = idx_l + (c - c_begin) * CHUNK;
+        const int32_t mine = ic[r_lane];
+        const uint32_t mask =
+            (uint32_t)(__ballot((mine >= 0) && ((int64_t)mine < ra + rb)) & 0xffffffffull);
+        if (mask) {
+            const uint32_t st = lds0 + (uint32_t)((c % S::NST) * S::STAGE);
+#pragma unroll
+            for (int rr = 0; rr < S::RPW; ++rr) {
+                const int r = wave * S::RPW + rr;
+                if (lane < D / 8) dma16(row_src(ic[r]) + lane * 8, st + (uint32_t)(r * S::RS));
+            }
+        }
+        return mask;
+    };
+
+    uint32_t mk[S::PD + 1];
+#pragma unroll
+    for (int j = 0; j < S::PD; ++j) mk[j] = (c_begin + j < c_end) ? issue(c_begin + j) : 0u;
 
     for (int c = c_begin; c < c_end; ++c) {
-        // 1. resolve this lane's row and load the wave's dims of it
-        const int e = c * CHUNK + r_lane;
-        const int32_t iv = (e < T) ? idx_q[e] : -1;
-        const bool valid = (iv >= 0) && ((int64_t)iv < ra + rb);
-        const uint64_t vmask = __ballot(valid) & 0xffffffffull;  // rows 0..31 (both halves agree)
-        if (vmask == 0) continue;  // identical decision in every wave of the block
-        const uint16_t* rp = nullptr;
-        if (valid) rp = ((int64_t)iv < ra) ? rows_a_b + (int64_t)iv * D : rows_b_b + ((int64_t)iv - ra) * D;
-        u32x4 rr[S::KS];
+        // chunk c's copies done (later chunks' copies may still fly), then everyone's
+        int after = 0;
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
-            rr[ks] = valid ? load16(rp + dim0 + ks * 16 + half * 8) : u32x4{0, 0, 0, 0};
+        for (int j = 1; j < S::PD; ++j) after += mk[j] ? S::RPW : 0;
+        if (mk[0]) wait_rows<S::RPW>(after);
+        __syncthreads();
+        mk[S::PD] = (c + S::PD < c_end) ? issue(c + S::PD) : 0u;  // into the stage chunk c-1 used
+        const uint32_t mask = mk[0];
+#pragma unroll
+        for (int j = 0; j < S::PD; ++j) mk[j] = mk[j + 1];
+        if (mask == 0) continue;
+        const unsigned char* stp = lds + (c % S::NST) * S::STAGE;
 
         // 2. partial logits over this wave's dims
         f32x16 sp[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            sp[mt] = zero16();
+        for (int mt = 0; mt < MT; ++mt) sp[mt] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < S::KS; ++ks) sp[mt] = mfma32x32x16(qa[mt][ks], as_bf16x8(rr[ks]), sp[mt]);
+        for (int ks = 0; ks < S::KS; ++ks) {
+            const bf16x8 bk =
+                *reinterpret_cast<const bf16x8*>(stp + r_lane * S::RS + (dim0 + ks * 16 + half * 8) * 2);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) sp[mt] = mfma32x32x16(qa[mt][ks], bk, sp[mt]);
         }
-        // 3. exchange partial tiles: sx[buf][wave][head][row]
-        float* sxb = sx + buf * (NW * S::HP * SX_STRIDE);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                sxb[(wave * S::HP + mt * 32 + d_row(i, lane)) * SX_STRIDE + r_lane] = sp[mt][i];
-        // transposed copy of this wave's rows for P.R (wave-private)
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const int d = ks * 16 + half * 8 + e2 * 2;
-                rt[d * RT_STRIDE + r_lane] = (uint16_t)(rr[ks][e2] & 0xffffu);
-                rt[(d + 1) * RT_STRIDE + r_lane] = (uint16_t)(rr[ks][e2] >> 16);
-            }
+                sx[(wave * S::HP + mt * 32 + d_row(i, lane)) * S::SXS + r_lane] = sp[mt][i];
         __syncthreads();
 
-        // full logits in A layout: head mt*32 + r_lane, rows kr*16 + half*8 + 0..7
-        float x[MT][2][8];
+        // 3. this wave's heads: sum the NW partial tiles (fixed order), online softmax
+        float x[S::VPL];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < S::VPL; ++j) x[j] = 0.0f;
 #pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
+        for (int ww = 0; ww < NW; ++ww) {
+            const float* src = sx + (ww * S::HP + hr) * S::SXS + r0;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) x[mt][kr][j] = 0.0f;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) {
-                    const float* src = sxb + (ww * S::HP + mt * 32 + r_lane) * SX_STRIDE + kr * 16 + half * 8;
-                    const float4 a0 = *reinterpret_cast<const float4*>(src);
-                    const float4 a1 = *reinterpret_cast<const float4*>(src + 4);
-                    x[mt][kr][0] += a0.x;
-                    x[mt][kr][1] += a0.y;
-                    x[mt][kr][2] += a0.z;
-                    x[mt][kr][3] += a0.w;
-                    x[mt][kr][4] += a1.x;
-                    x[mt][kr][5] += a1.y;
-                    x[mt][kr][6] += a1.z;
-                    x[mt][kr][7] += a1.w;
-                }
+            for (int j4 = 0; j4 < S::VPL / 4; ++j4) {
+                const float4 a = *reinterpret_cast<const float4*>(src + 4 * j4);
+                x[4 * j4 + 0] += a.x;
+                x[4 * j4 + 1] += a.y;
+                x[4 * j4 + 2] += a.z;
+                x[4 * j4 + 3] += a.w;
             }
-        buf ^= 1;
-
-        // 4. online softmax in base 2
-        bf16x8 pa[MT][2];
-        float alpha[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float cmax = -INFINITY;
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int row = kr * 16 + half * 8 + j;
-                    const float v = ((vmask >> row) & 1ull) ? x[mt][kr][j] * scale_log2 : -INFINITY;
-                    x[mt][kr][j] = v;
-                    cmax = fmaxf(cmax, v);
-                }
-            cmax = fmaxf(cmax, shfl_xor32(cmax));
-            const float m_new = fmaxf(m_run[mt], cmax);
-            alpha[mt] = exp2f(m_run[mt] - m_new);
-            float psum = 0.0f;
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
-                u32x4 packed;
-#pragma unroll
-                for (int j2 = 0; j2 < 4; ++j2) {
-                    const uint32_t p0 = f32_to_bf16_bits(exp2f(x[mt][kr][2 * j2] - m_new));
-                    const uint32_t p1 = f32_to_bf16_bits(exp2f(x[mt][kr][2 * j2 + 1] - m_new));
-                    psum += bf16_bits_to_f32(p0) + bf16_bits_to_f32(p1);
-                    packed[j2] = p0 | (p1 << 16);
-                }
-                pa[mt][kr] = as_bf16x8(packed);
-            }
-            psum += shfl_xor32(psum);
-            l_run[mt] = l_run[mt] * alpha[mt] + psum;
-            m_run[mt] = m_new;
         }
-        // rescale O rows (D layout heads) by their head's alpha
+        float cmax = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < S::VPL; ++j) {
+            x[j] = ((mask >> (r0 + j)) & 1u) ? x[j] * scale_log2 : -INFINITY;
+            cmax = fmaxf(cmax, x[j]);
+        }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float a = __shfl(alpha[mt], d_row(i, lane), 64);
+        for (int off = 1; off < S::LPH; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
+        const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
+        const float alpha = exp2f(m_run - m_new);
+        float psum = 0.0f;
+        uint32_t pk[S::VPL / 2];
 #pragma unroll
-                for (int nt = 0; nt < S::NT; ++nt) o[mt][nt][i] *= a;
-            }
+        for (int j = 0; j < S::VPL; j += 2) {
+            const uint32_t p0 = f32_to_bf16_bits(exp2f(x[j] - m_new));
+            const uint32_t p1 = f32_to_bf16_bits(exp2f(x[j + 1] - m_new));
+            psum += bf16_bits_to_f32(p0) + bf16_bits_to_f32(p1);
+            pk[j / 2] = p0 | (p1 << 16);
+        }
+#pragma unroll
+        for (int off = 1; off < S::LPH; off <<= 1) psum += __shfl_xor(psum, off, 64);
+        l_run = l_run * alpha + psum;
+        const bool moved = m_new != m_run;
+        m_run = m_new;
+        {
+            uint16_t* dst = pl + hr * S::PS + r0;
+#pragma unroll
+            for (int j4 = 0; j4 < S::VPL / 4; ++j4)
+                *reinterpret_cast<uint2*>(dst + 4 * j4) = make_uint2(pk[2 * j4], pk[2 * j4 + 1]);
+        }
+        if (lane % S::LPH == 0) alpha_l[hr] = alpha;
+        const uint64_t any_moved = __ballot(moved);
+        if (lane == 0) flags[wave] = any_moved != 0;
+        __syncthreads();
 
-        // 5. O[:, dims_w] += P . R[:, dims_w]
-        wave_lds_sync();
+        // 4. O[:, dims_w] (+)= P . R[:, dims_w]
+        bool rescale = false;
 #pragma unroll
-        for (int nt = 0; nt < S::NT; ++nt) {
-            bf16x8 rb2[2];
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr)
-                rb2[kr] = as_bf16x8(
-                    *reinterpret_cast<const u32x4*>(rt + (nt * 32 + r_lane) * RT_STRIDE + kr * 16 + half * 8));
+        for (int ww = 0; ww < NW; ++ww) rescale |= flags[ww] != 0;
+        if (rescale) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-                for (int kr = 0; kr < 2; ++kr) o[mt][nt] = mfma32x32x16(pa[mt][kr], rb2[kr], o[mt][nt]);
+                for (int ig = 0; ig < 4; ++ig) {
+                    const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + mt * 32 + ig * 8 + half * 4);
+#pragma unroll
+                    for (int nt = 0; nt < S::NT; ++nt) {
+                        o[mt][nt][ig * 4 + 0] *= a4.x;
+                        o[mt][nt][ig * 4 + 1] *= a4.y;
+                        o[mt][nt][ig * 4 + 2] *= a4.z;
+                        o[mt][nt][ig * 4 + 3] *= a4.w;
+                    }
+                }
         }
-        wave_lds_sync();
+        bf16x8 pa[MT][2];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int kr = 0; kr < 2; ++kr)
+                pa[mt][kr] = *reinterpret_cast<const bf16x8*>(pl + (mt * 32 + r_lane) * S::PS + kr * 16 + half * 8);
+        const int g = lane >> 4;
+        const int quad = (lane & 15) >> 2;
+        const int a4l = lane & 3;
+#pragma unroll
+        for (int nt = 0; nt < S::NT; ++nt) {
+            const int dcol = dim0 + nt * 32 + (g & 1) * 16 + 4 * a4l;
+#pragma unroll
+            for (int kr = 0; kr < 2; ++kr) {
+                const int row = kr * 16 + (g >> 1) * 8 + quad;
+                const i16x4 lo = lds_read_tr16(stp + row * S::RS + dcol * 2);
+                const i16x4 hi = lds_read_tr16(stp + (row + 4) * S::RS + dcol * 2);
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) o[mt][nt] = mfma32x32x16(pa[mt][kr], bv, o[mt][nt]);
+            }
+        }
     }
 
     // ---- epilogue
     if (nsplit == 1) {
+        if (lane % S::LPH == 0) lsum_l[hr] = l_run;
+        __syncthreads();
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int h = mt * 32 + d_row(i, lane);
-                const float inv = 1.0f / __shfl(l_run[mt], d_row(i, lane), 64);
-                if (h < H) {
-                    uint16_t* orow = out + (qi * H + h) * (int64_t)D + dim0;
+            for (int ig = 0; ig < 4; ++ig) {
+                const float4 l4 = *reinterpret_cast<const float4*>(lsum_l + mt * 32 + ig * 8 + half * 4);
+                const float inv[4] = {1.0f / l4.x, 1.0f / l4.y, 1.0f / l4.z, 1.0f / l4.w};
 #pragma unroll
-                    for (int nt = 0; nt < S::NT; ++nt)
-                        orow[nt * 32 + r_lane] = (uint16_t)f32_to_bf16_bits(o[mt][nt][i] * inv);
+                for (int e = 0; e < 4; ++e) {
+                    const int h = mt * 32 + ig * 8 + half * 4 + e;
+                    if (h < H) {
+                        uint16_t* orow = out + (qi * H + h) * (int64_t)D + dim0;
+#pragma unroll
+                        for (int nt = 0; nt < S::NT; ++nt)
+                            orow[nt * 32 + r_lane] = (uint16_t)f32_to_bf16_bits(o[mt][nt][ig * 4 + e] * inv[e]);
+                    }
                 }
             }
     } else {
         const int64_t pbase = (qi * nsplit + split) * (int64_t)H;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int h = mt * 32 + d_row(i, lane);
@@ -261,11 +331,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
                     for (int nt = 0; nt < S::NT; ++nt) prow[nt * 32 + r_lane] = o[mt][nt][i];
                 }
             }
-            const int h = mt * 32 + r_lane;
-            if (wave == 0 && half == 0 && h < H) {
-                part_ml[(pbase + h) * 2 + 0] = m_run[mt];
-                part_ml[(pbase + h) * 2 + 1] = l_run[mt];
-            }
+        if (lane % S::LPH == 0 && hr < H) {
+            part_ml[(pbase + hr) * 2 + 0] = m_run;
+            part_ml[(pbase + hr) * 2 + 1] = l_run;
         }
     }
 }
@@ -305,7 +373,8 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     int64_t want = (256 + nq - 1) / nq;
     if (want > nchunks) want = nchunks;
     if (want < 1) want = 1;
-    const int cps = (int)((nchunks + want - 1) / want);
+    int cps = (int)((nchunks + want - 1) / want);
+    if (cps > MAX_CPS) cps = MAX_CPS;
     *chunks_per_split = cps;
     *nsplit = (nchunks + cps - 1) / cps;
 }

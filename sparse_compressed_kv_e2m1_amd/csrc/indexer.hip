@@ -80,13 +80,14 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
                 }
             amax = fmaxf(amax, shfl_xor32(amax));
             const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
+            const float inv_s = pow2_reciprocal(s);
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     uint32_t v = raw[2 * c + kk][e];
-                    uint32_t lo = fp4_value_bits(bf16_bits_to_f32(v & 0xffffu), s);
-                    uint32_t hi = fp4_value_bits(bf16_bits_to_f32(v >> 16), s);
+                    uint32_t lo = fp4_value_bits_pow2(bf16_bits_to_f32(v & 0xffffu), s, inv_s);
+                    uint32_t hi = fp4_value_bits_pow2(bf16_bits_to_f32(v >> 16), s, inv_s);
                     raw[2 * c + kk][e] = lo | (hi << 16);
                 }
         }
@@ -109,12 +110,22 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     uint16_t* kout = keys + qi * n_c;
     uint16_t* sout = scores ? scores + qi * n_c : nullptr;
 
-    for (int64_t s0 = row0 + (int64_t)wave * 32; s0 < row_end; s0 += SCORE_WAVES * 32) {
+    // k rows of a 32-row tile in B layout: row s0 + lane%32, dims ks*16 + (lane/32)*8 + 0..7;
+    // the next tile's rows are requested before this tile is consumed
+    auto load_tile = [&](int64_t s0, u32x4* kr) {
         const int64_t s = s0 + (lane & 31);
-        u32x4 kr[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             kr[ks] = (s < n_c) ? load16(kb + s * DI + ks * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+    };
+    int64_t s0 = row0 + (int64_t)wave * 32;
+    u32x4 kr[KS], kn[KS];
+    if (s0 < row_end) load_tile(s0, kn);
+    for (; s0 < row_end; s0 += SCORE_WAVES * 32) {
+        const int64_t s = s0 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kr[ks] = kn[ks];
+        if (s0 + SCORE_WAVES * 32 < row_end) load_tile(s0 + SCORE_WAVES * 32, kn);
         f32x16 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -161,115 +172,130 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     }
 }
 
-// ---- block-wide scans (LDS, Hillis-Steele), all threads of the block call them
+// ---- top-k: one block per query, keys held in registers
+//
+// Thread t owns the KPT consecutive rows [t*KPT, t*KPT + KPT).  The K-th
+// largest key tau is built bit by bit (16 rounds: keep bit b when at least K
+// keys are >= the candidate), counting in registers and summing over the
+// block; then the rows with key > tau and the first (K - #greater) rows with
+// key == tau (lowest rows first) are written in ascending row order with two
+// block prefix sums.  No atomics; missing rows hold key 0, below every real
+// key (finite scores have keys >= 0x007f).
 
-// Inclusive prefix sum over the block's threads of `x`; `buf` holds blockDim.x words.
-__device__ uint32_t block_inclusive_scan(uint32_t x, uint32_t* buf) {
-    const int tid = threadIdx.x;
-    buf[tid] = x;
-    __syncthreads();
-    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
-        uint32_t add = (tid >= off) ? buf[tid - off] : 0u;
-        __syncthreads();
-        buf[tid] += add;
-        __syncthreads();
-    }
-    uint32_t r = buf[tid];
-    __syncthreads();
-    return r;
+constexpr int TOPK_WAVES = TOPK_THREADS / 64;
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
 }
 
-// Given a 256-bin histogram in hist and a target count `need` (>= 1, <= total),
-// find the bin b such that (# in bins > b) < need <= (# in bins >= b).  Returns
-// b and writes the count strictly above b into *above.  Uses threads 0..255 of
-// the block for the scan; every thread calls it.
-__device__ int find_threshold_bin(const uint32_t* hist, uint32_t need, uint32_t* buf, uint32_t* shared_out,
-                                  uint32_t* above) {
-    const int tid = threadIdx.x;
-    // reversed so the prefix over i is the suffix over bins 255 - i .. 255
-    uint32_t x = (tid < 256) ? hist[255 - tid] : 0u;
-    uint32_t incl = block_inclusive_scan(x, buf);
-    uint32_t excl = incl - x;
-    if (tid < 256 && incl >= need && excl < need) {
-        shared_out[0] = 255 - tid;
-        shared_out[1] = excl;
-    }
+// Sum over the block; buf holds TOPK_WAVES words and must not be reused by the
+// very next call (callers alternate two buffers).
+__device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* buf) {
+    const uint32_t w = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = w;
     __syncthreads();
-    int bin = (int)shared_out[0];
-    *above = shared_out[1];
-    __syncthreads();
-    return bin;
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < TOPK_WAVES; ++i) t += buf[i];
+    return t;
 }
 
-// One block per query: select the K largest keys among rows 0 .. vis-1 (ties
-// to the lower row) and write offset + row in ascending row order.
+// Exclusive prefix sum over the block's threads.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tot) {
+    const int lane = threadIdx.x & 63;
+    uint32_t incl = x;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63) tot[threadIdx.x >> 6] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int i = 0; i < (int)(threadIdx.x >> 6); ++i) before += tot[i];
+    __syncthreads();
+    return before + incl - x;
+}
+
+template <int KPT>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const uint16_t* __restrict__ keys, int64_t n_c,
                                                             int64_t m, int ratio, int64_t start_pos, int K,
                                                             int32_t offset, int32_t* __restrict__ idx, int64_t ld,
                                                             int64_t col0) {
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t buf[TOPK_THREADS];
-    __shared__ uint32_t sh[2];
+    __shared__ uint32_t red[2][TOPK_WAVES];
+    __shared__ uint32_t tot[TOPK_WAVES];
     const int tid = threadIdx.x;
     const int64_t qi = blockIdx.x;
     const int64_t t = qi % m;
     int64_t vis = (start_pos + t + 1) / ratio;
     vis = vis < n_c ? vis : n_c;
     int32_t* out = idx + qi * ld + col0;
-    const uint16_t* kp = keys + qi * n_c;
-
-    if (tid < 2) sh[tid] = 0u;
     if (vis <= K) {
         for (int j = tid; j < K; j += TOPK_THREADS) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
         return;
     }
-    // pass 1: high byte
-    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0u;
-    __syncthreads();
-    for (int64_t s = tid; s < vis; s += TOPK_THREADS) atomicAdd(&hist[kp[s] >> 8], 1u);
-    __syncthreads();
-    uint32_t above1;
-    const int b1 = find_threshold_bin(hist, (uint32_t)K, buf, sh, &above1);
-    // pass 2: low byte among keys with high byte b1
-    for (int i = tid; i < 256; i += TOPK_THREADS) hist[i] = 0u;
-    __syncthreads();
-    for (int64_t s = tid; s < vis; s += TOPK_THREADS) {
-        uint32_t key = kp[s];
-        if ((int)(key >> 8) == b1) atomicAdd(&hist[key & 0xffu], 1u);
-    }
-    __syncthreads();
-    uint32_t above0;
-    const int b0 = find_threshold_bin(hist, (uint32_t)K - above1, buf, sh, &above0);
-    const uint32_t tau = ((uint32_t)b1 << 8) | (uint32_t)b0;
-    const uint32_t need_eq = (uint32_t)K - above1 - above0;  // >= 1
+    const uint16_t* kp = keys + qi * n_c;
+    const int64_t s0 = (int64_t)tid * KPT;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = (s0 + j < vis) ? (uint32_t)kp[s0 + j] : 0u;
 
-    // ordered compaction: thread tid owns rows [tid*seg, (tid+1)*seg)
-    const int64_t seg = (vis + TOPK_THREADS - 1) / TOPK_THREADS;
-    const int64_t lo = (int64_t)tid * seg;
-    const int64_t hi = (lo + seg < vis) ? lo + seg : vis;
-    uint32_t gt = 0, eq = 0;
-    for (int64_t s = lo; s < hi; ++s) {
-        uint32_t key = kp[s];
-        gt += key > tau;
-        eq += key == tau;
+    uint32_t tau = 0;
+    int rb = 0;
+#pragma unroll 1
+    for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t cand = tau | (1u << bit);
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += key[j] >= cand;
+        const uint32_t total = block_sum(c, red[rb]);
+        rb ^= 1;
+        if (total >= (uint32_t)K) tau = cand;
     }
-    const uint32_t eq_incl = block_inclusive_scan(eq, buf);
-    const uint32_t eq_base = eq_incl - eq;
-    uint32_t take_eq = (need_eq > eq_base) ? (need_eq - eq_base) : 0u;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gt += key[j] > tau;
+        eq += key[j] == tau;
+    }
+    const uint32_t gt_total = block_sum(gt, red[rb]);
+    const uint32_t need_eq = (uint32_t)K - gt_total;  // >= 1 by the choice of tau
+    const uint32_t eq_before = block_excl_scan(eq, tot);
+    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
     take_eq = take_eq < eq ? take_eq : eq;
-    const uint32_t sel = gt + take_eq;
-    const uint32_t sel_incl = block_inclusive_scan(sel, buf);
-    uint32_t pos = sel_incl - sel;
+    uint32_t pos = block_excl_scan(gt + take_eq, tot);
     uint32_t eq_seen = 0;
-    for (int64_t s = lo; s < hi; ++s) {
-        uint32_t key = kp[s];
-        bool take = key > tau;
-        if (key == tau) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = key[j];
+        bool take = k > tau;
+        if (k == tau) {
             take = eq_seen < take_eq;
             ++eq_seen;
         }
-        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s);
+        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s0 + j);
     }
+}
+
+void launch_topk(const uint16_t* keys, int64_t nq, int64_t n_c, int64_t m, int ratio, int64_t start_pos, int K,
+                 int32_t offset, int32_t* idx, int64_t ld, int64_t col0, hipStream_t s) {
+    const int64_t kpt = (n_c + TOPK_THREADS - 1) / TOPK_THREADS;
+#define SCKV_TOPK(KPT)                                                                                        \
+    topk_kernel<KPT><<<dim3((unsigned)nq), dim3(TOPK_THREADS), 0, s>>>(keys, n_c, m, ratio, start_pos, K, offset, \
+                                                                        idx, ld, col0)
+    if (kpt <= 2)
+        SCKV_TOPK(2);
+    else if (kpt <= 8)
+        SCKV_TOPK(8);
+    else if (kpt <= 32)
+        SCKV_TOPK(32);
+    else if (kpt <= 64)
+        SCKV_TOPK(64);
+    else
+        SCKV_TOPK(128);
+#undef SCKV_TOPK
 }
 
 template <int MT, int DI>
@@ -315,16 +341,15 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
     if (B == 0 || m == 0 || K == 0) return SCKV_OK;
     if (!idx) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null idx");
     if (ld < col0 + K) return fail(SCKV_EINVAL, "sckv_index_scores_topk: ld < col0 + K");
-    if (n_c >= 0x7fffffffLL || (int64_t)offset + n_c > 0x7fffffffLL)
-        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: offset + n_c >= 2^31");
+    if (n_c > 65536 || (int64_t)offset + n_c > 0x7fffffffLL)
+        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: n_c > 65536 or offset + n_c >= 2^31");
     const int64_t nq = (int64_t)B * m;
     hipStream_t s = (hipStream_t)stream;
     // no compressed row is visible to any query: every list is K x -1 (the pages' empty selection)
     int64_t vmax = (start_pos + m) / ratio;
     vmax = vmax < n_c ? vmax : n_c;
     if (vmax == 0) {
-        topk_kernel<<<dim3((unsigned)nq), dim3(TOPK_THREADS), 0, s>>>(nullptr, 0, m, ratio, start_pos, K, offset, idx,
-                                                                      ld, col0);
+        launch_topk(nullptr, nq, 0, m, ratio, start_pos, K, offset, idx, ld, col0, s);
         return check_launch("sckv_index_scores_topk");
     }
     if (!q || !k || !w) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null input");
@@ -353,7 +378,6 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
 #undef SCKV_SCORES
     int rc = check_launch("sckv_index_scores_topk (scores)");
     if (rc) return rc;
-    topk_kernel<<<dim3((unsigned)nq), dim3(TOPK_THREADS), 0, s>>>(keys, n_c, m, ratio, start_pos, K, offset, idx, ld,
-                                                                  col0);
+    launch_topk(keys, nq, n_c, m, ratio, start_pos, K, offset, idx, ld, col0, s);
     return check_launch("sckv_index_scores_topk (top-k)");
 }

@@ -46,3 +46,37 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 }  // namespace sckv
+
+namespace sckv {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS byte offset of a pointer into shared memory.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Asynchronous 16-byte-per-lane copy global -> LDS (global_load_lds_dwordx4):
+// lane i's 16 bytes from `gaddr` land at LDS byte lds_byte + 16 * i.  Written
+// as inline asm so the compiler does not add its own conservative vmcnt(0)
+// waits in front of every LDS read; the caller waits with wait_vmcnt<N>().
+__device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_byte) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_byte) : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lanes 4j..4j+3 each point at 4 consecutive 16-bit values, together one row
+// j of a 4 x 16 block; lane i of the group receives column i (rows 0..3).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const __attribute__((address_space(3))) char*)p);
+}
+
+}  // namespace sckv

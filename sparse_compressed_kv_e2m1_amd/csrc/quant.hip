@@ -48,10 +48,11 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_
         amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
     }
     const float s = block_scale<MODE>(amax);
+    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
 #pragma unroll
     for (int i = 0; i < BLOCK / 2; ++i) {
-        uint32_t lo = fp4_value_bits(bf16_bits_to_f32(w[i] & 0xffffu), s);
-        uint32_t hi = fp4_value_bits(bf16_bits_to_f32(w[i] >> 16), s);
+        uint32_t lo = fp4_value<MODE>(bf16_bits_to_f32(w[i] & 0xffffu), s, inv_s);
+        uint32_t hi = fp4_value<MODE>(bf16_bits_to_f32(w[i] >> 16), s, inv_s);
         w[i] = lo | (hi << 16);
     }
     if (VEC) {

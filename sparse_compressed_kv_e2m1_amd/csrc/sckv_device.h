@@ -100,6 +100,27 @@ __device__ __forceinline__ uint32_t fp4_value_bits(float v, float s) {
     return f32_to_bf16_bits(e2m1_round(y) * s);
 }
 
+// Exact reciprocal of a power of two 2^-126 <= s <= 2^126 (exponent flip).
+__device__ __forceinline__ float pow2_reciprocal(float s) {
+    return __uint_as_float((254u - ((__float_as_uint(s) >> 23) & 0xffu)) << 23);
+}
+
+// The same value as fp4_value_bits(v, s) when s is a power of two: v * (1/s)
+// rounds the same exact real number v / s once (1/s is exact), so the bits
+// are identical, subnormal results included, and no division is needed.
+__device__ __forceinline__ uint32_t fp4_value_bits_pow2(float v, float s, float inv_s) {
+    float y = v * inv_s;
+    y = fminf(fmaxf(y, -6.0f), 6.0f);
+    return f32_to_bf16_bits(e2m1_round(y) * s);
+}
+
+// One value of a block in either mode (inv_s only used for power-of-two scales).
+template <int MODE>
+__device__ __forceinline__ uint32_t fp4_value(float v, float s, float inv_s) {
+    if (MODE == SCKV_FP4_E8M0_B32) return fp4_value_bits_pow2(v, s, inv_s);
+    return fp4_value_bits(v, s);
+}
+
 template <int MODE>
 struct QuantMode;
 template <>
