@@ -62,8 +62,29 @@ struct AttnShape {
     static constexpr int OFF_FLAG = OFF_L + HP * 4;
     static constexpr int OFF_IDX = OFF_FLAG + 16;
     static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
-    static_assert(VPL % 4 == 0 && LPH >= 1 && LPH <= 64, "softmax split");
+    static_assert(VPL % 4 == 0 && LPH >= 1 && LPH <= 16 && RPW % 4 == 0, "softmax split");
 };
+
+// Max / sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16),
+// every lane receiving the group's result, with DPP lane permutes (no LDS
+// round trip): quad_perm swaps within 2 and 4 lanes, half-row and row mirrors
+// pair the 4-lane and 8-lane halves.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    if (G >= 2) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false)));
+    if (G >= 4) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false)));
+    if (G >= 8) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false)));
+    if (G >= 16) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false)));
+    return v;
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if (G >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+    if (G >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+    if (G >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
+    if (G >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false));
+    return v;
+}
 
 // Wait until at most n of this wave's row copies are in flight (n uniform, one of 0, RPW, 2*RPW).
 template <int RPW>
@@ -90,6 +111,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     float* alpha_l = reinterpret_cast<float*>(lds + S::OFF_ALPHA);
     float* lsum_l = reinterpret_cast<float*>(lds + S::OFF_L);
     int* flags = reinterpret_cast<int*>(lds + S::OFF_FLAG);
+    int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
     const uint32_t lds0 = lds_offset(lds);
 
     const int lane = threadIdx.x & 63;
@@ -115,39 +137,27 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
             qa[mt][ks] = as_bf16x8((h < H) ? load16(qrow + (int64_t)h * D + dim0 + ks * 16 + half * 8)
                                            : u32x4{0, 0, 0, 0});
     }
-
-    // ---- softmax state of the head this lane helps own: hr, rows r0 .. r0+VPL-1
+    // softmax state of the head this lane helps own: hr, rows r0 .. r0+VPL-1
     const int hr = S::HW * wave + lane / S::LPH;
     const int r0 = (lane % S::LPH) * S::VPL;
     float m_run = (hr < H) ? sink[hr] * LOG2E : 0.0f;  // base-2 running max, starting at the sink
     float l_run = (nsplit == 1) ? 1.0f : 0.0f;          // e^(sink - M) at M = sink; splits add it when merged
 
-    f32x16 o[MT][S::NT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < S::NT; ++nt) o[mt][nt] = zero16();
-
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int c_begin = split * chunks_per_split;
     int c_end = c_begin + chunks_per_split;
     c_end = c_end < nchunks ? c_end : nchunks;
-
-    // Copy chunk c's rows (this wave's share) into its stage; returns the chunk's
-    // valid-row mask (identical in every wave).  Invalid rows of a partly valid
-    // chunk copy this query's first q row instead (finite data; masked later).
-    // This workgroup's slice of the index list, staged once in LDS.
-    int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
     {
+        // this workgroup's slice of the index list, staged once in LDS
         const int e0 = c_begin * CHUNK;
         const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
         for (int i = threadIdx.x; i < (c_end - c_begin) * CHUNK; i += NW * 64) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
-        __syncthreads();
     }
-    auto row_src = [&](int32_t iv) -> const uint16_t* {
-        const bool valid = (iv >= 0) && ((int64_t)iv < ra + rb);
-        return !valid ? qrow : (((int64_t)iv < ra) ? rows_a_b + (int64_t)iv * D : rows_b_b + ((int64_t)iv - ra) * D);
-    };
+    // Every ordinary global load above is complete before the first row copy is
+    // issued, so no compiler-placed wait inside the loop can stall on the copies.
+    wait_vmcnt<0>();
+    __syncthreads();
+
     // Copy chunk c's rows (this wave's share) into its stage; returns the chunk's
     // valid-row mask (identical in every wave).  Invalid rows of a partly valid
     // chunk copy this query's first q row instead (finite data; masked later).
@@ -158,130 +168,51 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
             (uint32_t)(__ballot((mine >= 0) && ((int64_t)mine < ra + rb)) & 0xffffffffull);
         if (mask) {
             const uint32_t st = lds0 + (uint32_t)((c % S::NST) * S::STAGE);
+            // this wave's RPW entries in one go (broadcast LDS reads), then scalar
+            int32_t ivv[S::RPW];
+#pragma unroll
+            for (int v4 = 0; v4 < S::RPW / 4; ++v4) {
+                const int4 t4 = *reinterpret_cast<const int4*>(ic + wave * S::RPW + 4 * v4);
+                ivv[4 * v4 + 0] = t4.x;
+                ivv[4 * v4 + 1] = t4.y;
+                ivv[4 * v4 + 2] = t4.z;
+                ivv[4 * v4 + 3] = t4.w;
+            }
 #pragma unroll
             for (int rr = 0; rr < S::RPW; ++rr) {
                 const int r = wave * S::RPW + rr;
-                if (lane < D / 8) dma16(row_src(ic[r]) + lane * 8, st + (uint32_t)(r * S::RS));
+                const int32_t iv = __builtin_amdgcn_readfirstlane(ivv[rr]);
+                const bool valid = (iv >= 0) && ((int64_t)iv < ra + rb);
+                const uint16_t* src = !valid ? qrow
+                                             : (((int64_t)iv < ra) ? rows_a_b + (int64_t)iv * D
+                                                                   : rows_b_b + ((int64_t)iv - ra) * D);
+                if (lane < D / 8) dma16_s(src, (uint32_t)lane * 16u, st + (uint32_t)(r * S::RS));
             }
         }
         return mask;
     };
 
+    f32x16 o[MT][S::NT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < S::NT; ++nt) o[mt][nt] = zero16();
+
     uint32_t mk[S::PD + 1];
 #pragma unroll
     for (int j = 0; j < S::PD; ++j) mk[j] = (c_begin + j < c_end) ? issue(c_begin + j) : 0u;
 
-    for (int c = c_begin; c < c_end; ++c) {
-        // chunk c's copies done (later chunks' copies may still fly), then everyone's
-        int after = 0;
-#pragma unroll
-        for (int j = 1; j < S::PD; ++j) after += mk[j] ? S::RPW : 0;
-        if (mk[0]) wait_rows<S::RPW>(after);
-        __syncthreads();
-        mk[S::PD] = (c + S::PD < c_end) ? issue(c + S::PD) : 0u;  // into the stage chunk c-1 used
-        const uint32_t mask = mk[0];
-#pragma unroll
-        for (int j = 0; j < S::PD; ++j) mk[j] = mk[j + 1];
-        if (mask == 0) continue;
-        const unsigned char* stp = lds + (c % S::NST) * S::STAGE;
-
-        // 2. partial logits over this wave's dims
-        f32x16 sp[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) sp[mt] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) {
-            const bf16x8 bk =
-                *reinterpret_cast<const bf16x8*>(stp + r_lane * S::RS + (dim0 + ks * 16 + half * 8) * 2);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sp[mt] = mfma32x32x16(qa[mt][ks], bk, sp[mt]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                sx[(wave * S::HP + mt * 32 + d_row(i, lane)) * S::SXS + r_lane] = sp[mt][i];
-        __syncthreads();
-
-        // 3. this wave's heads: sum the NW partial tiles (fixed order), online softmax
-        float x[S::VPL];
-#pragma unroll
-        for (int j = 0; j < S::VPL; ++j) x[j] = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float* src = sx + (ww * S::HP + hr) * S::SXS + r0;
-#pragma unroll
-            for (int j4 = 0; j4 < S::VPL / 4; ++j4) {
-                const float4 a = *reinterpret_cast<const float4*>(src + 4 * j4);
-                x[4 * j4 + 0] += a.x;
-                x[4 * j4 + 1] += a.y;
-                x[4 * j4 + 2] += a.z;
-                x[4 * j4 + 3] += a.w;
-            }
-        }
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < S::VPL; ++j) {
-            x[j] = ((mask >> (r0 + j)) & 1u) ? x[j] * scale_log2 : -INFINITY;
-            cmax = fmaxf(cmax, x[j]);
-        }
-#pragma unroll
-        for (int off = 1; off < S::LPH; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
-        const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.0f;
-        uint32_t pk[S::VPL / 2];
-#pragma unroll
-        for (int j = 0; j < S::VPL; j += 2) {
-            const uint32_t p0 = f32_to_bf16_bits(exp2f(x[j] - m_new));
-            const uint32_t p1 = f32_to_bf16_bits(exp2f(x[j + 1] - m_new));
-            psum += bf16_bits_to_f32(p0) + bf16_bits_to_f32(p1);
-            pk[j / 2] = p0 | (p1 << 16);
-        }
-#pragma unroll
-        for (int off = 1; off < S::LPH; off <<= 1) psum += __shfl_xor(psum, off, 64);
-        l_run = l_run * alpha + psum;
-        const bool moved = m_new != m_run;
-        m_run = m_new;
-        {
-            uint16_t* dst = pl + hr * S::PS + r0;
-#pragma unroll
-            for (int j4 = 0; j4 < S::VPL / 4; ++j4)
-                *reinterpret_cast<uint2*>(dst + 4 * j4) = make_uint2(pk[2 * j4], pk[2 * j4 + 1]);
-        }
-        if (lane % S::LPH == 0) alpha_l[hr] = alpha;
-        const uint64_t any_moved = __ballot(moved);
-        if (lane == 0) flags[wave] = any_moved != 0;
-        __syncthreads();
-
-        // 4. O[:, dims_w] (+)= P . R[:, dims_w]
-        bool rescale = false;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) rescale |= flags[ww] != 0;
-        if (rescale) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int ig = 0; ig < 4; ++ig) {
-                    const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + mt * 32 + ig * 8 + half * 4);
-#pragma unroll
-                    for (int nt = 0; nt < S::NT; ++nt) {
-                        o[mt][nt][ig * 4 + 0] *= a4.x;
-                        o[mt][nt][ig * 4 + 1] *= a4.y;
-                        o[mt][nt][ig * 4 + 2] *= a4.z;
-                        o[mt][nt][ig * 4 + 3] *= a4.w;
-                    }
-                }
-        }
+    const int g = lane >> 4;
+    const int quad = (lane & 15) >> 2;
+    const int a4l = lane & 3;
+    // O[:, dims_w] += P . R[:, dims_w] for the chunk in stage stp
+    auto pv = [&](const unsigned char* stp) {
         bf16x8 pa[MT][2];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int kr = 0; kr < 2; ++kr)
                 pa[mt][kr] = *reinterpret_cast<const bf16x8*>(pl + (mt * 32 + r_lane) * S::PS + kr * 16 + half * 8);
-        const int g = lane >> 4;
-        const int quad = (lane & 15) >> 2;
-        const int a4l = lane & 3;
 #pragma unroll
         for (int nt = 0; nt < S::NT; ++nt) {
             const int dcol = dim0 + nt * 32 + (g & 1) * 16 + 4 * a4l;
@@ -295,6 +226,124 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
                 for (int mt = 0; mt < MT; ++mt) o[mt][nt] = mfma32x32x16(pa[mt][kr], bv, o[mt][nt]);
             }
         }
+    };
+
+    // Chunk loop.  The inner loop never touches O with vector ALU work (so O
+    // stays in accumulation registers); it leaves only when a head's running
+    // max must move, which the outer loop handles by rescaling O.
+    int c = c_begin;
+    for (;;) {
+        bool moved = false;
+        const unsigned char* stp = lds;
+        for (; c < c_end; ++c) {
+            // chunk c's copies done (later chunks' copies may still fly), then everyone's
+            int after = 0;
+#pragma unroll
+            for (int j = 1; j < S::PD; ++j) after += mk[j] ? S::RPW : 0;
+            if (mk[0]) wait_rows<S::RPW>(after);
+            __syncthreads();
+            mk[S::PD] = (c + S::PD < c_end) ? issue(c + S::PD) : 0u;  // into the stage chunk c-1 used
+            const uint32_t mask = mk[0];
+#pragma unroll
+            for (int j = 0; j < S::PD; ++j) mk[j] = mk[j + 1];
+            if (mask == 0) continue;
+            stp = lds + (c % S::NST) * S::STAGE;
+
+            // partial logits over this wave's dims, as S^T = R . Q^T: rows are the
+            // MFMA M dimension, heads the N dimension, so each lane ends up with one
+            // head and runs of 4 consecutive rows (the A/B register layouts of R and
+            // Q are the same as for S = Q . R^T, only the operand order changes)
+            f32x16 sp[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) sp[mt] = zero16();
+#pragma unroll
+            for (int ks = 0; ks < S::KS; ++ks) {
+                const bf16x8 rk =
+                    *reinterpret_cast<const bf16x8*>(stp + r_lane * S::RS + (dim0 + ks * 16 + half * 8) * 2);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) sp[mt] = mfma32x32x16(rk, qa[mt][ks], sp[mt]);
+            }
+            // sx[wave][head][row]: lane's head mt*32 + r_lane, rows d_row(4*i4, lane) .. +3
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int i4 = 0; i4 < 4; ++i4)
+                    *reinterpret_cast<float4*>(sx + (wave * S::HP + mt * 32 + r_lane) * S::SXS + d_row(4 * i4, lane)) =
+                        make_float4(sp[mt][4 * i4], sp[mt][4 * i4 + 1], sp[mt][4 * i4 + 2], sp[mt][4 * i4 + 3]);
+            __syncthreads();
+
+            // this wave's heads: sum the NW partial tiles (fixed order), online softmax
+            float x[S::VPL];
+#pragma unroll
+            for (int j = 0; j < S::VPL; ++j) x[j] = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                const float* src = sx + (ww * S::HP + hr) * S::SXS + r0;
+#pragma unroll
+                for (int j4 = 0; j4 < S::VPL / 4; ++j4) {
+                    const float4 a = *reinterpret_cast<const float4*>(src + 4 * j4);
+                    x[4 * j4 + 0] += a.x;
+                    x[4 * j4 + 1] += a.y;
+                    x[4 * j4 + 2] += a.z;
+                    x[4 * j4 + 3] += a.w;
+                }
+            }
+            float cmax = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < S::VPL; ++j) {
+                x[j] = ((mask >> (r0 + j)) & 1u) ? x[j] * scale_log2 : -INFINITY;
+                cmax = fmaxf(cmax, x[j]);
+            }
+            cmax = group_max<S::LPH>(cmax);
+            const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+            float psum = 0.0f;
+            uint32_t pk[S::VPL / 2];
+#pragma unroll
+            for (int j = 0; j < S::VPL; j += 2) {
+                // hardware exp2 (v_exp_f32) and round-to-nearest-even pack to bf16
+                // (v_cvt_pk_bf16_f32); the sum uses the rounded weights
+                const f32x2 pf = {__builtin_amdgcn_exp2f(x[j] - m_new), __builtin_amdgcn_exp2f(x[j + 1] - m_new)};
+                const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2));
+                psum += __uint_as_float(pb << 16) + __uint_as_float(pb & 0xffff0000u);
+                pk[j / 2] = pb;
+            }
+            psum = group_sum<S::LPH>(psum);
+            l_run = l_run * alpha + psum;
+            const bool my_move = m_new != m_run;
+            m_run = m_new;
+            {
+                uint16_t* dst = pl + hr * S::PS + r0;
+#pragma unroll
+                for (int j4 = 0; j4 < S::VPL / 4; ++j4)
+                    *reinterpret_cast<uint2*>(dst + 4 * j4) = make_uint2(pk[2 * j4], pk[2 * j4 + 1]);
+            }
+            if (lane % S::LPH == 0) alpha_l[hr] = alpha;
+            const uint64_t any_moved = __ballot(my_move);
+            if (lane == 0) flags[wave] = any_moved != 0;
+            __syncthreads();
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww) moved |= flags[ww] != 0;
+            if (moved) break;
+            pv(stp);
+        }
+        if (!moved) break;
+        // rare: some head's max moved by more than the slack; rescale O, then this chunk's P.R
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ig = 0; ig < 4; ++ig) {
+                const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + mt * 32 + ig * 8 + half * 4);
+#pragma unroll
+                for (int nt = 0; nt < S::NT; ++nt) {
+                    o[mt][nt][ig * 4 + 0] *= a4.x;
+                    o[mt][nt][ig * 4 + 1] *= a4.y;
+                    o[mt][nt][ig * 4 + 2] *= a4.z;
+                    o[mt][nt][ig * 4 + 3] *= a4.w;
+                }
+            }
+        pv(stp);
+        ++c;
     }
 
     // ---- epilogue

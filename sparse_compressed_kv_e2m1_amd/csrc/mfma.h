@@ -14,6 +14,8 @@ namespace sckv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -63,6 +65,13 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 // waits in front of every LDS read; the caller waits with wait_vmcnt<N>().
 __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_byte) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gaddr), "s"(lds_byte) : "memory", "m0");
+}
+
+// Same copy with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (the saddr form): no 64-bit address arithmetic per lane.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_byte)
+                 : "memory", "m0");
 }
 
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding).

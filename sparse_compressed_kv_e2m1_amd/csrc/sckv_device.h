@@ -13,7 +13,7 @@
 
 #include <string>
 
-#include "../../include/sckv.h"
+#include "sckv.h"
 
 namespace sckv {
 
