@@ -34,14 +34,53 @@ __device__ __forceinline__ uint32_t score_key(uint32_t b) {
     return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
 
+// Shape of one score workgroup for MT head tiles and head dim DI.
+template <int MT, int DI>
+struct ScoreShape {
+    static constexpr int HP = MT * 32;                 // padded heads
+    static constexpr int KS = DI / 16;                 // k-steps
+    static constexpr int ROWB = DI * 2;                // bytes per k row
+    static constexpr int TILE = 32 * ROWB;             // bytes per 32-row tile
+    static constexpr int NINST = TILE / 1024;          // 16-byte-per-lane copies per tile
+    static constexpr int NST = (TILE >= 16384) ? 1 : 3;  // tiles per wave in the ring
+    static constexpr int PD = NST - 1;                   // tiles requested ahead of the one used
+    static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
+    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
+    static constexpr int QS = DI * 2 + 16;             // bytes per q_hat row in LDS (padded)
+    static constexpr int OFF_Q = SCORE_WAVES * NST * TILE;
+    static constexpr int OFF_KEYS = OFF_Q + HP * QS;
+    static constexpr size_t lds_bytes(int rows_per_wg, bool with_scores) {
+        return (size_t)OFF_KEYS + (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
+    }
+    static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 2, "copy counts");
+};
+
+template <int NINST, int NAHEAD>
+__device__ __forceinline__ void wait_tiles(int ahead) {
+    // at most `ahead` later tiles (NINST copies each) may still be in flight
+    if (ahead <= 0)
+        wait_vmcnt<0>();
+    else if (ahead == 1 || NAHEAD < 2)
+        wait_vmcnt<NINST>();
+    else
+        wait_vmcnt<(2 * NINST < 64 ? 2 * NINST : 63)>();
+}
+
 template <int MT, int DI>
 __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w, int64_t m, int Hi,
     int64_t n_c, int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys,
     uint16_t* __restrict__ scores) {
-    constexpr int KS = DI / 16;  // k-steps
+    using S = ScoreShape<MT, DI>;
+    constexpr int KS = S::KS;
+    extern __shared__ __align__(16) unsigned char lds[];
+    unsigned char* qh_l = lds + S::OFF_Q;
+    uint16_t* keys_l = reinterpret_cast<uint16_t*>(lds + S::OFF_KEYS);
+    uint16_t* sc_l = keys_l + rows_per_wg;
+    const uint32_t lds0 = lds_offset(lds);
+
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t qi = blockIdx.x / nsplit;
     const int split = (int)(blockIdx.x - qi * nsplit);
     const int64_t b = qi / m;
@@ -54,47 +93,35 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     int64_t row_end = row0 + rows_per_wg;
     row_end = row_end < vis ? row_end : vis;
 
-    // ---- q_hat in A layout: head mt*32 + lane%32, dims ks*16 + (lane/32)*8 + 0..7
+    // ---- q_hat = E8M0_B32 round trip of the raw q, one 32-value block per thread and step, into LDS
     const uint16_t* qrow = q + qi * (int64_t)Hi * DI;
-    bf16x8 qa[MT][KS];
+    for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += SCORE_WAVES * 64) {
+        const int h = blk / (DI / 32);
+        const int c = blk - h * (DI / 32);
+        u32x4 raw[4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int h = mt * 32 + (lane & 31);
-        u32x4 raw[KS];
+        for (int i = 0; i < 4; ++i) raw[i] = (h < Hi) ? load16(qrow + (int64_t)h * DI + c * 32 + i * 8) : u32x4{0, 0, 0, 0};
+        float amax = 0.0f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            raw[ks] = (h < Hi) ? load16(qrow + (int64_t)h * DI + ks * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] & 0xffffu)));
+                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] >> 16)));
+            }
+        const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
+        const float inv_s = pow2_reciprocal(s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t v = raw[i][e];
+                raw[i][e] = fp4_value_bits_pow2(bf16_bits_to_f32(v & 0xffffu), s, inv_s) |
+                            (fp4_value_bits_pow2(bf16_bits_to_f32(v >> 16), s, inv_s) << 16);
+            }
+            *reinterpret_cast<u32x4*>(qh_l + h * S::QS + (c * 32 + i * 8) * 2) = raw[i];
         }
-        // E8M0_B32 blocks: dims [32c, 32c+32) = k-steps 2c and 2c+1 of this lane
-        // and of lane^32.
-#pragma unroll
-        for (int c = 0; c < KS / 2; ++c) {
-            float amax = 0.0f;
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t v = raw[2 * c + kk][e];
-                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v & 0xffffu)));
-                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(v >> 16)));
-                }
-            amax = fmaxf(amax, shfl_xor32(amax));
-            const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
-            const float inv_s = pow2_reciprocal(s);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    uint32_t v = raw[2 * c + kk][e];
-                    uint32_t lo = fp4_value_bits_pow2(bf16_bits_to_f32(v & 0xffffu), s, inv_s);
-                    uint32_t hi = fp4_value_bits_pow2(bf16_bits_to_f32(v >> 16), s, inv_s);
-                    raw[2 * c + kk][e] = lo | (hi << 16);
-                }
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qa[mt][ks] = as_bf16x8(raw[ks]);
     }
-
     // ---- head weights in D layout: head mt*32 + d_row(i, lane)
     float wd[MT][16];
     const float* wrow = w + qi * (int64_t)Hi;
@@ -105,33 +132,64 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
             const int h = mt * 32 + d_row(i, lane);
             wd[mt][i] = (h < Hi) ? wrow[h] : 0.0f;
         }
-
-    const uint16_t* kb = k + b * n_c * DI;
-    uint16_t* kout = keys + qi * n_c;
-    uint16_t* sout = scores ? scores + qi * n_c : nullptr;
-
-    // k rows of a 32-row tile in B layout: row s0 + lane%32, dims ks*16 + (lane/32)*8 + 0..7;
-    // the next tile's rows are requested before this tile is consumed
-    auto load_tile = [&](int64_t s0, u32x4* kr) {
-        const int64_t s = s0 + (lane & 31);
+    // every ordinary load is done before the first tile copy is issued
+    wait_vmcnt<0>();
+    __syncthreads();
+    bf16x8 qa[MT][KS];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            kr[ks] = (s < n_c) ? load16(kb + s * DI + ks * 16 + (lane >> 5) * 8) : u32x4{0, 0, 0, 0};
-    };
-    int64_t s0 = row0 + (int64_t)wave * 32;
-    u32x4 kr[KS], kn[KS];
-    if (s0 < row_end) load_tile(s0, kn);
-    for (; s0 < row_end; s0 += SCORE_WAVES * 32) {
-        const int64_t s = s0 + (lane & 31);
+            qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + (lane & 31)) * S::QS +
+                                                          (ks * 16 + (lane >> 5) * 8) * 2);
+
+    // ---- this wave's rows: a contiguous run, streamed in 32-row tiles through
+    // a wave-private ring; lane i of copy j brings 16 bytes of tile byte j*1024 +
+    // 16 i, taken from chunk (chunk ^ (row & SWZ)) of its row so that the B-operand
+    // reads below (32 rows at one chunk) spread over all banks.
+    const int64_t nrows = row_end - row0;
+    const int64_t per_wave = (((nrows + SCORE_WAVES - 1) / SCORE_WAVES) + 31) / 32 * 32;
+    const int64_t w0 = row0 + (int64_t)wave * per_wave;
+    int64_t w1 = w0 + per_wave;
+    w1 = w1 < row_end ? w1 : row_end;
+    const int ntiles = (w0 < w1) ? (int)((w1 - w0 + 31) / 32) : 0;
+    const uint16_t* kb = k + b * n_c * DI;
+    const uint32_t ring = lds0 + (uint32_t)(wave * S::NST * S::TILE);
+    auto issue = [&](int tile) {
+        const int64_t s0 = w0 + (int64_t)tile * 32;
+        const uint32_t st = ring + (uint32_t)((tile % S::NST) * S::TILE);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) kr[ks] = kn[ks];
-        if (s0 + SCORE_WAVES * 32 < row_end) load_tile(s0 + SCORE_WAVES * 32, kn);
+        for (int j = 0; j < S::NINST; ++j) {
+            const int byte = j * 1024 + lane * 16;
+            const int r = byte / S::ROWB;
+            const int ch = (byte % S::ROWB) / 16;
+            int64_t row = s0 + r;
+            row = row < n_c ? row : n_c - 1;  // tail rows re-read a real row; their results are dropped
+            const uint32_t off = (uint32_t)(row * S::ROWB + ((ch ^ (r & S::SWZ)) * 16));
+            dma16_s(kb, off, st + (uint32_t)(j * 1024));
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < S::PD; ++i)
+        if (i < ntiles) issue(i);
+
+    for (int tile = 0; tile < ntiles; ++tile) {
+        if (S::PD == 0) issue(tile);
+        // tiles tile+1 .. tile+PD-1 may still be in flight; tile itself must be done
+        const int ahead = (ntiles - 1 - tile) < (S::PD - 1) ? (ntiles - 1 - tile) : (S::PD - 1);
+        wait_tiles<S::NINST, S::PD - 1>(ahead);
+        if (S::PD > 0 && tile + S::PD < ntiles) issue(tile + S::PD);  // into the stage tile-1 used
+        const unsigned char* stp = lds + (wave * S::NST + tile % S::NST) * S::TILE;
+        const int r = lane & 31;
         f32x16 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            acc[mt] = zero16();
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = zero16();
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc[mt] = mfma32x32x16(qa[mt][ks], as_bf16x8(kr[ks]), acc[mt]);
+        for (int ks = 0; ks < KS; ++ks) {
+            const int ch = ks * 2 + (lane >> 5);
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(stp + r * S::ROWB + ((ch ^ (r & S::SWZ)) * 16));
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16(qa[mt][ks], kr, acc[mt]);
         }
         // r_h = fl32(w_h * relu(d_h)); relu maps every d <= 0 (and -0) to +0
         float v[MT * 16];
@@ -164,11 +222,20 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
             v[1] = v[1] + v[3];
         }
         if (Hi > 1) v[0] = v[0] + v[1];
-        if (lane < 32 && s < row_end) {
+        const int64_t s = w0 + (int64_t)tile * 32 + r;
+        if (lane < 32 && s < w1) {
             const uint32_t bits = f32_to_bf16_bits(v[0]);
-            kout[s] = (uint16_t)score_key(bits);
-            if (sout) sout[s] = (uint16_t)bits;
+            keys_l[s - row0] = (uint16_t)score_key(bits);
+            if (scores) sc_l[s - row0] = (uint16_t)bits;
         }
+    }
+    // ---- flush this workgroup's keys (and scores) with coalesced stores
+    __syncthreads();
+    uint16_t* kout = keys + qi * n_c + row0;
+    for (int64_t i = threadIdx.x; i < nrows; i += SCORE_WAVES * 64) kout[i] = keys_l[i];
+    if (scores) {
+        uint16_t* sout = scores + qi * n_c + row0;
+        for (int64_t i = threadIdx.x; i < nrows; i += SCORE_WAVES * 64) sout[i] = sc_l[i];
     }
 }
 
@@ -299,21 +366,32 @@ void launch_topk(const uint16_t* keys, int64_t nq, int64_t n_c, int64_t m, int r
 }
 
 template <int MT, int DI>
-void launch_scores(const uint16_t* q, const uint16_t* k, const float* w, int64_t nq, int64_t m, int Hi, int64_t n_c,
-                   int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* keys, uint16_t* scores,
-                   hipStream_t stream) {
-    index_score_kernel<MT, DI><<<dim3((unsigned)(nq * nsplit)), dim3(SCORE_WAVES * 64), 0, stream>>>(
+int launch_scores(const uint16_t* q, const uint16_t* k, const float* w, int64_t nq, int64_t m, int Hi, int64_t n_c,
+                  int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* keys, uint16_t* scores,
+                  hipStream_t stream) {
+    using Sh = ScoreShape<MT, DI>;
+    const size_t lds = Sh::lds_bytes(rows_per_wg, scores != nullptr);
+    if (lds > 160 * 1024) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: score tile does not fit in LDS");
+    if (lds > 65536) {
+        hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_index_scores_topk: ") + hipGetErrorString(e));
+    }
+    index_score_kernel<MT, DI><<<dim3((unsigned)(nq * nsplit)), dim3(SCORE_WAVES * 64), lds, stream>>>(
         q, k, w, m, Hi, n_c, ratio, start_pos, rows_per_wg, nsplit, keys, scores);
+    return SCKV_OK;
 }
 
-// Rows per workgroup: a multiple of 128 (4 waves x 32 rows), small enough
-// that the launch has about 1024 workgroups when the queries alone do not.
+// Rows per workgroup: a multiple of 128 (4 waves x 32 rows), at most 4096
+// (the keys are buffered in LDS), and small enough that the launch has about
+// 512 workgroups when the queries alone do not.
 int score_rows_per_wg(int64_t nq, int64_t n_c) {
     int64_t tiles = (n_c + 127) / 128;  // 128-row tiles of one query
-    int64_t want_splits = (1024 + nq - 1) / nq;
+    int64_t want_splits = (512 + nq - 1) / nq;
     if (want_splits > tiles) want_splits = tiles;
     if (want_splits < 1) want_splits = 1;
     int64_t tiles_per = (tiles + want_splits - 1) / want_splits;
+    if (tiles_per > 32) tiles_per = 32;
     return (int)(tiles_per * 128);
 }
 
@@ -369,14 +447,16 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
     uint16_t* sc = (uint16_t*)scores;
     const bool two = Hi > 32;
 #define SCKV_SCORES(MT, DI) launch_scores<MT, DI>(qq, kk, w, nq, m, Hi, n_c, ratio, start_pos, rpw, nsplit, keys, sc, s)
+    int rc;
     switch (Di) {
-        case 32: two ? SCKV_SCORES(2, 32) : SCKV_SCORES(1, 32); break;
-        case 64: two ? SCKV_SCORES(2, 64) : SCKV_SCORES(1, 64); break;
-        case 128: two ? SCKV_SCORES(2, 128) : SCKV_SCORES(1, 128); break;
-        default: two ? SCKV_SCORES(2, 256) : SCKV_SCORES(1, 256); break;
+        case 32: rc = two ? SCKV_SCORES(2, 32) : SCKV_SCORES(1, 32); break;
+        case 64: rc = two ? SCKV_SCORES(2, 64) : SCKV_SCORES(1, 64); break;
+        case 128: rc = two ? SCKV_SCORES(2, 128) : SCKV_SCORES(1, 128); break;
+        default: rc = two ? SCKV_SCORES(2, 256) : SCKV_SCORES(1, 256); break;
     }
 #undef SCKV_SCORES
-    int rc = check_launch("sckv_index_scores_topk (scores)");
+    if (rc) return rc;
+    rc = check_launch("sckv_index_scores_topk (scores)");
     if (rc) return rc;
     launch_topk(keys, nq, n_c, m, ratio, start_pos, K, offset, idx, ld, col0, s);
     return check_launch("sckv_index_scores_topk (top-k)");
