@@ -42,7 +42,7 @@ struct ScoreShape {
     static constexpr int ROWB = DI * 2;                // bytes per k row
     static constexpr int TILE = 32 * ROWB;             // bytes per 32-row tile
     static constexpr int NINST = TILE / 1024;          // 16-byte-per-lane copies per tile
-    static constexpr int NST = (TILE >= 16384) ? 1 : 3;  // tiles per wave in the ring
+    static constexpr int NST = (TILE >= 16384) ? 1 : 4;  // tiles per wave in the ring
     static constexpr int PD = NST - 1;                   // tiles requested ahead of the one used
     static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
@@ -52,7 +52,7 @@ struct ScoreShape {
     static constexpr size_t lds_bytes(int rows_per_wg, bool with_scores) {
         return (size_t)OFF_KEYS + (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
     }
-    static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 2, "copy counts");
+    static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 3, "copy counts");
 };
 
 template <int NINST, int NAHEAD>
@@ -251,9 +251,31 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
 
 constexpr int TOPK_WAVES = TOPK_THREADS / 64;
 
+// DPP helpers (no LDS round trip).  update_dpp(old, src, ctrl, row_mask,
+// bank_mask, bound_ctrl): lanes outside row_mask keep `old`.
+#define SCKV_DPP(v, ctrl, rmask, bc) \
+    ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rmask), 0xf, (bc)))
+
+// Sum of x over the wave (uniform result): butterfly inside each 16-lane row,
+// then the four row sums through readlane.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    x += SCKV_DPP(x, 0xb1, 0xf, false);   // quad_perm [1,0,3,2]
+    x += SCKV_DPP(x, 0x4e, 0xf, false);   // quad_perm [2,3,0,1]
+    x += SCKV_DPP(x, 0x141, 0xf, false);  // row_half_mirror
+    x += SCKV_DPP(x, 0x140, 0xf, false);  // row_mirror
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, 0) + (uint32_t)__builtin_amdgcn_readlane((int)x, 16) +
+           (uint32_t)__builtin_amdgcn_readlane((int)x, 32) + (uint32_t)__builtin_amdgcn_readlane((int)x, 48);
+}
+
+// Inclusive prefix sum over the wave's lanes: shifts inside 16-lane rows, then
+// row 15 / lane 31 broadcasts into the later rows.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += SCKV_DPP(x, 0x111, 0xf, true);  // row_shr:1
+    x += SCKV_DPP(x, 0x112, 0xf, true);  // row_shr:2
+    x += SCKV_DPP(x, 0x114, 0xf, true);  // row_shr:4
+    x += SCKV_DPP(x, 0x118, 0xf, true);  // row_shr:8
+    x += SCKV_DPP(x, 0x142, 0xa, false);  // row_bcast15 into rows 1 and 3
+    x += SCKV_DPP(x, 0x143, 0xc, false);  // row_bcast31 into rows 2 and 3
     return x;
 }
 
@@ -271,14 +293,8 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t x, uint32_t* buf) {
 
 // Exclusive prefix sum over the block's threads.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tot) {
-    const int lane = threadIdx.x & 63;
-    uint32_t incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += y;
-    }
-    if (lane == 63) tot[threadIdx.x >> 6] = incl;
+    const uint32_t incl = wave_incl_scan(x);
+    if ((threadIdx.x & 63) == 63) tot[threadIdx.x >> 6] = incl;
     __syncthreads();
     uint32_t before = 0;
     for (int i = 0; i < (int)(threadIdx.x >> 6); ++i) before += tot[i];
@@ -306,8 +322,24 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_kernel(const uint16_t* __re
     const uint16_t* kp = keys + qi * n_c;
     const int64_t s0 = (int64_t)tid * KPT;
     uint32_t key[KPT];
+    if (KPT % 8 == 0 && (n_c % 8) == 0) {
+        // whole 16-byte groups of 8 keys; groups past n_c are not read
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = (s0 + j < vis) ? (uint32_t)kp[s0 + j] : 0u;
+        for (int j8 = 0; j8 < KPT / 8; ++j8) {
+            const int64_t g0 = s0 + 8 * j8;
+            const u32x4 v = (g0 + 8 <= n_c) ? load16(kp + g0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                key[8 * j8 + 2 * e] = v[e] & 0xffffu;
+                key[8 * j8 + 2 * e + 1] = v[e] >> 16;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = (s0 + j < vis) ? key[j] : 0u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = (s0 + j < vis) ? (uint32_t)kp[s0 + j] : 0u;
+    }
 
     uint32_t tau = 0;
     int rb = 0;
@@ -382,7 +414,7 @@ int launch_scores(const uint16_t* q, const uint16_t* k, const float* w, int64_t 
     return SCKV_OK;
 }
 
-// Rows per workgroup: a multiple of 128 (4 waves x 32 rows), at most 4096
+// Rows per workgroup: a multiple of 128 (4 waves x 32 rows), at most 2048
 // (the keys are buffered in LDS), and small enough that the launch has about
 // 512 workgroups when the queries alone do not.
 int score_rows_per_wg(int64_t nq, int64_t n_c) {
@@ -391,7 +423,7 @@ int score_rows_per_wg(int64_t nq, int64_t n_c) {
     if (want_splits > tiles) want_splits = tiles;
     if (want_splits < 1) want_splits = 1;
     int64_t tiles_per = (tiles + want_splits - 1) / want_splits;
-    if (tiles_per > 32) tiles_per = 32;
+    if (tiles_per > 16) tiles_per = 16;
     return (int)(tiles_per * 128);
 }
 
