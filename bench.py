@@ -19,6 +19,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -81,10 +82,15 @@ def counts(w, B, call):
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources with comments and blank space removed, so that
+    only code changes invalidate counters taken earlier."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(f.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -102,6 +108,114 @@ def traffic_for(workload, B, call):
         return None
     entry = rec.get("entries", {}).get(f"{workload}/B{B}/{call}")
     return None if entry is None else entry.get("hbm_bytes_per_launch")
+
+
+# Library call -> the kernels it launches (demangled-name prefixes).
+CALL_KERNELS = {
+    "quant_latent": ["quant_rows_kernel<0,"],
+    "quant_index_k": ["quant_rows_kernel<1,"],
+    "ring_write": ["ring_write_kernel"],
+    "window_idx": ["window_idx_kernel"],
+    "visible_idx": ["visible_idx_kernel"],
+    "index_scores_topk": ["index_score_kernel", "topk_kernel"],
+    "sparse_attn_sink": ["sparse_attn_kernel", "combine_kernel"],
+}
+
+
+def _kernel_short(name):
+    name = re.sub(r"^void ", "", name)
+    name = name.replace("sckv::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name).replace(" ", "")
+
+
+def _steady_groups(rows, key):
+    """Per kernel: the dispatches of its most frequent grid size (the step's
+    launches; one-off set-up launches of other sizes drop out)."""
+    groups = {}
+    for r in rows:
+        if "sckv::" not in r["Kernel_Name"]:
+            continue
+        groups.setdefault(_kernel_short(r["Kernel_Name"]), {}).setdefault(key(r), []).append(r)
+    return {k: max(v.values(), key=len) for k, v in groups.items()}
+
+
+def _csv_rows(folder, suffix):
+    import csv  # noqa: PLC0415
+    import glob  # noqa: PLC0415
+
+    paths = glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)
+    if len(paths) != 1:
+        raise SystemExit(f"expected one *{suffix} under {folder}, found {paths}")
+    return list(csv.DictReader(open(paths[0])))
+
+
+def summarize_profiles(w, B, folder, commands):
+    """Turn rocprofv3 output under `folder` (trace/, FETCH_SIZE/, WRITE_SIZE/,
+    copy_FETCH_SIZE/, copy_WRITE_SIZE/) into the text summary
+    profiles/hot_path_kernels_<workload>_B<B>.txt and the HBM-traffic entries
+    of profiles/traffic.json (counter KiB per dispatch, scaled so that a plain
+    1 GiB device copy reads and writes 1 GiB)."""
+    tr = _steady_groups(_csv_rows(os.path.join(folder, "trace"), "kernel_trace.csv"),
+                        lambda r: (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"]))
+    dur = {k: sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in v) / len(v) / 1e3
+           for k, v in tr.items()}
+    calls = {k: len(v) for k, v in tr.items()}
+    res = {"FETCH_SIZE": None, "WRITE_SIZE": None}
+    scale = {}
+    for c in res:
+        d = os.path.join(folder, c)
+        if not os.path.isdir(d):
+            continue
+        g = _steady_groups(_csv_rows(d, "counter_collection.csv"), lambda r: r["Grid_Size"])
+        res[c] = {k: sum(float(r["Counter_Value"]) for r in v) / len(v) * 1024 for k, v in g.items()}
+        cdir = os.path.join(folder, "copy_" + c)
+        if not os.path.isdir(cdir):  # one calibration next to several workloads' folders
+            cdir = os.path.join(os.path.dirname(os.path.normpath(folder)), "copy_" + c)
+        cp = _csv_rows(cdir, "counter_collection.csv")
+        # the 1 GiB copy: the largest per-dispatch value of the copy kernel
+        copy_bytes = max(float(r["Counter_Value"]) * 1024 for r in cp if "copyBuffer" in r["Kernel_Name"]
+                         or "copy" in r["Kernel_Name"].lower())
+        scale[c] = (1 << 30) / copy_bytes
+    lines = [f"# rocprofv3 summary: compressed sparse attention hot path, {describe(w)}, B={B}", "#"]
+    lines += ["# commands (repo root as working directory):"] + [f"#   {c}" for c in commands]
+    lines += [f"# counter scale (1 GiB device copy): FETCH_SIZE x{scale.get('FETCH_SIZE', float('nan')):.3f}, "
+              f"WRITE_SIZE x{scale.get('WRITE_SIZE', float('nan')):.3f}",
+              "# steady-state dispatches only (most frequent grid size per kernel)", "#",
+              f"{'kernel':<44} {'calls':>5} {'avg_us':>9} {'read_MB':>9} {'write_MB':>9}"]
+    for k in sorted(dur, key=lambda k: -dur[k]):
+        rd = res["FETCH_SIZE"].get(k) if res["FETCH_SIZE"] else None
+        wr = res["WRITE_SIZE"].get(k) if res["WRITE_SIZE"] else None
+        rd = "-" if rd is None else f"{rd * scale['FETCH_SIZE'] / 1e6:.2f}"
+        wr = "-" if wr is None else f"{wr * scale['WRITE_SIZE'] / 1e6:.2f}"
+        lines.append(f"{k[:44]:<44} {calls[k]:>5} {dur[k]:>9.2f} {rd:>9} {wr:>9}")
+    lines += ["#", f"{'library call':<20} {'avg_us':>9} {'alg_MB':>9} {'hbm_MB':>9}"]
+    entries = {}
+    for call, pre in CALL_KERNELS.items():
+        ks = [k for k in dur if any(k.startswith(p.replace(" ", "")) for p in pre)]
+        if not ks:
+            continue
+        us = sum(dur[k] for k in ks)
+        hbm = None
+        if res["FETCH_SIZE"] and res["WRITE_SIZE"] and all(k in res[c] for c in res for k in ks):
+            hbm = sum(res["FETCH_SIZE"].get(k, 0) * scale["FETCH_SIZE"] + res["WRITE_SIZE"].get(k, 0)
+                      * scale["WRITE_SIZE"] for k in ks)
+        alg = counts(w, B, call)["bytes"]
+        lines.append(f"{call:<20} {us:>9.2f} {alg / 1e6:>9.2f} {'-' if hbm is None else f'{hbm / 1e6:.2f}':>9}")
+        entries[f"{w.name}/B{B}/{call}"] = {"kernels": ks, "avg_us": round(us, 3),
+                                            "hbm_bytes_per_launch": None if hbm is None else int(hbm)}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", f"hot_path_kernels_{w.name}_B{B}.txt")
+    open(out, "w").write("\n".join(lines) + "\n")
+    tj = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(tj)) if os.path.exists(tj) else {}
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        rec = {"kernel_source_hash": kernel_source_hash(), "entries": {}}
+    rec["note"] = ("HBM bytes per library call (all its kernels), rocprofv3 FETCH_SIZE + WRITE_SIZE scaled by a "
+                   "1 GiB copy; valid only for the kernel sources whose hash is kernel_source_hash")
+    if res["FETCH_SIZE"] and res["WRITE_SIZE"]:
+        rec["entries"].update(entries)
+    json.dump(rec, open(tj, "w"), indent=1, sort_keys=True)
+    log(f"wrote {out} and {tj}")
 
 
 def cpu_baseline(w, seconds):
@@ -146,7 +260,16 @@ def main():
     ap.add_argument("--no-single", action="store_true", help="skip the B = 1 latency run (for profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
+    ap.add_argument("--summarize", metavar="DIR", default=None,
+                    help="only write the profiles/ summary of the rocprofv3 output under DIR (no GPU)")
+    ap.add_argument("--command", action="append", default=[], help="profiling command to record (--summarize)")
     args = ap.parse_args()
+    if args.summarize:
+        import sckv_synth as synth  # noqa: PLC0415
+
+        w = synth.WORKLOADS[args.workload]
+        summarize_profiles(w, args.instances or DEFAULT_B[args.workload], args.summarize, args.command)
+        return
     if args.copy_calibration:
         import torch  # noqa: PLC0415
 

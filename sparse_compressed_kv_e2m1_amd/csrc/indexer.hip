@@ -1,6 +1,7 @@
 // indexer.hip -- indexer scores of every query against its visible compressed
 // rows (MFMA contraction, fused q round trip, fixed pairwise head sum) and the
-// per-query top-K (two-pass byte radix select, then an ordered compaction).
+// per-query top-K (bitwise threshold search over keys held in registers, then
+// an ordered compaction).
 //
 // Pages: "metrale_model_arch/deepseek_v41_ref/compress.rs" (module doc: q and
 // k through the e2m1 round trip with power-of-two scales in blocks of 32,
@@ -9,15 +10,20 @@
 // window and compressed lists).  The head combination is the lightning-indexer
 // reading: score = bf16(pairwise sum over h of fl32(w[t,h] * relu(q_hat.k))).
 //
-// Score kernel.  One wave = one query x tiles of 32 compressed rows; heads are
-// the MFMA M dimension (32 or 64 rows of A), rows the N dimension, the
-// indexer head dim the K dimension.  q_hat lives in registers in A layout;
-// k rows are read straight from HBM in B layout (16 bytes per lane per
-// k-step).  All products are exact and, for round-tripped data, every partial
-// sum is a binary32 value, so the MFMA accumulation order does not matter.
-// The head sum follows the fixed pairwise order (stride Hi/2 first): in the D
-// tile layout strides 32, 16, 8, 2 and 1 stay inside a lane and stride 4 is
-// the lane^32 exchange.
+// Score kernel.  One workgroup (4 waves) = one query x a range of compressed
+// rows; each wave takes a contiguous run of that range in 32-row tiles.  The
+// workgroup first round-trips the raw q into LDS (one 32-value block per
+// thread), then every wave holds q_hat in registers in MFMA A layout: heads are
+// the M dimension (32 or 64), rows the N dimension, the indexer head dim the
+// K dimension.  k tiles stream HBM -> LDS through a wave-private ring of
+// asynchronous copies (global_load_lds_dwordx4, 1 KiB per instruction,
+// 16-byte chunks swizzled by row so the B-operand reads hit every bank).  All
+// products are exact and, for round-tripped data, every partial sum is a
+// binary32 value, so the MFMA accumulation order does not matter.  The head
+// sum follows the fixed pairwise order (stride Hi/2 first): in the D tile
+// layout strides 32, 16, 8, 2 and 1 stay inside a lane and stride 4 is the
+// lane^32 exchange.  Ordered 16-bit keys collect in LDS and leave with
+// coalesced stores.
 #include "mfma.h"
 #include "sckv_device.h"
 
