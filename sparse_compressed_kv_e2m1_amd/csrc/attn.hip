@@ -39,28 +39,32 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float STALE_MAX = 8.0f;  // base-2 slack before the running max moves
 constexpr int MAX_CPS = 64;        // chunks one workgroup handles at most (its index range sits in LDS)
 
-template <int MT, int DW, int NW>
+// MT head tiles of 32 per wave, NG head groups, NW waves per group splitting
+// the head dim into slices of DW: NG * NW waves, NG * MT * 32 padded heads.
+template <int MT, int NG, int DW, int NW>
 struct AttnShape {
-    static constexpr int HP = MT * 32;             // padded heads
+    static constexpr int WAVES = NG * NW;
+    static constexpr int HG = MT * 32;             // padded heads of one group
+    static constexpr int HP = NG * HG;             // padded heads
     static constexpr int D = DW * NW;
     static constexpr int KS = DW / 16;             // k-steps of Q.R^T per wave
     static constexpr int NT = DW / 32;             // 32-wide output tiles per wave
-    static constexpr int RPW = CHUNK / NW;         // rows each wave copies in per chunk
+    static constexpr int RPW = CHUNK / WAVES;      // rows each wave copies in per chunk
     static constexpr int PD = (RPW <= 16) ? 2 : 1; // chunks in flight ahead of the one computed
     static constexpr int NST = PD + 1;             // stages in the ring
     static constexpr int RS = 2 * D + 32;          // bytes per row in a stage (32-byte pad: no bank conflicts)
     static constexpr int STAGE = CHUNK * RS;
-    static constexpr int HW = HP / NW;             // heads whose softmax one wave owns
+    static constexpr int HW = HP / WAVES;          // heads whose softmax one wave owns
     static constexpr int LPH = 64 / HW;            // lanes per owned head
     static constexpr int VPL = CHUNK / LPH;        // logits per lane in the softmax
     static constexpr int SXS = CHUNK + 4;          // floats per head row of a partial-logit tile
     static constexpr int PS = CHUNK + 8;           // bf16 per head row of P
     static constexpr int OFF_SX = NST * STAGE;
-    static constexpr int OFF_P = OFF_SX + NW * HP * SXS * 4;
+    static constexpr int OFF_P = OFF_SX + NW * HP * SXS * 4;  // NW partial tiles per head
     static constexpr int OFF_ALPHA = OFF_P + HP * PS * 2;
     static constexpr int OFF_L = OFF_ALPHA + HP * 4;
     static constexpr int OFF_FLAG = OFF_L + HP * 4;
-    static constexpr int OFF_IDX = OFF_FLAG + 16;
+    static constexpr int OFF_IDX = OFF_FLAG + 4 * WAVES;
     static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
     static_assert(VPL % 4 == 0 && LPH >= 1 && LPH <= 16 && RPW % 4 == 0, "softmax split");
 };
@@ -97,14 +101,15 @@ __device__ __forceinline__ void wait_rows(int n) {
         wait_vmcnt<(2 * RPW < 64 ? 2 * RPW : 63)>();
 }
 
-template <int MT, int DW, int NW>
-__global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
+template <int MT, int NG, int DW, int NW>
+__global__ __launch_bounds__(NG * NW * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    using S = AttnShape<MT, DW, NW>;
+    using S = AttnShape<MT, NG, DW, NW>;
     constexpr int D = S::D;
+    constexpr int NTH = S::WAVES * 64;
     extern __shared__ __align__(16) unsigned char lds[];
     float* sx = reinterpret_cast<float*>(lds + S::OFF_SX);
     uint16_t* pl = reinterpret_cast<uint16_t*>(lds + S::OFF_P);
@@ -121,7 +126,9 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     const int64_t qi = blockIdx.x / nsplit;
     const int split = (int)(blockIdx.x - qi * nsplit);
     const int64_t b = qi / m;
-    const int dim0 = wave * DW;
+    const int grp = wave / NW;          // head group: heads grp*HG .. grp*HG + HG-1
+    const int dim0 = (wave % NW) * DW;  // head-dim slice
+    const int hg0 = grp * S::HG;
     const uint16_t* rows_a_b = rows_a + b * ra * D;
     const uint16_t* rows_b_b = rows_b ? rows_b + b * rb * D : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
@@ -131,7 +138,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
     bf16x8 qa[MT][S::KS];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-        const int h = mt * 32 + r_lane;
+        const int h = hg0 + mt * 32 + r_lane;
 #pragma unroll
         for (int ks = 0; ks < S::KS; ++ks)
             qa[mt][ks] = as_bf16x8((h < H) ? load16(qrow + (int64_t)h * D + dim0 + ks * 16 + half * 8)
@@ -151,7 +158,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         // this workgroup's slice of the index list, staged once in LDS
         const int e0 = c_begin * CHUNK;
         const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
-        for (int i = threadIdx.x; i < (c_end - c_begin) * CHUNK; i += NW * 64) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
+        for (int i = threadIdx.x; i < (c_end - c_begin) * CHUNK; i += NTH) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
     }
     // Every ordinary global load above is complete before the first row copy is
     // issued, so no compiler-placed wait inside the loop can stall on the copies.
@@ -212,7 +219,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int kr = 0; kr < 2; ++kr)
-                pa[mt][kr] = *reinterpret_cast<const bf16x8*>(pl + (mt * 32 + r_lane) * S::PS + kr * 16 + half * 8);
+                pa[mt][kr] = *reinterpret_cast<const bf16x8*>(pl + (hg0 + mt * 32 + r_lane) * S::PS + kr * 16 + half * 8);
 #pragma unroll
         for (int nt = 0; nt < S::NT; ++nt) {
             const int dcol = dim0 + nt * 32 + (g & 1) * 16 + 4 * a4l;
@@ -268,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
                 for (int i4 = 0; i4 < 4; ++i4)
-                    *reinterpret_cast<float4*>(sx + (wave * S::HP + mt * 32 + r_lane) * S::SXS + d_row(4 * i4, lane)) =
+                    *reinterpret_cast<float4*>(sx + ((wave % NW) * S::HP + hg0 + mt * 32 + r_lane) * S::SXS + d_row(4 * i4, lane)) =
                         make_float4(sp[mt][4 * i4], sp[mt][4 * i4 + 1], sp[mt][4 * i4 + 2], sp[mt][4 * i4 + 3]);
             __syncthreads();
 
@@ -323,7 +330,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
             if (lane == 0) flags[wave] = any_moved != 0;
             __syncthreads();
 #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) moved |= flags[ww] != 0;
+            for (int ww = 0; ww < S::WAVES; ++ww) moved |= flags[ww] != 0;
             if (moved) break;
             pv(stp);
         }
@@ -333,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
-                const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + mt * 32 + ig * 8 + half * 4);
+                const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + hg0 + mt * 32 + ig * 8 + half * 4);
 #pragma unroll
                 for (int nt = 0; nt < S::NT; ++nt) {
                     o[mt][nt][ig * 4 + 0] *= a4.x;
@@ -354,11 +361,11 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int ig = 0; ig < 4; ++ig) {
-                const float4 l4 = *reinterpret_cast<const float4*>(lsum_l + mt * 32 + ig * 8 + half * 4);
+                const float4 l4 = *reinterpret_cast<const float4*>(lsum_l + hg0 + mt * 32 + ig * 8 + half * 4);
                 const float inv[4] = {1.0f / l4.x, 1.0f / l4.y, 1.0f / l4.z, 1.0f / l4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int h = mt * 32 + ig * 8 + half * 4 + e;
+                    const int h = hg0 + mt * 32 + ig * 8 + half * 4 + e;
                     if (h < H) {
                         uint16_t* orow = out + (qi * H + h) * (int64_t)D + dim0;
 #pragma unroll
@@ -373,7 +380,7 @@ __global__ __launch_bounds__(NW * 64) void sparse_attn_kernel(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int h = mt * 32 + d_row(i, lane);
+                const int h = hg0 + mt * 32 + d_row(i, lane);
                 if (h < H) {
                     float* prow = part_o + (pbase + h) * D + dim0;
 #pragma unroll
@@ -428,17 +435,17 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     *nsplit = (nchunks + cps - 1) / cps;
 }
 
-template <int MT, int DW, int NW>
+template <int MT, int NG, int DW, int NW>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                 int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
-    using Sh = AttnShape<MT, DW, NW>;
+    using Sh = AttnShape<MT, NG, DW, NW>;
     if (Sh::LDS_BYTES > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<MT, DW, NW>,
+        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<MT, NG, DW, NW>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<MT, DW, NW><<<dim3((unsigned)(nq * nsplit)), dim3(NW * 64), Sh::LDS_BYTES, s>>>(
+    sparse_attn_kernel<MT, NG, DW, NW><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
         q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps, nsplit, out, part_o, part_ml);
     return check_launch("sckv_sparse_attn_sink");
 }
@@ -500,14 +507,17 @@ extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t 
     int rc;
     const bool two = H > 32;
 #define SCKV_ATTN(MT, DW, NW) \
-    launch_attn<MT, DW, NW>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
+    launch_attn<MT, 1, DW, NW>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
+#define SCKV_ATTN2(MT, NG, DW, NW) \
+    launch_attn<MT, NG, DW, NW>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
     switch (D) {
         case 64: rc = two ? SCKV_ATTN(2, 64, 1) : SCKV_ATTN(1, 64, 1); break;
         case 128: rc = two ? SCKV_ATTN(2, 128, 1) : SCKV_ATTN(1, 128, 1); break;
         case 256: rc = two ? SCKV_ATTN(2, 128, 2) : SCKV_ATTN(1, 128, 2); break;
-        default: rc = two ? SCKV_ATTN(2, 128, 4) : SCKV_ATTN(1, 128, 4); break;
+        default: rc = two ? SCKV_ATTN2(1, 2, 128, 4) : SCKV_ATTN(1, 128, 4); break;
     }
 #undef SCKV_ATTN
+#undef SCKV_ATTN2
     if (rc || nsplit == 1) return rc;
     if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: too many queries");
     combine_kernel<<<dim3((unsigned)nq, (unsigned)H), dim3(COMBINE_THREADS), 0, s>>>(part_o, part_ml, sink, nsplit, H,
