@@ -74,6 +74,13 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32
                  : "memory", "m0");
 }
 
+// 4-byte-per-lane form (global_load_lds_dword): lane i's 4 bytes land at
+// LDS byte lds_byte + 4 * i.
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_byte)
+                 : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(N), leaving the other counters unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -33,21 +33,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 
 // ---------------------------------------------------------------- e2m1 grid
 
-// Nearest point of {0, .5, 1, 1.5, 2, 3, 4, 6} to |y| with exact ties going to
-// the even code (codes 0..7 in grid order), sign of y kept.  The tie points
-// are the midpoints .25 .75 1.25 1.75 2.5 3.5 5: the even neighbour is 0, 1,
-// 1, 2, 2, 4, 4, which decides whether each comparison is strict.
-__device__ __forceinline__ float e2m1_round(float y) {
-    float a = fabsf(y);
-    float r = 6.0f;
-    r = (a <= 5.0f) ? 4.0f : r;
-    r = (a < 3.5f) ? 3.0f : r;
-    r = (a <= 2.5f) ? 2.0f : r;
-    r = (a < 1.75f) ? 1.5f : r;
-    r = (a <= 1.25f) ? 1.0f : r;
-    r = (a < 0.75f) ? 0.5f : r;
-    r = (a <= 0.25f) ? 0.0f : r;
-    return copysignf(r, y);
+// a = |y| (0 <= a <= 6) rounded to the nearest point of the e2m1 grid
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, exact ties going to the even code (codes 0..7
+// in grid order).
+// The grid is the multiples of 0.5 below 2, of 1 in [2, 4) and of 2 from 4
+// on, and at every midpoint the even code is the even multiple of that
+// spacing (.25 -> 0, .75 -> 1, 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4,
+// 5 -> 4).  Adding and subtracting 1.5 * 2^(23 + log2 spacing) rounds a to a
+// multiple of the spacing, half to even, in one binary32 add (exact
+// otherwise).
+__device__ __forceinline__ float e2m1_round_mag(float a) {
+    const float m = (a < 2.0f) ? 0x1.8p22f : ((a < 4.0f) ? 0x1.8p23f : 0x1.8p24f);
+    return (a + m) - m;
 }
 
 // ---------------------------------------------------------------- scale rules
@@ -91,13 +88,20 @@ __device__ __forceinline__ float block_scale(float amax) {
     }
 }
 
+// e2m1 * s is exact in bf16 for both scale kinds (at most 2 + 4 significant
+// bits, exponent within range), so the conversion is a truncation; the sign of
+// v is put back afterwards (small negative values give -0).
+__device__ __forceinline__ uint32_t signed_bf16_bits(float r, float v) {
+    return (__float_as_uint(r) | (__float_as_uint(v) & 0x80000000u)) >> 16;
+}
+
 // One value of a block: bf16 bits of e2m1(clamp(v / s, -6, 6)) * s.  The
 // quotient is the correctly rounded binary32 division (true division, not a
-// reciprocal multiply: the two differ on some exact e2m1 midpoints).
+// reciprocal multiply: the two differ on some exact e2m1 midpoints); |v| / s
+// is |v / s| since division is sign-symmetric.
 __device__ __forceinline__ uint32_t fp4_value_bits(float v, float s) {
-    float y = __fdiv_rn(v, s);
-    y = fminf(fmaxf(y, -6.0f), 6.0f);
-    return f32_to_bf16_bits(e2m1_round(y) * s);
+    const float a = fminf(__fdiv_rn(fabsf(v), s), 6.0f);
+    return signed_bf16_bits(e2m1_round_mag(a) * s, v);
 }
 
 // Exact reciprocal of a power of two 2^-126 <= s <= 2^126 (exponent flip).
@@ -105,13 +109,12 @@ __device__ __forceinline__ float pow2_reciprocal(float s) {
     return __uint_as_float((254u - ((__float_as_uint(s) >> 23) & 0xffu)) << 23);
 }
 
-// The same value as fp4_value_bits(v, s) when s is a power of two: v * (1/s)
-// rounds the same exact real number v / s once (1/s is exact), so the bits
-// are identical, subnormal results included, and no division is needed.
+// The same value as fp4_value_bits(v, s) when s is a power of two: |v| * (1/s)
+// rounds the same exact real number |v| / s once (1/s is exact), so the bits
+// are identical, subnormal quotients included, and no division is needed.
 __device__ __forceinline__ uint32_t fp4_value_bits_pow2(float v, float s, float inv_s) {
-    float y = v * inv_s;
-    y = fminf(fmaxf(y, -6.0f), 6.0f);
-    return f32_to_bf16_bits(e2m1_round(y) * s);
+    const float a = fminf(fabsf(v) * inv_s, 6.0f);
+    return signed_bf16_bits(e2m1_round_mag(a) * s, v);
 }
 
 // One value of a block in either mode (inv_s only used for power-of-two scales).

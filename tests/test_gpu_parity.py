@@ -242,6 +242,70 @@ def test_index_topk_ties(sk):
         assert np.array_equal(idx[0, t].cpu().numpy(), oracle.topk(sc[t], n_c, K, 0))
 
 
+# The one-launch path (scores and top-K in one workgroup per query) is taken
+# when no scores are requested and there are enough queries; these cases cover
+# its three key counts per thread, both head tilings, the shallow ring of the
+# widest head dim, queries that see at most K rows, and ties.
+FUSED_CASES = [
+    # B, m, Hi, Di, n_c, ratio, start_pos, K
+    (192, 1, 64, 128, 1024, 4, 4095, 200),   # decode-like, 4 keys per thread
+    (200, 1, 4, 32, 9000, 1, 8999, 1000),    # 9088 rows: 128 keys per thread
+    (192, 1, 32, 256, 1500, 1, 1499, 100),   # head dim 256 (shallow ring), 8 keys per thread
+    (1, 256, 8, 64, 64, 1, 0, 16),           # prefill from 0: queries 0..15 see <= K rows
+    (1, 300, 64, 128, 700, 2, 1000, 350),    # ragged tail, V from 500 to 650
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "B{}m{}Hi{}Di{}nc{}K{}".format(*c[:5], c[7]))
+def test_index_topk_fused_bit_exact(sk, case):
+    """Every sequence shares one k cache and has its own q and w; the oracle
+    checks a sample of the (sequence, query) lists, spread over the grid."""
+    B, m, Hi, Di, n_c, ratio, start_pos, K = case
+    rng = np.random.default_rng(sum(case) + 7)
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di))))
+    kb = oracle.quant(bits(bf16_of(rng.standard_normal((n_c, Di)))).reshape(-1), oracle.E8M0_B32).reshape(n_c, Di)
+    k = np.broadcast_to(kb, (B, n_c, Di)).copy()
+    w = (rng.standard_normal((B, m, Hi)) * (Hi * Di) ** -0.5).astype(np.float32)
+    col0, off = 2, 77
+    ld = col0 + K + 1
+    idx = torch.full((B, m, ld), -5, dtype=torch.int32, device="cuda")
+    say(f"fused indexer case {case}")
+    sk.sckv_index_scores_topk(from_bits(q, "cuda"), from_bits(k, "cuda"), torch.from_numpy(w).cuda(), B, m, Hi, Di,
+                              n_c, ratio, start_pos, K, off, idx, ld, col0)
+    got = idx.cpu().numpy()
+    assert np.all(got[:, :, :col0] == -5) and np.all(got[:, :, col0 + K:] == -5)
+    bsel = sorted({0, B - 1, *rng.integers(0, B, size=4).tolist()})
+    tsel = np.array(sorted({0, m - 1, *rng.integers(0, m, size=8).tolist()} if m > 1 else {0}), dtype=np.int64)
+    if m == 256:
+        tsel = np.arange(m, dtype=np.int64)  # cheap: every query
+    for b in bsel:
+        sc, bad = oracle.index_scores(q[b], kb, w[b], start_pos, ratio, qsel=tsel)
+        assert bad == 0
+        for i, t in enumerate(tsel):
+            v = oracle.visible(start_pos + int(t), ratio, n_c)
+            assert np.array_equal(got[b, t, col0:col0 + K], oracle.topk(sc[i], v, K, off)), (b, t)
+
+
+def test_index_topk_fused_ties(sk):
+    """The one-launch path with forced ties at the K-th place (repeated k rows,
+    one weighted head): the lower rows must win."""
+    B, m, Hi, Di, n_c, K = 192, 1, 4, 32, 500, 64
+    rng = np.random.default_rng(98)
+    base = bits(bf16_of(rng.standard_normal((8, Di))))
+    kb = oracle.quant(base[rng.integers(0, 8, size=n_c)].reshape(-1), oracle.E8M0_B32).reshape(n_c, Di)
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di))))
+    w = np.zeros((B, m, Hi), np.float32)
+    w[:, :, 0] = 1.0
+    idx = torch.empty((B, m, K), dtype=torch.int32, device="cuda")
+    say("fused indexer ties")
+    sk.sckv_index_scores_topk(from_bits(q, "cuda"), from_bits(np.broadcast_to(kb, (B, n_c, Di)).copy(), "cuda"),
+                              torch.from_numpy(w).cuda(), B, m, Hi, Di, n_c, 1, n_c - 1, K, 0, idx, K, 0)
+    got = idx.cpu().numpy()
+    for b in (0, 1, 95, 191):
+        sc, _ = oracle.index_scores(q[b], kb, w[b], n_c - 1, 1)
+        assert np.array_equal(got[b, 0], oracle.topk(sc[0], n_c, K, 0)), b
+
+
 # --------------------------------------------------------------------- attention
 
 ATTN_CASES = [
