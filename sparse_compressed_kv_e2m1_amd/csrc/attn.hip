@@ -9,25 +9,26 @@
 // no value row; every row is both key and value (MQA, one shared row).
 //
 // Design (gfx950).  One workgroup = one query x a range of 32-row chunks of
-// its index list.  All heads (padded to 32 or 64) form the MFMA M dimension,
-// so every gathered row byte feeds every head.  NW waves split the head
-// dimension D: wave w owns dims [w*DW, (w+1)*DW) of Q (in registers) and of O
-// (in accumulators).  Per chunk:
-//   1. rows arrive by asynchronous global->LDS copies (global_load_lds_dwordx4:
-//      one instruction moves one whole 1 KiB row, fully coalesced), issued two
-//      chunks ahead into a 3-stage ring; each wave brings in 32/NW rows;
-//   2. S_w = Q[:, dims_w] . R[:, dims_w]^T on the matrix cores (B operand read
-//      from the row-major stage);
-//   3. the NW partial logit tiles meet in LDS; wave w sums the tiles of its own
-//      HP/NW heads (fixed order) and runs the online softmax for them in base 2
-//      (the running max starts at the sink logit and only moves when a logit
-//      exceeds it by more than 2^8, so rescaling is rare); P goes back to LDS
-//      in bf16;
-//   4. every wave reads all of P (A layout) and O[:, dims_w] += P . R[:, dims_w],
-//      the B operand coming from the same row-major stage through the
-//      transposing LDS read (ds_read_b64_tr_b16), so no second copy of the rows.
-// A query's chunks may be split over several workgroups; their partial
-// (max, sum, O) are merged by a small combine kernel that adds the sink once.
+// its index list.  Its waves form two sets that take alternate chunks; inside
+// a set, wave w owns heads 16w .. 16w+15 over the whole head dim, so a wave
+// never needs another wave's numbers until the very end:
+//   1. a chunk's rows arrive by asynchronous global->LDS copies
+//      (global_load_lds_dwordx4, one instruction per 1 KiB row, fully
+//      coalesced), spread over the set's waves and requested one chunk ahead
+//      into a two-stage ring per set;
+//   2. S^T = R . Q^T on the matrix cores (16x16x32 bf16: rows are M, the
+//      wave's 16 heads N, the head dim K; Q^T sits in registers);
+//   3. the online softmax runs in the MFMA result layout (a lane holds one
+//      head and 8 of the 32 rows; max and sum finish with two lane swaps), in
+//      base 2, with a running max that starts at the sink logit and moves only
+//      when a logit exceeds it by more than the slack;
+//   4. the probabilities are already the A operand of O += P . R (16x16x32
+//      again, K = the chunk's rows), whose B operand comes from the same stage
+//      through the transposing LDS read (ds_read_b64_tr_b16).
+// One barrier per pair of chunks (one per set).  At the end the second set
+// hands its (max, sum, O) to the first through LDS.  A query's chunks may
+// also be split over several workgroups; their partials are merged by a small
+// combine kernel that adds the sink once.
 #include "mfma.h"
 #include "sckv_device.h"
 
@@ -39,357 +40,306 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float STALE_MAX = 8.0f;  // base-2 slack before the running max moves
 constexpr int MAX_CPS = 64;        // chunks one workgroup handles at most (its index range sits in LDS)
 
-// MT head tiles of 32 per wave, NG head groups, NW waves per group splitting
-// the head dim into slices of DW: NG * NW waves, NG * MT * 32 padded heads.
-template <int MT, int NG, int DW, int NW>
+// Head dim D, NHW head waves per set (16 heads each): 2 * NHW waves.
+template <int D, int NHW>
 struct AttnShape {
-    static constexpr int WAVES = NG * NW;
-    static constexpr int HG = MT * 32;             // padded heads of one group
-    static constexpr int HP = NG * HG;             // padded heads
-    static constexpr int D = DW * NW;
-    static constexpr int KS = DW / 16;             // k-steps of Q.R^T per wave
-    static constexpr int NT = DW / 32;             // 32-wide output tiles per wave
-    static constexpr int RPW = CHUNK / WAVES;      // rows each wave copies in per chunk
-    static constexpr int PD = (RPW <= 16) ? 2 : 1; // chunks in flight ahead of the one computed
-    static constexpr int NST = PD + 1;             // stages in the ring
-    static constexpr int RS = 2 * D + 32;          // bytes per row in a stage (32-byte pad: no bank conflicts)
+    static constexpr int WAVES = 2 * NHW;
+    static constexpr int HP = 16 * NHW;     // padded heads
+    static constexpr int KS = D / 32;       // k-steps of S^T = R . Q^T
+    static constexpr int NT = D / 16;       // 16-wide output tiles
+    static constexpr int RPW = CHUNK / NHW; // rows a wave copies in per chunk of its set
+    static constexpr int NST = 2;           // stages per set
+    // row stride in a stage: RS / 4 is 4 times an odd number, so 16 rows read at one column
+    // (the A operand) and the transposing reads hit every bank evenly
+    static constexpr int RS = 2 * D + 16;
     static constexpr int STAGE = CHUNK * RS;
-    static constexpr int HW = HP / WAVES;          // heads whose softmax one wave owns
-    static constexpr int LPH = 64 / HW;            // lanes per owned head
-    static constexpr int VPL = CHUNK / LPH;        // logits per lane in the softmax
-    static constexpr int SXS = CHUNK + 4;          // floats per head row of a partial-logit tile
-    static constexpr int PS = CHUNK + 8;           // bf16 per head row of P
-    static constexpr int OFF_SX = NST * STAGE;
-    static constexpr int OFF_P = OFF_SX + NW * HP * SXS * 4;  // NW partial tiles per head
-    static constexpr int OFF_ALPHA = OFF_P + HP * PS * 2;
-    static constexpr int OFF_L = OFF_ALPHA + HP * 4;
-    static constexpr int OFF_FLAG = OFF_L + HP * 4;
-    static constexpr int OFF_IDX = OFF_FLAG + 4 * WAVES;
+    static constexpr int OFF_IDX = 2 * NST * STAGE;
     static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
-    static_assert(VPL % 4 == 0 && LPH >= 1 && LPH <= 16 && RPW % 4 == 0, "softmax split");
+    // the second set's O (HP rows of D + 4 floats) and (max, sum) reuse the stages
+    static constexpr int OS = D + 4;
+    static_assert((size_t)HP * OS * 4 + HP * 8 <= (size_t)OFF_IDX, "merge space");
+    static_assert(RPW % 4 == 0 && ((RS / 4) % 8) == 4, "shape");
 };
 
-// Max / sum over aligned groups of G consecutive lanes (G = 1, 2, 4, 8, 16),
-// every lane receiving the group's result, with DPP lane permutes (no LDS
-// round trip): quad_perm swaps within 2 and 4 lanes, half-row and row mirrors
-// pair the 4-lane and 8-lane halves.
-template <int G>
-__device__ __forceinline__ float group_max(float v) {
-    if (G >= 2) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false)));
-    if (G >= 4) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false)));
-    if (G >= 8) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false)));
-    if (G >= 16) v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false)));
-    return v;
+// max / sum over the four lanes l, l^16, l^32, l^48 (same head in the MFMA
+// result layout)
+__device__ __forceinline__ float max4x16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
 }
-template <int G>
-__device__ __forceinline__ float group_sum(float v) {
-    if (G >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
-    if (G >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
-    if (G >= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xf, 0xf, false));
-    if (G >= 16) v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xf, 0xf, false));
-    return v;
+__device__ __forceinline__ float sum4x16(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
 }
 
-// Wait until at most n of this wave's row copies are in flight (n uniform, one of 0, RPW, 2*RPW).
-template <int RPW>
-__device__ __forceinline__ void wait_rows(int n) {
-    if (n == 0)
-        wait_vmcnt<0>();
-    else if (n == RPW)
-        wait_vmcnt<RPW>();
-    else
-        wait_vmcnt<(2 * RPW < 64 ? 2 * RPW : 63)>();
-}
-
-template <int MT, int NG, int DW, int NW>
-__global__ __launch_bounds__(NG * NW * 64) void sparse_attn_kernel(
+template <int D, int NHW>
+__global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    using S = AttnShape<MT, NG, DW, NW>;
-    constexpr int D = S::D;
+    using S = AttnShape<D, NHW>;
     constexpr int NTH = S::WAVES * 64;
     extern __shared__ __align__(16) unsigned char lds[];
-    float* sx = reinterpret_cast<float*>(lds + S::OFF_SX);
-    uint16_t* pl = reinterpret_cast<uint16_t*>(lds + S::OFF_P);
-    float* alpha_l = reinterpret_cast<float*>(lds + S::OFF_ALPHA);
-    float* lsum_l = reinterpret_cast<float*>(lds + S::OFF_L);
-    int* flags = reinterpret_cast<int*>(lds + S::OFF_FLAG);
     int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
     const uint32_t lds0 = lds_offset(lds);
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int r_lane = lane & 31;  // row of this lane in B layout / head in A layout
-    const int half = lane >> 5;
+    const int set = wave / NHW;  // chunk parity this wave computes
+    const int hw = wave % NHW;   // heads 16 hw .. 16 hw + 15
+    const int l16 = lane & 15;
+    const int g = lane >> 4;
     const int64_t qi = blockIdx.x / nsplit;
     const int split = (int)(blockIdx.x - qi * nsplit);
     const int64_t b = qi / m;
-    const int grp = wave / NW;          // head group: heads grp*HG .. grp*HG + HG-1
-    const int dim0 = (wave % NW) * DW;  // head-dim slice
-    const int hg0 = grp * S::HG;
     const uint16_t* rows_a_b = rows_a + b * ra * D;
     const uint16_t* rows_b_b = rows_b ? rows_b + b * rb * D : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
     const uint16_t* qrow = q + qi * (int64_t)H * D;
 
-    // ---- Q slice in A layout: head mt*32 + r_lane, dims dim0 + ks*16 + half*8 + 0..7
-    bf16x8 qa[MT][S::KS];
+    // ---- Q^T in B layout: head 16 hw + l16, dims ks*32 + g*8 + 0..7
+    const int head = 16 * hw + l16;  // the head this lane follows in the softmax
+    bf16x8 qb[S::KS];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int h = hg0 + mt * 32 + r_lane;
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks)
-            qa[mt][ks] = as_bf16x8((h < H) ? load16(qrow + (int64_t)h * D + dim0 + ks * 16 + half * 8)
-                                           : u32x4{0, 0, 0, 0});
-    }
-    // softmax state of the head this lane helps own: hr, rows r0 .. r0+VPL-1
-    const int hr = S::HW * wave + lane / S::LPH;
-    const int r0 = (lane % S::LPH) * S::VPL;
-    float m_run = (hr < H) ? sink[hr] * LOG2E : 0.0f;  // base-2 running max, starting at the sink
-    float l_run = (nsplit == 1) ? 1.0f : 0.0f;          // e^(sink - M) at M = sink; splits add it when merged
+    for (int ks = 0; ks < S::KS; ++ks)
+        qb[ks] = as_bf16x8((head < H) ? load16(qrow + (int64_t)head * D + ks * 32 + g * 8) : u32x4{0, 0, 0, 0});
+    float m_run = (head < H) ? sink[head] * LOG2E : 0.0f;  // base-2 running max, starting at the sink
+    // e^(sink - M) at M = sink, counted once: by the first set of an unsplit query
+    float l_run = (nsplit == 1 && set == 0) ? 1.0f : 0.0f;
 
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int c_begin = split * chunks_per_split;
     int c_end = c_begin + chunks_per_split;
     c_end = c_end < nchunks ? c_end : nchunks;
+    const int nch = c_end - c_begin;
     {
         // this workgroup's slice of the index list, staged once in LDS
         const int e0 = c_begin * CHUNK;
         const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
-        for (int i = threadIdx.x; i < (c_end - c_begin) * CHUNK; i += NTH) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
+        for (int i = threadIdx.x; i < nch * CHUNK; i += NTH) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
     }
     // Every ordinary global load above is complete before the first row copy is
     // issued, so no compiler-placed wait inside the loop can stall on the copies.
     wait_vmcnt<0>();
     __syncthreads();
 
-    // Copy chunk c's rows (this wave's share) into its stage; returns the chunk's
-    // valid-row mask (identical in every wave).  Invalid rows of a partly valid
-    // chunk copy this query's first q row instead (finite data; masked later).
-    auto issue = [&](int c) -> uint32_t {
-        const int32_t* ic = idx_l + (c - c_begin) * CHUNK;
-        const int32_t mine = ic[r_lane];
-        const uint32_t mask =
-            (uint32_t)(__ballot((mine >= 0) && ((int64_t)mine < ra + rb)) & 0xffffffffull);
-        if (mask) {
-            const uint32_t st = lds0 + (uint32_t)((c % S::NST) * S::STAGE);
-            // this wave's RPW entries in one go (broadcast LDS reads), then scalar
-            int32_t ivv[S::RPW];
-#pragma unroll
-            for (int v4 = 0; v4 < S::RPW / 4; ++v4) {
-                const int4 t4 = *reinterpret_cast<const int4*>(ic + wave * S::RPW + 4 * v4);
-                ivv[4 * v4 + 0] = t4.x;
-                ivv[4 * v4 + 1] = t4.y;
-                ivv[4 * v4 + 2] = t4.z;
-                ivv[4 * v4 + 3] = t4.w;
-            }
-#pragma unroll
-            for (int rr = 0; rr < S::RPW; ++rr) {
-                const int r = wave * S::RPW + rr;
-                const int32_t iv = __builtin_amdgcn_readfirstlane(ivv[rr]);
-                const bool valid = (iv >= 0) && ((int64_t)iv < ra + rb);
-                const uint16_t* src = !valid ? qrow
-                                             : (((int64_t)iv < ra) ? rows_a_b + (int64_t)iv * D
-                                                                   : rows_b_b + ((int64_t)iv - ra) * D);
-                if (lane < D / 8) dma16_s(src, (uint32_t)lane * 16u, st + (uint32_t)(r * S::RS));
-            }
-        }
-        return mask;
+    // Non-empty chunks as a bitmap (uniform): bit j set when chunk c_begin + j
+    // names at least one valid row.  Empty chunks are neither copied nor
+    // computed.  Non-empty chunk number k goes to set k % 2.
+    const uint32_t rab = (uint32_t)(ra + rb);
+    uint64_t todo = 0;
+    for (int j = 0; j < nch; j += 2) {
+        const int jj = j + (lane >> 5);
+        const bool v = (jj < nch) && ((uint32_t)idx_l[jj * CHUNK + (lane & 31)] < rab);
+        const uint64_t bal = __ballot(v);
+        todo |= (uint64_t)((bal & 0xffffffffull) != 0) << j;
+        todo |= (uint64_t)((bal >> 32) != 0) << (j + 1);
+    }
+    const int n = __builtin_popcountll(todo);
+    const int n_own = (n > set) ? (n - set + 1) / 2 : 0;  // chunks of this wave's set
+    const int n_it = (n + 1) / 2;                         // iterations (same in every wave)
+    // this set's chunks in order: take one bit, skip the other set's next one
+    auto next_own = [](uint64_t& bits) -> int {
+        const int j = __builtin_ctzll(bits);
+        bits &= bits - 1;
+        if (bits) bits &= bits - 1;
+        return j;
     };
-
-    f32x16 o[MT][S::NT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < S::NT; ++nt) o[mt][nt] = zero16();
-
-    uint32_t mk[S::PD + 1];
-#pragma unroll
-    for (int j = 0; j < S::PD; ++j) mk[j] = (c_begin + j < c_end) ? issue(c_begin + j) : 0u;
-
-    const int g = lane >> 4;
-    const int quad = (lane & 15) >> 2;
-    const int a4l = lane & 3;
-    // O[:, dims_w] += P . R[:, dims_w] for the chunk in stage stp
-    auto pv = [&](const unsigned char* stp) {
-        bf16x8 pa[MT][2];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr)
-                pa[mt][kr] = *reinterpret_cast<const bf16x8*>(pl + (hg0 + mt * 32 + r_lane) * S::PS + kr * 16 + half * 8);
-#pragma unroll
-        for (int nt = 0; nt < S::NT; ++nt) {
-            const int dcol = dim0 + nt * 32 + (g & 1) * 16 + 4 * a4l;
-#pragma unroll
-            for (int kr = 0; kr < 2; ++kr) {
-                const int row = kr * 16 + (g >> 1) * 8 + quad;
-                const i16x4 lo = lds_read_tr16(stp + row * S::RS + dcol * 2);
-                const i16x4 hi = lds_read_tr16(stp + (row + 4) * S::RS + dcol * 2);
-                const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) o[mt][nt] = mfma32x32x16(pa[mt][kr], bv, o[mt][nt]);
-            }
-        }
-    };
-
-    // Chunk loop.  The inner loop never touches O with vector ALU work (so O
-    // stays in accumulation registers); it leaves only when a head's running
-    // max must move, which the outer loop handles by rescaling O.
-    int c = c_begin;
-    for (;;) {
-        bool moved = false;
-        const unsigned char* stp = lds;
-        for (; c < c_end; ++c) {
-            // chunk c's copies done (later chunks' copies may still fly), then everyone's
-            int after = 0;
-#pragma unroll
-            for (int j = 1; j < S::PD; ++j) after += mk[j] ? S::RPW : 0;
-            if (mk[0]) wait_rows<S::RPW>(after);
-            __syncthreads();
-            mk[S::PD] = (c + S::PD < c_end) ? issue(c + S::PD) : 0u;  // into the stage chunk c-1 used
-            const uint32_t mask = mk[0];
-#pragma unroll
-            for (int j = 0; j < S::PD; ++j) mk[j] = mk[j + 1];
-            if (mask == 0) continue;
-            stp = lds + (c % S::NST) * S::STAGE;
-
-            // partial logits over this wave's dims, as S^T = R . Q^T: rows are the
-            // MFMA M dimension, heads the N dimension, so each lane ends up with one
-            // head and runs of 4 consecutive rows (the A/B register layouts of R and
-            // Q are the same as for S = Q . R^T, only the operand order changes)
-            f32x16 sp[MT];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) sp[mt] = zero16();
-#pragma unroll
-            for (int ks = 0; ks < S::KS; ++ks) {
-                const bf16x8 rk =
-                    *reinterpret_cast<const bf16x8*>(stp + r_lane * S::RS + (dim0 + ks * 16 + half * 8) * 2);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) sp[mt] = mfma32x32x16(rk, qa[mt][ks], sp[mt]);
-            }
-            // sx[wave][head][row]: lane's head mt*32 + r_lane, rows d_row(4*i4, lane) .. +3
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4)
-                    *reinterpret_cast<float4*>(sx + ((wave % NW) * S::HP + hg0 + mt * 32 + r_lane) * S::SXS + d_row(4 * i4, lane)) =
-                        make_float4(sp[mt][4 * i4], sp[mt][4 * i4 + 1], sp[mt][4 * i4 + 2], sp[mt][4 * i4 + 3]);
-            __syncthreads();
-
-            // this wave's heads: sum the NW partial tiles (fixed order), online softmax
-            float x[S::VPL];
-#pragma unroll
-            for (int j = 0; j < S::VPL; ++j) x[j] = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                const float* src = sx + (ww * S::HP + hr) * S::SXS + r0;
-#pragma unroll
-                for (int j4 = 0; j4 < S::VPL / 4; ++j4) {
-                    const float4 a = *reinterpret_cast<const float4*>(src + 4 * j4);
-                    x[4 * j4 + 0] += a.x;
-                    x[4 * j4 + 1] += a.y;
-                    x[4 * j4 + 2] += a.z;
-                    x[4 * j4 + 3] += a.w;
-                }
-            }
-            float cmax = -INFINITY;
-#pragma unroll
-            for (int j = 0; j < S::VPL; ++j) {
-                x[j] = ((mask >> (r0 + j)) & 1u) ? x[j] * scale_log2 : -INFINITY;
-                cmax = fmaxf(cmax, x[j]);
-            }
-            cmax = group_max<S::LPH>(cmax);
-            const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            float psum = 0.0f;
-            uint32_t pk[S::VPL / 2];
-#pragma unroll
-            for (int j = 0; j < S::VPL; j += 2) {
-                // hardware exp2 (v_exp_f32) and round-to-nearest-even pack to bf16
-                // (v_cvt_pk_bf16_f32); the sum uses the rounded weights
-                const f32x2 pf = {__builtin_amdgcn_exp2f(x[j] - m_new), __builtin_amdgcn_exp2f(x[j + 1] - m_new)};
-                const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2));
-                psum += __uint_as_float(pb << 16) + __uint_as_float(pb & 0xffff0000u);
-                pk[j / 2] = pb;
-            }
-            psum = group_sum<S::LPH>(psum);
-            l_run = l_run * alpha + psum;
-            const bool my_move = m_new != m_run;
-            m_run = m_new;
-            {
-                uint16_t* dst = pl + hr * S::PS + r0;
-#pragma unroll
-                for (int j4 = 0; j4 < S::VPL / 4; ++j4)
-                    *reinterpret_cast<uint2*>(dst + 4 * j4) = make_uint2(pk[2 * j4], pk[2 * j4 + 1]);
-            }
-            if (lane % S::LPH == 0) alpha_l[hr] = alpha;
-            const uint64_t any_moved = __ballot(my_move);
-            if (lane == 0) flags[wave] = any_moved != 0;
-            __syncthreads();
-#pragma unroll
-            for (int ww = 0; ww < S::WAVES; ++ww) moved |= flags[ww] != 0;
-            if (moved) break;
-            pv(stp);
-        }
-        if (!moved) break;
-        // rare: some head's max moved by more than the slack; rescale O, then this chunk's P.R
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int ig = 0; ig < 4; ++ig) {
-                const float4 a4 = *reinterpret_cast<const float4*>(alpha_l + hg0 + mt * 32 + ig * 8 + half * 4);
-#pragma unroll
-                for (int nt = 0; nt < S::NT; ++nt) {
-                    o[mt][nt][ig * 4 + 0] *= a4.x;
-                    o[mt][nt][ig * 4 + 1] *= a4.y;
-                    o[mt][nt][ig * 4 + 2] *= a4.z;
-                    o[mt][nt][ig * 4 + 3] *= a4.w;
-                }
-            }
-        pv(stp);
-        ++c;
+    uint64_t ib = todo, cb = todo;
+    if (set == 1 && ib) {
+        ib &= ib - 1;
+        cb &= cb - 1;
     }
 
-    // ---- epilogue
-    if (nsplit == 1) {
-        if (lane % S::LPH == 0) lsum_l[hr] = l_run;
-        __syncthreads();
+    // Copy this wave's RPW rows of chunk j into stage `slot` of its set.
+    // Invalid entries of a partly valid chunk copy this query's first q row
+    // instead (finite data; their weights are zero).
+    const uint16_t* rows_b_sh = rows_b_b ? rows_b_b - ra * D : rows_a_b;  // + iv*D == rows_b[iv - ra]
+    auto issue = [&](int slot, int j) {
+        const int32_t* ic = idx_l + j * CHUNK + hw * S::RPW;
+        const uint32_t st = lds0 + (uint32_t)((set * S::NST + slot) * S::STAGE);
+        int32_t ivv[S::RPW];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int v4 = 0; v4 < S::RPW / 4; ++v4) {
+            const int4 t4 = *reinterpret_cast<const int4*>(ic + 4 * v4);
+            ivv[4 * v4 + 0] = t4.x;
+            ivv[4 * v4 + 1] = t4.y;
+            ivv[4 * v4 + 2] = t4.z;
+            ivv[4 * v4 + 3] = t4.w;
+        }
 #pragma unroll
-            for (int ig = 0; ig < 4; ++ig) {
-                const float4 l4 = *reinterpret_cast<const float4*>(lsum_l + hg0 + mt * 32 + ig * 8 + half * 4);
-                const float inv[4] = {1.0f / l4.x, 1.0f / l4.y, 1.0f / l4.z, 1.0f / l4.w};
+        for (int rr = 0; rr < S::RPW; ++rr) {
+            const uint32_t iv = (uint32_t)__builtin_amdgcn_readfirstlane(ivv[rr]);
+            const uint16_t* base = (iv < (uint32_t)ra) ? rows_a_b : rows_b_sh;
+            const uint16_t* src = (iv < rab) ? base + (size_t)iv * D : qrow;
+            if (lane < D / 8) dma16_s(src, (uint32_t)lane * 16u, st + (uint32_t)((hw * S::RPW + rr) * S::RS));
+        }
+    };
+
+    f32x4 o[S::NT];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int h = hg0 + mt * 32 + ig * 8 + half * 4 + e;
-                    if (h < H) {
-                        uint16_t* orow = out + (qi * H + h) * (int64_t)D + dim0;
+    for (int nt = 0; nt < S::NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    bf16x8 pa;          // this chunk's probabilities, A operand of P . R
+    float alpha = 1.0f; // rescale factor of the last max move (head of this lane)
+
+    if (n_own > 0) issue(0, next_own(ib));
+
+    // ---- chunk loop.  The inner loop never applies vector ALU work to O (so O
+    // stays in accumulation registers); it leaves when one of the wave's heads
+    // moved its running max, and the outer loop rescales O before P . R.
+    int it = 0;
+    bool resume = false;
+    for (;;) {
+        bool rescale = false;
+        for (; it < n_it; ++it) {
+            const unsigned char* stp = lds + (set * S::NST + (it & 1)) * S::STAGE;
+            if (!resume) {
+                wait_vmcnt<0>();  // this wave's copies of its current chunk landed
+                __syncthreads();  // everyone's did; last iteration's stages are free
+                if (it + 1 < n_own) issue((it + 1) & 1, next_own(ib));
+                if (it < n_own) {
+                    const int j = next_own(cb);
+                    const uint32_t mask =
+                        (uint32_t)(__ballot((uint32_t)idx_l[j * CHUNK + (lane & 31)] < rab) & 0xffffffffull);
+                    // S^T for rows 0-15 and 16-31: lane holds head l16, rows mt*16 + g*4 + 0..3
+                    f32x4 sp[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-                        for (int nt = 0; nt < S::NT; ++nt)
-                            orow[nt * 32 + r_lane] = (uint16_t)f32_to_bf16_bits(o[mt][nt][ig * 4 + e] * inv[e]);
+                    for (int ks = 0; ks < S::KS; ++ks)
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt) {
+                            const bf16x8 rk = *reinterpret_cast<const bf16x8*>(stp + (mt * 16 + l16) * S::RS +
+                                                                               ks * 64 + g * 16);
+                            sp[mt] = mfma16x16x32(rk, qb[ks], sp[mt]);
+                        }
+                    float x[8];
+                    float cmax = -INFINITY;
+#pragma unroll
+                    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int r = mt * 16 + g * 4 + i;
+                            const float v = ((mask >> r) & 1u) ? sp[mt][i] * scale_log2 : -INFINITY;
+                            x[mt * 4 + i] = v;
+                            cmax = fmaxf(cmax, v);
+                        }
+                    cmax = max4x16(cmax);
+                    const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
+                    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    float psum = 0.0f;
+                    uint32_t pk[4];
+#pragma unroll
+                    for (int j2 = 0; j2 < 4; ++j2) {
+                        // hardware exp2 (v_exp_f32) and round-to-nearest-even pack to
+                        // bf16 (v_cvt_pk_bf16_f32); the sum uses the rounded weights
+                        const f32x2 pf = {__builtin_amdgcn_exp2f(x[2 * j2] - m_new),
+                                          __builtin_amdgcn_exp2f(x[2 * j2 + 1] - m_new)};
+                        const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2));
+                        psum += __uint_as_float(pb << 16) + __uint_as_float(pb & 0xffff0000u);
+                        pk[j2] = pb;
+                    }
+                    l_run = l_run * alpha + sum4x16(psum);
+                    const bool moved = __ballot(m_new != m_run) != 0;
+                    m_run = m_new;
+                    pa = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
+                    if (moved) {
+                        rescale = true;
+                        break;
                     }
                 }
             }
-    } else {
-        const int64_t pbase = (qi * nsplit + split) * (int64_t)H;
+            resume = false;
+            if (it < n_own) {
+                // O[heads, :] += P . R: k = g*8 + 0..3 are rows g*4 + 0..3, k = g*8 + 4..7
+                // rows 16 + g*4 + 0..3 (the order the probabilities sit in)
+                const int jj = l16 >> 2;
+                const int c4 = 4 * (l16 & 3);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int h = hg0 + mt * 32 + d_row(i, lane);
-                if (h < H) {
-                    float* prow = part_o + (pbase + h) * D + dim0;
-#pragma unroll
-                    for (int nt = 0; nt < S::NT; ++nt) prow[nt * 32 + r_lane] = o[mt][nt][i];
+                for (int nt = 0; nt < S::NT; ++nt) {
+                    const unsigned char* pc = stp + (nt * 16 + c4) * 2;
+                    const i16x4 lo = lds_read_tr16(pc + (g * 4 + jj) * S::RS);
+                    const i16x4 hi = lds_read_tr16(pc + (16 + g * 4 + jj) * S::RS);
+                    const bf16x8 bv =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[nt] = mfma16x16x32(pa, bv, o[nt]);
                 }
             }
-        if (lane % S::LPH == 0 && hr < H) {
-            part_ml[(pbase + hr) * 2 + 0] = m_run;
-            part_ml[(pbase + hr) * 2 + 1] = l_run;
+        }
+        if (!rescale) break;
+        // rare: a running max moved by more than the slack; O rows are heads
+        // 16 hw + g*4 + i, whose factors sit in lanes g*4 + i
+        float a4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a4[i] = __shfl(alpha, g * 4 + i, 64);
+#pragma unroll
+        for (int nt = 0; nt < S::NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[nt][i] *= a4[i];
+        resume = true;
+    }
+
+    // ---- epilogue: the second set hands (max, sum, O) to the first through LDS
+    __syncthreads();  // all stages idle
+    float* mo = reinterpret_cast<float*>(lds);           // [HP][OS]
+    float* ml = reinterpret_cast<float*>(lds) + S::HP * S::OS;  // [HP][2]
+    if (set == 1) {
+#pragma unroll
+        for (int nt = 0; nt < S::NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mo[(16 * hw + g * 4 + i) * S::OS + nt * 16 + l16] = o[nt][i];
+        if (g == 0) {
+            ml[head * 2 + 0] = m_run;
+            ml[head * 2 + 1] = l_run;
+        }
+    }
+    __syncthreads();
+    if (set == 0) {
+        const float m1 = ml[head * 2 + 0], l1 = ml[head * 2 + 1];
+        const float M = fmaxf(m_run, m1);
+        const float a0 = __builtin_amdgcn_exp2f(m_run - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
+        const float L = l_run * a0 + l1 * a1;
+        // per O row (head 16 hw + g*4 + i): the factors from lane g*4 + i
+        float f0[4], f1[4], Li[4], Mi[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f0[i] = __shfl(a0, g * 4 + i, 64);
+            f1[i] = __shfl(a1, g * 4 + i, 64);
+            Li[i] = __shfl(L, g * 4 + i, 64);
+            Mi[i] = __shfl(M, g * 4 + i, 64);
+        }
+        if (nsplit == 1) {
+            float inv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) inv[i] = 1.0f / Li[i];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * hw + g * 4 + i;
+                if (h < H) {
+                    uint16_t* orow = out + (qi * H + h) * (int64_t)D;
+                    const float* prow = mo + h * S::OS;
+#pragma unroll
+                    for (int nt = 0; nt < S::NT; ++nt) {
+                        const float v = (o[nt][i] * f0[i] + prow[nt * 16 + l16] * f1[i]) * inv[i];
+                        orow[nt * 16 + l16] = (uint16_t)f32_to_bf16_bits(v);
+                    }
+                }
+            }
+        } else {
+            const int64_t pbase = (qi * nsplit + split) * (int64_t)H;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 16 * hw + g * 4 + i;
+                if (h < H) {
+                    float* orow = part_o + (pbase + h) * D;
+                    const float* prow = mo + h * S::OS;
+#pragma unroll
+                    for (int nt = 0; nt < S::NT; ++nt) orow[nt * 16 + l16] = o[nt][i] * f0[i] + prow[nt * 16 + l16] * f1[i];
+                    if (l16 == 0) {
+                        part_ml[(pbase + h) * 2 + 0] = Mi[i];
+                        part_ml[(pbase + h) * 2 + 1] = Li[i];
+                    }
+                }
+            }
         }
     }
 }
@@ -435,19 +385,33 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     *nsplit = (nchunks + cps - 1) / cps;
 }
 
-template <int MT, int NG, int DW, int NW>
+template <int D, int NHW>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                 int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
-    using Sh = AttnShape<MT, NG, DW, NW>;
+    using Sh = AttnShape<D, NHW>;
     if (Sh::LDS_BYTES > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<MT, NG, DW, NW>,
+        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<MT, NG, DW, NW><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
+    sparse_attn_kernel<D, NHW><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
         q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps, nsplit, out, part_o, part_ml);
     return check_launch("sckv_sparse_attn_sink");
+}
+
+template <int D>
+int launch_attn_d(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
+                  const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
+                  int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
+    if (H <= 16)
+        return launch_attn<D, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
+                                 part_o, part_ml, s);
+    if (H <= 32)
+        return launch_attn<D, 2>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
+                                 part_o, part_ml, s);
+    return launch_attn<D, 4>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out, part_o,
+                             part_ml, s);
 }
 
 }  // namespace
@@ -505,19 +469,15 @@ extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t 
     const uint16_t* bb = (const uint16_t*)rows_b;
     uint16_t* oo = (uint16_t*)out;
     int rc;
-    const bool two = H > 32;
-#define SCKV_ATTN(MT, DW, NW) \
-    launch_attn<MT, 1, DW, NW>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
-#define SCKV_ATTN2(MT, NG, DW, NW) \
-    launch_attn<MT, NG, DW, NW>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
+#define SCKV_ATTN(D) \
+    launch_attn_d<D>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
     switch (D) {
-        case 64: rc = two ? SCKV_ATTN(2, 64, 1) : SCKV_ATTN(1, 64, 1); break;
-        case 128: rc = two ? SCKV_ATTN(2, 128, 1) : SCKV_ATTN(1, 128, 1); break;
-        case 256: rc = two ? SCKV_ATTN(2, 128, 2) : SCKV_ATTN(1, 128, 2); break;
-        default: rc = two ? SCKV_ATTN2(1, 2, 128, 4) : SCKV_ATTN(1, 128, 4); break;
+        case 64: rc = SCKV_ATTN(64); break;
+        case 128: rc = SCKV_ATTN(128); break;
+        case 256: rc = SCKV_ATTN(256); break;
+        default: rc = SCKV_ATTN(512); break;
     }
 #undef SCKV_ATTN
-#undef SCKV_ATTN2
     if (rc || nsplit == 1) return rc;
     if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: too many queries");
     combine_kernel<<<dim3((unsigned)nq, (unsigned)H), dim3(COMBINE_THREADS), 0, s>>>(part_o, part_ml, sink, nsplit, H,

@@ -166,9 +166,13 @@ struct ScoreShape {
     static constexpr int QS = DI * 2;                  // bytes per q row in LDS (raw, then q_hat in place)
     static constexpr int OFF_Q = SCORE_WAVES * NST * TILE;
     static constexpr int OFF_W = OFF_Q + HP * QS;      // 64 f32 head weights
-    static constexpr int OFF_KEYS = OFF_W + 64 * 4;
+    // keys (then scores) reuse the q / w space once q_hat and the weights sit
+    // in registers
+    static constexpr int OFF_KEYS = OFF_Q;
     static constexpr size_t lds_bytes(int rows_per_wg, bool with_scores) {
-        return (size_t)OFF_KEYS + (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
+        const size_t qw = (size_t)HP * QS + 64 * 4;
+        const size_t ks = (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
+        return (size_t)OFF_Q + (qw > ks ? qw : ks);
     }
     static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 3, "copy counts");
 };
@@ -187,7 +191,7 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 // Ring depth of the fused kernel: the keys of a whole query share the LDS
 // with the ring (KPT keys per thread, 256 threads).
 constexpr int fused_ring_depth(int DI, int KPT) {
-    return (64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : (KPT >= 32 ? 3 : 4));
+    return (64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4);
 }
 
 // KPT == 0: scores of a row range, ordered keys flushed to `keys` for the
@@ -321,6 +325,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
             const int h = mt * 32 + d_row(i, lane);
             wd[mt][i] = (h < Hi) ? w_l[h] : 0.0f;
         }
+    __syncthreads();  // every wave holds q_hat and w before keys overwrite them
 
 
     for (int tile = 0; tile < ntiles; ++tile) {

@@ -16,9 +16,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x32_bf16 (one wave, D[16x16] += A[16x32] * B[32x16]), lane l:
+//   A: row l%16, k = (l/16)*8 + 0..7      B: column l%16, k = (l/16)*8 + 0..7
+//   D: 4 f32, element i at row (l/16)*4 + i, column l%16
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -69,15 +77,19 @@ __device__ __forceinline__ void dma16(const void* gaddr, uint32_t lds_byte) {
 
 // Same copy with a uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset (the saddr form): no 64-bit address arithmetic per lane.
+// lds_byte must be wave-uniform; it is read from the first lane so that it
+// always sits in a scalar register.
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_byte)
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lb)
                  : "memory", "m0");
 }
 
 // 4-byte-per-lane form (global_load_lds_dword): lane i's 4 bytes land at
 // LDS byte lds_byte + 4 * i.
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_byte) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lds_byte)
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_byte);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "s"(lb)
                  : "memory", "m0");
 }
 
