@@ -48,7 +48,8 @@ enum sckv_quant_mode {
 /* Operations whose workspace size sckv_workspace_bytes() reports. */
 enum sckv_op {
     SCKV_OP_INDEX_SCORES_TOPK = 0,
-    SCKV_OP_SPARSE_ATTN_SINK = 1
+    SCKV_OP_SPARSE_ATTN_SINK = 1,
+    SCKV_OP_INDEX_SCORES_TOPK_FP4 = 2
 };
 
 /*
@@ -77,6 +78,26 @@ int sckv_quant(const void* x, void* y, int64_t n, int mode, void* stream);
  */
 int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols, int mode,
                     void* stream);
+
+/*
+ * sckv_quant_pack -- the same round trip as sckv_quant_rows, stored packed:
+ * each value as its 4-bit e2m1 code (bits 0-2 the index into
+ * {0, .5, 1, 1.5, 2, 3, 4, 6}, bit 3 the sign, so small negative values give
+ * code 8, i.e. -0) and each block's scale as one byte: the E8M0 exponent e of
+ * s = 2^(e - 127) (SCKV_FP4_E8M0_B32) or the E4M3FN code of s
+ * (SCKV_FP4_E4M3_B16).  Codes of elements 2j and 2j+1 of a row share byte j,
+ * 2j in the low nibble.  code value * scale is exactly the bf16 value
+ * sckv_quant_rows would produce.  The packing is this library's storage of the
+ * pages' round trip (the pages keep the values in bf16): 68 bytes instead of
+ * 256 for a 128-wide indexer k row, 288 instead of 1024 for a 512-wide
+ * latent row.
+ *   x       [rows, cols] bf16, row stride ldx (elements)
+ *   codes   [rows, cols/2] bytes, row stride ldc (bytes)
+ *   scales  [rows, cols/block] bytes, row stride lds (bytes)
+ * cols must be a multiple of the block; the three regions must not overlap.
+ */
+int sckv_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
+                    int64_t cols, int mode, void* stream);
 
 /*
  * sckv_ring_write -- write this step's m kv rows into the window ring: the row
@@ -161,6 +182,24 @@ int sckv_index_scores_topk(const void* q, const void* k, const float* w, int B, 
                            int64_t ld, int64_t col0, void* scores, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sckv_index_scores_topk_fp4 -- sckv_index_scores_topk with the k cache
+ * stored packed (sckv_quant_pack, SCKV_FP4_E8M0_B32): the same scores, bit for
+ * bit, and the same top-K lists.  q is still the raw bf16 q; its round trip
+ * is packed into the workspace and both operands go through the gfx950 scaled
+ * fp4 matrix cores (e2m1 x e2m1 with one E8M0 scale per 32 values, exact
+ * products; the exactness note above applies unchanged).
+ *   k_codes   [B, n_c, Di/2] bytes, contiguous, 16-byte aligned
+ *   k_scales  [B, n_c, Di/32] bytes, contiguous, 4-byte aligned
+ *   ws        at least sckv_workspace_bytes(SCKV_OP_INDEX_SCORES_TOPK_FP4,
+ *             B, m, Hi, Di, n_c)
+ * Supported: as sckv_index_scores_topk, with Di in {128, 256}.
+ */
+int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, const void* k_scales, const float* w, int B,
+                               int64_t m, int Hi, int Di, int64_t n_c, int ratio, int64_t start_pos, int K,
+                               int32_t offset, int32_t* idx, int64_t ld, int64_t col0, void* scores, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/*
  * sckv_sparse_attn_sink -- sparse MQA attention over the rows named by each
  * query's index list, with a per-head sink logit (compress.rs attention_any:
  * the sparse_attn call with scale = head_dim^-1/2, the kv rows being the
@@ -185,8 +224,9 @@ int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const v
 
 /*
  * sckv_workspace_bytes -- device workspace an operation needs for the given
- * shape: op = SCKV_OP_INDEX_SCORES_TOPK with (H, D, n) = (Hi, Di, n_c), or
- * SCKV_OP_SPARSE_ATTN_SINK with (H, D, n) = (H, D, T).  0 means none needed.
+ * shape: op = SCKV_OP_INDEX_SCORES_TOPK or SCKV_OP_INDEX_SCORES_TOPK_FP4 with
+ * (H, D, n) = (Hi, Di, n_c), or SCKV_OP_SPARSE_ATTN_SINK with (H, D, n) =
+ * (H, D, T).  0 means none needed.
  * Returns (size_t)-1 for invalid arguments.
  */
 size_t sckv_workspace_bytes(int op, int B, int64_t m, int H, int D, int64_t n);

@@ -24,6 +24,7 @@ _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 _i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 
@@ -54,6 +55,10 @@ def lib():
     L.sckvo_quant_e8m0.restype = None
     L.sckvo_quant_e4m3.argtypes = [_u16p, _u16p, _i64, _i64]
     L.sckvo_quant_e4m3.restype = None
+    L.sckvo_pack_fp4.argtypes = [_u16p, _i64, _i64, _int, _u8p, _u8p]
+    L.sckvo_pack_fp4.restype = None
+    L.sckvo_unpack_fp4.argtypes = [_u8p, _u8p, _i64, _i64, _int, _u16p]
+    L.sckvo_unpack_fp4.restype = None
     L.sckvo_ring_write.argtypes = [_u16p, _int, _int, _u16p, _i64, _i64]
     L.sckvo_ring_write.restype = None
     L.sckvo_rows_a_len.argtypes = [_int, _i64, _i64]
@@ -127,6 +132,29 @@ def quant(x_bits, mode: str, block: int | None = None):
     else:
         raise ValueError(mode)
     return y.reshape(np.shape(x_bits))
+
+
+def pack(x_bits, mode: str):
+    """Packed storage of the round trip of a flat bf16 array: (codes uint8
+    [n/2], two 4-bit e2m1 codes a byte, the even element in the low nibble;
+    scales uint8 [n/block], E8M0 exponents or E4M3 codes)."""
+    x = _u16(x_bits).reshape(-1)
+    block, m = (32, 1) if mode == E8M0_B32 else (16, 0)
+    if x.size % block:
+        raise ValueError("size is not a multiple of the block")
+    codes = np.zeros(x.size // 2, dtype=np.uint8)
+    scales = np.zeros(x.size // block, dtype=np.uint8)
+    lib().sckvo_pack_fp4(x, x.size, block, m, codes, scales)
+    return codes, scales
+
+
+def unpack(codes, scales, n: int, mode: str):
+    """bf16 bits of the values packed codes and scales stand for."""
+    block, m = (32, 1) if mode == E8M0_B32 else (16, 0)
+    y = np.empty(n, dtype=np.uint16)
+    lib().sckvo_unpack_fp4(np.ascontiguousarray(codes, dtype=np.uint8).reshape(-1),
+                           np.ascontiguousarray(scales, dtype=np.uint8).reshape(-1), n, block, m, y)
+    return y
 
 
 # --- window ring, window rows, visibility (forward.rs ring copies) ---------

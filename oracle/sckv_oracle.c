@@ -199,6 +199,69 @@ void sckvo_quant_e4m3(const uint16_t* x, uint16_t* y, int64_t n, int64_t block) 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Packed storage of the round trip (not on the pages: the e2m1 values and  */
+/* their block scales in 4-bit codes and one scale byte per block)           */
+/* ------------------------------------------------------------------------ */
+
+/* Storage format (a reading; the pages keep the round-tripped values in
+ * bf16): value i of a block is the 4-bit e2m1 code (bit 3 the sign, bits 0-2
+ * the index into {0, .5, 1, 1.5, 2, 3, 4, 6}); codes 2j and 2j+1 of the flat
+ * array share byte j, 2j in the low nibble.  One scale byte per block: the
+ * E8M0 exponent e (scale 2^(e - 127)) for power-of-two scales, the E4M3FN
+ * code of the scale otherwise.  A value and its code give the same number, so
+ * unpacking returns exactly the round trip. */
+static const float oracle_grid[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+static int oracle_e2m1_code(float r) {
+    float a = fabsf(r);
+    int idx = -1;
+    for (int i = 0; i < 8; ++i)
+        if (oracle_grid[i] == a) idx = i;
+    if (idx < 0) abort(); /* r is always a grid value here */
+    return idx | (signbit(r) ? 8 : 0);
+}
+
+/* mode 1: power-of-two scales (E8M0), mode 0: e4m3 scales; n a multiple of block. */
+void sckvo_pack_fp4(const uint16_t* x, int64_t n, int64_t block, int mode, uint8_t* codes, uint8_t* scales) {
+    const float floor_amax = mode ? 6.0f * ldexpf(1.0f, -126) : 6.0f * ldexpf(1.0f, -9);
+    memset(codes, 0, (size_t)(n / 2));
+    for (int64_t b0 = 0; b0 < n; b0 += block) {
+        float amax = oracle_block_amax(x + b0, block);
+        if (amax < floor_amax) amax = floor_amax;
+        float s;
+        if (mode) {
+            s = sckvo_pow2_ceil(amax / 6.0f);
+            int e;
+            frexpf(s, &e); /* s = 0.5 * 2^e exactly */
+            scales[b0 / block] = (uint8_t)(e - 1 + 127);
+        } else {
+            uint8_t c = sckvo_f32_to_e4m3(amax / 6.0f);
+            s = sckvo_e4m3_to_f32(c);
+            scales[b0 / block] = c;
+        }
+        for (int64_t i = 0; i < block; ++i) {
+            float y = sckvo_bf16_to_f32(x[b0 + i]) / s;
+            if (y > 6.0f) y = 6.0f;
+            if (y < -6.0f) y = -6.0f;
+            int code = oracle_e2m1_code(sckvo_e2m1_rne(y));
+            int64_t k = b0 + i;
+            codes[k / 2] |= (uint8_t)(code << ((k & 1) ? 4 : 0));
+        }
+    }
+}
+
+/* The bf16 values that packed codes and scales stand for. */
+void sckvo_unpack_fp4(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t block, int mode, uint16_t* y) {
+    for (int64_t k = 0; k < n; ++k) {
+        int code = (codes[k / 2] >> ((k & 1) ? 4 : 0)) & 15;
+        uint8_t sb = scales[k / block];
+        double s = mode ? ldexp(1.0, (int)sb - 127) : (double)sckvo_e4m3_to_f32(sb);
+        double v = (double)oracle_grid[code & 7] * s;
+        y[k] = sckvo_f32_to_bf16((float)((code & 8) ? -v : v));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Window ring, window rows, visibility  [forward.rs: ring copies, offset,   */
 /* compress_len; compress.rs: attention_any]                                 */
 /* ------------------------------------------------------------------------ */

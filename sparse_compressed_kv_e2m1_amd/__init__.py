@@ -15,14 +15,17 @@ from ._binding import (  # noqa: F401
     SCKV_FP4_E8M0_B32,
     SCKV_OK,
     SCKV_OP_INDEX_SCORES_TOPK,
+    SCKV_OP_INDEX_SCORES_TOPK_FP4,
     SCKV_OP_SPARSE_ATTN_SINK,
     LIB_PATH,
     SckvError,
     lib,
     sckv_abi_version,
     sckv_index_scores_topk,
+    sckv_index_scores_topk_fp4,
     sckv_last_error,
     sckv_quant,
+    sckv_quant_pack,
     sckv_quant_rows,
     sckv_ring_write,
     sckv_rows_a_len,

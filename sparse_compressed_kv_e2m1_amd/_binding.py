@@ -26,6 +26,7 @@ SCKV_FP4_E8M0_B32 = 1
 
 SCKV_OP_INDEX_SCORES_TOPK = 0
 SCKV_OP_SPARSE_ATTN_SINK = 1
+SCKV_OP_INDEX_SCORES_TOPK_FP4 = 2
 
 
 class SckvError(RuntimeError):
@@ -41,6 +42,7 @@ def _load():
     vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.sckv_quant.argtypes = [vp, vp, i64, i32, vp]
     L.sckv_quant_rows.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]
+    L.sckv_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, vp]
     L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
     L.sckv_rows_a_len.argtypes = [i32, i64, i64]
     L.sckv_rows_a_len.restype = i64
@@ -48,6 +50,8 @@ def _load():
     L.sckv_visible_idx.argtypes = [i32, i64, i64, i32, i64, i32, ctypes.c_int32, vp, i64, i64, vp]
     L.sckv_index_scores_topk.argtypes = [vp, vp, vp, i32, i64, i32, i32, i64, i32, i64, i32, ctypes.c_int32, vp,
                                          i64, i64, vp, vp, sz, vp]
+    L.sckv_index_scores_topk_fp4.argtypes = [vp, vp, vp, vp, i32, i64, i32, i32, i64, i32, i64, i32, ctypes.c_int32,
+                                             vp, i64, i64, vp, vp, sz, vp]
     L.sckv_sparse_attn_sink.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32, vp,
                                         vp, sz, vp]
     L.sckv_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i64]
@@ -55,8 +59,9 @@ def _load():
     L.sckv_last_error.argtypes = []
     L.sckv_last_error.restype = ctypes.c_char_p
     L.sckv_abi_version.argtypes = []
-    for name in ("sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_window_idx", "sckv_visible_idx",
-                 "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_abi_version"):
+    for name in ("sckv_quant", "sckv_quant_rows", "sckv_quant_pack", "sckv_ring_write", "sckv_window_idx",
+                 "sckv_visible_idx", "sckv_index_scores_topk", "sckv_index_scores_topk_fp4", "sckv_sparse_attn_sink",
+                 "sckv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
     return L
 
@@ -124,6 +129,19 @@ def sckv_quant_rows(x: torch.Tensor, ldx: int, y: torch.Tensor, ldy: int, rows: 
                                                   _stream(stream)))
 
 
+def sckv_quant_pack(x: torch.Tensor, ldx: int, codes: torch.Tensor, ldc: int, scales: torch.Tensor, lds: int,
+                    rows: int, cols: int, mode: int, stream=None):
+    """x: bf16 device tensor; codes / scales: uint8 device tensors (row strides
+    ldx in elements, ldc / lds in bytes)."""
+    if not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x: expected a bf16 device tensor")
+    for t, n in ((codes, "codes"), (scales, "scales")):
+        if not t.is_cuda or t.dtype != torch.uint8:
+            raise ValueError(f"{n}: expected a uint8 device tensor")
+    _check("sckv_quant_pack", lib.sckv_quant_pack(x.data_ptr(), ldx, codes.data_ptr(), ldc, scales.data_ptr(), lds,
+                                                  rows, cols, mode, _stream(stream)))
+
+
 def sckv_ring_write(rows: torch.Tensor, rows_bstride: int, ring: torch.Tensor, ring_bstride: int, B: int, m: int,
                     start_pos: int, win: int, D: int, stream=None):
     for t, n in ((rows, "rows"), (ring, "ring")):
@@ -158,6 +176,19 @@ def sckv_index_scores_topk(q: torch.Tensor, k: torch.Tensor, w: torch.Tensor, B:
         _ptr(q, torch.bfloat16, "q"), _ptr(k, torch.bfloat16, "k"), _ptr(w, torch.float32, "w"), B, m, Hi, Di, n_c,
         ratio, start_pos, K, offset, _ptr(idx, torch.int32, "idx"), ld, col0, _ptr(scores, torch.bfloat16, "scores"),
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sckv_index_scores_topk_fp4(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, w: torch.Tensor, B: int,
+                               m: int, Hi: int, Di: int, n_c: int, ratio: int, start_pos: int, K: int, offset: int,
+                               idx: torch.Tensor, ld: int, col0: int, scores: torch.Tensor | None = None,
+                               ws: torch.Tensor | None = None, stream=None):
+    if ws is None:
+        ws = workspace(SCKV_OP_INDEX_SCORES_TOPK_FP4, B, m, Hi, Di, n_c, device=idx.device)
+    _check("sckv_index_scores_topk_fp4", lib.sckv_index_scores_topk_fp4(
+        _ptr(q, torch.bfloat16, "q"), _ptr(k_codes, torch.uint8, "k_codes"), _ptr(k_scales, torch.uint8, "k_scales"),
+        _ptr(w, torch.float32, "w"), B, m, Hi, Di, n_c, ratio, start_pos, K, offset, _ptr(idx, torch.int32, "idx"),
+        ld, col0, _ptr(scores, torch.bfloat16, "scores"), _ptr(ws, None, "ws"), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def sckv_sparse_attn_sink(q: torch.Tensor, rows_a: torch.Tensor, ra: int, rows_b: torch.Tensor | None, rb: int,

@@ -151,58 +151,83 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[KPT], int64_t 
 }
 
 // Shape of one score workgroup for MT head tiles and head dim DI; NST_ > 0
-// sets the ring depth (tiles per wave) instead of the default.
-template <int MT, int DI, int NST_ = 0>
+// sets the ring depth (tiles per wave) instead of the default.  FP4: the k
+// rows come packed (4-bit e2m1 codes, one E8M0 byte per 32 values) and the
+// contraction runs on the scaled fp4 matrix cores.
+template <int MT, int DI, int NST_ = 0, bool FP4 = false>
 struct ScoreShape {
     static constexpr int HP = MT * 32;                 // padded heads
-    static constexpr int KS = DI / 16;                 // k-steps
-    static constexpr int ROWB = DI * 2;                // bytes per k row
-    static constexpr int TILE = 32 * ROWB;             // bytes per 32-row tile
-    static constexpr int NINST = TILE / 1024;          // 16-byte-per-lane copies per tile
-    static constexpr int NST = NST_ > 0 ? NST_ : ((TILE >= 16384) ? 1 : 4);  // tiles per wave in the ring
-    static constexpr int PD = NST - 1;                   // tiles requested ahead of the one used
+    static constexpr int KS = FP4 ? DI / 64 : DI / 16; // k-steps (64 fp4 or 16 bf16 values each)
+    static constexpr int ROWB = FP4 ? DI / 2 : DI * 2; // bytes per k row (codes only for FP4)
+    static constexpr int SB = FP4 ? DI / 32 : 0;       // scale bytes per k row
+    static constexpr int CT = 32 * ROWB;               // bytes of a 32-row tile's rows
+    static constexpr int TILE = CT + 32 * SB;          // ... plus its scale bytes
+    static constexpr int NINST = CT / 1024 + (FP4 ? 1 : 0);  // copies per tile (the last one: scales)
+    static constexpr int NST = NST_ > 0 ? NST_ : (FP4 ? 8 : ((TILE >= 16384) ? 1 : 4));  // tiles per wave in the ring
+    static constexpr int PD = NST - 1;                 // tiles requested ahead of the one used
     static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
-    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // chunk swizzle mask
-    static constexpr int QS = DI * 2;                  // bytes per q row in LDS (raw, then q_hat in place)
+    static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // bf16 chunk swizzle mask
+    static constexpr int RPS = 16 / (CPR < 16 ? CPR : 16);  // fp4: rows sharing one swizzle value
+    static constexpr int QS = FP4 ? DI / 2 : DI * 2;   // bytes per q row in LDS (fp4: codes)
     static constexpr int OFF_Q = SCORE_WAVES * NST * TILE;
-    static constexpr int OFF_W = OFF_Q + HP * QS;      // 64 f32 head weights
+    static constexpr int OFF_QS = OFF_Q + HP * QS;     // fp4: q scale bytes [HP][SB]
+    static constexpr int OFF_W = OFF_QS + HP * SB;     // 64 f32 head weights
     // keys (then scores) reuse the q / w space once q_hat and the weights sit
     // in registers
     static constexpr int OFF_KEYS = OFF_Q;
     static constexpr size_t lds_bytes(int rows_per_wg, bool with_scores) {
-        const size_t qw = (size_t)HP * QS + 64 * 4;
+        const size_t qw = (size_t)HP * QS + (size_t)HP * SB + 64 * 4;
         const size_t ks = (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
         return (size_t)OFF_Q + (qw > ks ? qw : ks);
     }
-    static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 3, "copy counts");
+    static_assert(NINST >= 1 && NINST * PD < 64 && PD <= 7 && (TILE % 16) == 0, "copy counts");
 };
 
-template <int NINST, int NAHEAD>
+// Wait until at most `ahead` later tiles (NINST copies each) of this wave
+// may still be in flight (0 <= ahead <= PDMAX - 1).
+template <int NINST, int PDMAX>
 __device__ __forceinline__ void wait_tiles(int ahead) {
-    // at most `ahead` later tiles (NINST copies each) may still be in flight
-    if (ahead <= 0)
-        wait_vmcnt<0>();
-    else if (ahead == 1 || NAHEAD < 2)
-        wait_vmcnt<NINST>();
-    else
-        wait_vmcnt<(2 * NINST < 64 ? 2 * NINST : 63)>();
+    switch (ahead < PDMAX - 1 ? ahead : PDMAX - 1) {
+        case 6: wait_vmcnt<(6 * NINST < 64 ? 6 * NINST : 63)>(); break;
+        case 5: wait_vmcnt<(5 * NINST < 64 ? 5 * NINST : 63)>(); break;
+        case 4: wait_vmcnt<(4 * NINST < 64 ? 4 * NINST : 63)>(); break;
+        case 3: wait_vmcnt<(3 * NINST < 64 ? 3 * NINST : 63)>(); break;
+        case 2: wait_vmcnt<(2 * NINST < 64 ? 2 * NINST : 63)>(); break;
+        case 1: wait_vmcnt<NINST>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
 }
 
 // Ring depth of the fused kernel: the keys of a whole query share the LDS
 // with the ring (KPT keys per thread, 256 threads).
-constexpr int fused_ring_depth(int DI, int KPT) {
-    return (64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4);
+constexpr int fused_ring_depth(int DI, int KPT, bool FP4) {
+    return FP4 ? (KPT >= 128 ? 6 : 8) : ((64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4));
+}
+
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e2m1 (format 4): lane l
+// holds, for row l%32, the 32 codes of k-block l/32 (16 bytes, in the low four
+// registers) and that block's E8M0 scale in the low byte of its scale word.
+// Within a block any order of the codes works as long as A and B agree.
+__device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x16 c) {
+    typedef int i32x8 __attribute__((ext_vector_type(8)));
+    const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+    const i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, 0, (int)sa, 0, (int)sb);
 }
 
 // KPT == 0: scores of a row range, ordered keys flushed to `keys` for the
 // top-k kernel.  KPT > 0 (fused, one workgroup per query, no split): the
 // whole query's keys stay in LDS and the workgroup selects its top-K itself.
-template <int MT, int DI, int KPT>
+// FP4: k arrives as codes [n_c][DI/2] and scale bytes [n_c][DI/32], and q as
+// the already round-tripped, packed q_hat (codes [Hi][DI/2], scales
+// [Hi][DI/32] per query); otherwise k is bf16 [n_c][DI] and q the raw bf16 q.
+template <int MT, int DI, int KPT, bool FP4>
 __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const float* __restrict__ w, int64_t m, int Hi,
-    int64_t n_c, int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys,
-    uint16_t* __restrict__ scores, int K, int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0) {
-    using S = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT)>;
+    const void* __restrict__ q, const void* __restrict__ q_scales, const void* __restrict__ k,
+    const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
+    int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
+    int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0) {
+    using S = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4), FP4>;
     constexpr int KS = S::KS;
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* qh_l = lds + S::OFF_Q;
@@ -234,39 +259,59 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     row_end = row_end < vis ? row_end : vis;
 
     // ---- this wave's rows: a contiguous run, streamed in 32-row tiles through
-    // a wave-private ring; lane i of copy j brings 16 bytes of tile byte j*1024 +
-    // 16 i, taken from chunk (chunk ^ (row & SWZ)) of its row so that the B-operand
-    // reads below (32 rows at one chunk) spread over all banks.
+    // a wave-private ring.  Lane i of copy j brings 16 bytes to tile byte
+    // j*1024 + 16 i; which 16-byte chunk of which row lands there is swizzled
+    // so that the B-operand reads below (32 rows at one chunk) spread over all
+    // banks.  FP4: the tile's scale bytes follow its codes.
     const int64_t nrows = row_end - row0;
     const int64_t per_wave = (((nrows + SCORE_WAVES - 1) / SCORE_WAVES) + 31) / 32 * 32;
     const int64_t w0 = row0 + (int64_t)wave * per_wave;
     int64_t w1 = w0 + per_wave;
     w1 = w1 < row_end ? w1 : row_end;
     const int ntiles = (w0 < w1) ? (int)((w1 - w0 + 31) / 32) : 0;
-    const uint16_t* kb = k + b * n_c * DI;
+    const unsigned char* kb = reinterpret_cast<const unsigned char*>(k) + b * n_c * S::ROWB;
+    const uint8_t* ksb = FP4 ? k_scales + b * n_c * S::SB : nullptr;
     const uint32_t ring = lds0 + (uint32_t)(wave * S::NST * S::TILE);
     auto issue = [&](int tile) {
         const int64_t s0 = w0 + (int64_t)tile * 32;
         const uint32_t st = ring + (uint32_t)((tile % S::NST) * S::TILE);
 #pragma unroll
-        for (int j = 0; j < S::NINST; ++j) {
-            const int byte = j * 1024 + lane * 16;
-            const int r = byte / S::ROWB;
-            const int ch = (byte % S::ROWB) / 16;
+        for (int j = 0; j < S::CT / 1024; ++j) {
+            const int slot = j * 64 + lane;  // 16-byte slot of the tile
+            const int r = slot / S::CPR;
+            const int cp = slot % S::CPR;
+            const int ch = FP4 ? (cp ^ ((r / S::RPS) % S::CPR)) : (cp ^ (r & S::SWZ));
             int64_t row = s0 + r;
             row = row < n_c ? row : n_c - 1;  // tail rows re-read a real row; their results are dropped
-            const uint32_t off = (uint32_t)(row * S::ROWB + ((ch ^ (r & S::SWZ)) * 16));
-            dma16_s(kb, off, st + (uint32_t)(j * 1024));
+            dma16_s(kb, (uint32_t)(row * S::ROWB + ch * 16), st + (uint32_t)(j * 1024));
+        }
+        if (FP4) {
+            // scale bytes of the tile's 32 rows, 4 bytes a lane (SB = 2: 2 rows a lane)
+            const int per = S::SB >= 4 ? S::SB / 4 : 1;      // lanes per row
+            const int rpl = S::SB >= 4 ? 1 : 4 / S::SB;      // rows per lane
+            const int nl = 32 * per / rpl;
+            if (lane < nl) {
+                int64_t row = s0 + (lane / per) * rpl;
+                const int64_t last = n_c - rpl;  // keep the 4-byte read inside the array
+                row = row < last ? row : (last > 0 ? last : 0);
+                dma4_s(ksb, (uint32_t)(row * S::SB + (lane % per) * 4), st + (uint32_t)(S::CT));
+            }
         }
     };
-    // ---- prologue.  The raw q rows and the head weights come in by asynchronous
-    // copies, this wave's first k tiles are requested right behind them, and the
-    // q round trip runs while those tiles are in flight.  No ordinary global
-    // load is issued in this kernel, so every vmcnt wait below is explicit.
-    const int qbytes = Hi * DI * 2;
-    const uint16_t* qrow = q + qi * (int64_t)Hi * DI;
+    // ---- prologue.  q and the head weights come in by asynchronous copies, this
+    // wave's first k tiles are requested right behind them.  No ordinary
+    // global load is issued in this kernel, so every vmcnt wait is explicit.
+    const int qbytes = Hi * S::QS;
+    const unsigned char* qrow = reinterpret_cast<const unsigned char*>(q) + qi * (int64_t)qbytes;
     for (int j = wave; j * 1024 < qbytes; j += SCORE_WAVES)
         if (j * 1024 + lane * 16 < qbytes) dma16_s(qrow, (uint32_t)(j * 1024 + lane * 16), lds0 + S::OFF_Q + j * 1024);
+    if (FP4 && wave == 1) {
+        // Hi * SB scale bytes (a multiple of 4, at most 512), 256 bytes a copy
+        const uint8_t* qs = reinterpret_cast<const uint8_t*>(q_scales) + qi * (int64_t)(Hi * S::SB);
+        for (int j = 0; j * 256 < Hi * S::SB; ++j)
+            if (j * 256 + lane * 4 < Hi * S::SB)
+                dma4_s(qs, (uint32_t)(j * 256 + lane * 4), lds0 + S::OFF_QS + (uint32_t)(j * 256));
+    }
     if (wave == 0 && lane < Hi) dma4_s(w + qi * (int64_t)Hi, (uint32_t)lane * 4u, lds0 + S::OFF_W);
 #pragma unroll
     for (int i = 0; i < S::PD; ++i)
@@ -277,44 +322,62 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     else
         wait_vmcnt<0>();
     __syncthreads();
-    // q_hat = E8M0_B32 round trip of q, one 32-value block per thread and step,
-    // in place; padded heads (h >= Hi) become zero rows
-    for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += SCORE_WAVES * 64) {
-        const int h = blk / (DI / 32);
-        const int c = blk - h * (DI / 32);
-        u32x4* qb = reinterpret_cast<u32x4*>(qh_l + h * S::QS + c * 64);
-        u32x4 raw[4];
+
+    // ---- q_hat in A layout: head mt*32 + lane%32
+    bf16x8 qa[FP4 ? 1 : MT][FP4 ? 1 : KS];
+    u32x4 qc[FP4 ? MT : 1][FP4 ? KS : 1];     // fp4 codes of k-block 2*ks + lane/32
+    uint32_t qsc[FP4 ? MT : 1][FP4 ? KS : 1];  // and their E8M0 scale
+    if constexpr (!FP4) {
+        // q_hat = E8M0_B32 round trip of the raw q, one 32-value block per thread
+        // and step, in place; padded heads (h >= Hi) become zero rows
+        for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += SCORE_WAVES * 64) {
+            const int h = blk / (DI / 32);
+            const int c = blk - h * (DI / 32);
+            u32x4* qb = reinterpret_cast<u32x4*>(qh_l + h * S::QS + c * 64);
+            u32x4 raw[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = (h < Hi) ? qb[i] : u32x4{0, 0, 0, 0};
-        float amax = 0.0f;
+            for (int i = 0; i < 4; ++i) raw[i] = (h < Hi) ? qb[i] : u32x4{0, 0, 0, 0};
+            float amax = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] & 0xffffu)));
-                amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] >> 16)));
+                for (int e = 0; e < 4; ++e) {
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] & 0xffffu)));
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] >> 16)));
+                }
+            const float sc = block_scale<SCKV_FP4_E8M0_B32>(amax);
+            const float inv_s = pow2_reciprocal(sc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t v = raw[i][e];
+                    raw[i][e] = fp4_value_bits_pow2(bf16_bits_to_f32(v & 0xffffu), sc, inv_s) |
+                                (fp4_value_bits_pow2(bf16_bits_to_f32(v >> 16), sc, inv_s) << 16);
+                }
+                qb[i] = raw[i];
             }
-        const float sc = block_scale<SCKV_FP4_E8M0_B32>(amax);
-        const float inv_s = pow2_reciprocal(sc);
+        }
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t v = raw[i][e];
-                raw[i][e] = fp4_value_bits_pow2(bf16_bits_to_f32(v & 0xffffu), sc, inv_s) |
-                            (fp4_value_bits_pow2(bf16_bits_to_f32(v >> 16), sc, inv_s) << 16);
+            for (int ks = 0; ks < KS; ++ks)
+                qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + (lane & 31)) * S::QS +
+                                                              (ks * 16 + (lane >> 5) * 8) * 2);
+    } else {
+        const uint8_t* qs_l = lds + S::OFF_QS;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const int h = mt * 32 + (lane & 31);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int blk = 2 * ks + (lane >> 5);
+                qc[mt][ks] = (h < Hi) ? *reinterpret_cast<const u32x4*>(qh_l + h * S::QS + blk * 16) : u32x4{0, 0, 0, 0};
+                qsc[mt][ks] = (h < Hi) ? (uint32_t)qs_l[h * S::SB + blk] : 127u;
             }
-            qb[i] = raw[i];
         }
     }
-    __syncthreads();
-    bf16x8 qa[MT][KS];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + (lane & 31)) * S::QS +
-                                                          (ks * 16 + (lane >> 5) * 8) * 2);
     // head weights in D layout: head mt*32 + d_row(i, lane)
     const float* w_l = reinterpret_cast<const float*>(lds + S::OFF_W);
     float wd[MT][16];
@@ -327,24 +390,35 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
         }
     __syncthreads();  // every wave holds q_hat and w before keys overwrite them
 
-
     for (int tile = 0; tile < ntiles; ++tile) {
         if (S::PD == 0) issue(tile);
         // tiles tile+1 .. tile+PD-1 may still be in flight; tile itself must be done
         const int ahead = (ntiles - 1 - tile) < (S::PD - 1) ? (ntiles - 1 - tile) : (S::PD - 1);
-        wait_tiles<S::NINST, S::PD - 1>(ahead);
+        wait_tiles<S::NINST, (S::PD > 1 ? S::PD : 1)>(ahead);
         if (S::PD > 0 && tile + S::PD < ntiles) issue(tile + S::PD);  // into the stage tile-1 used
         const unsigned char* stp = lds + (wave * S::NST + tile % S::NST) * S::TILE;
         const int r = lane & 31;
         f32x16 acc[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt] = zero16();
+        if constexpr (!FP4) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int ch = ks * 2 + (lane >> 5);
-            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(stp + r * S::ROWB + ((ch ^ (r & S::SWZ)) * 16));
+            for (int ks = 0; ks < KS; ++ks) {
+                const int ch = ks * 2 + (lane >> 5);
+                const bf16x8 kr = *reinterpret_cast<const bf16x8*>(stp + r * S::ROWB + ((ch ^ (r & S::SWZ)) * 16));
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16(qa[mt][ks], kr, acc[mt]);
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma32x32x16(qa[mt][ks], kr, acc[mt]);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int blk = 2 * ks + (lane >> 5);
+                const int cp = blk ^ ((r / S::RPS) % S::CPR);
+                const u32x4 kc = *reinterpret_cast<const u32x4*>(stp + (r * S::CPR + cp) * 16);
+                const uint32_t ksc = stp[S::CT + r * S::SB + blk];
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_fp4(qc[mt][ks], qsc[mt][ks], kc, ksc, acc[mt]);
+            }
         }
         // r_h = fl32(w_h * relu(d_h)); relu maps every d <= 0 (and -0) to +0
         float v[MT * 16];
@@ -478,41 +552,57 @@ void launch_topk(const uint16_t* keys, int64_t nq, int64_t n_c, int64_t m, int r
 }
 
 // LDS bytes of a score launch (KPT as in index_score_kernel).
-template <int MT, int DI, int KPT>
+template <int MT, int DI, int KPT, bool FP4>
 size_t score_lds_bytes(int rows_per_wg, bool with_scores) {
-    using Sh = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT)>;
+    using Sh = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4), FP4>;
     return Sh::lds_bytes(rows_per_wg, with_scores);
 }
 
-template <int MT, int DI, int KPT>
-int launch_scores(const uint16_t* q, const uint16_t* k, const float* w, int64_t nq, int64_t m, int Hi, int64_t n_c,
-                  int ratio, int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* keys, uint16_t* scores, int K,
-                  int32_t offset, int32_t* idx, int64_t ld, int64_t col0, hipStream_t stream) {
-    const size_t lds = score_lds_bytes<MT, DI, KPT>(rows_per_wg, scores != nullptr);
+// Operands of one indexer call: q (raw bf16, or packed q_hat codes with
+// q_scales), k (bf16 rows, or codes with k_scales).
+struct IndexArgs {
+    const void* q;
+    const void* q_scales;
+    const void* k;
+    const uint8_t* k_scales;
+    const float* w;
+    int64_t nq, m;
+    int Hi;
+    int64_t n_c;
+    int ratio;
+    int64_t start_pos;
+    int K;
+    int32_t offset;
+    int32_t* idx;
+    int64_t ld, col0;
+    uint16_t* scores;
+    hipStream_t s;
+};
+
+template <int MT, int DI, int KPT, bool FP4>
+int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* keys) {
+    const size_t lds = score_lds_bytes<MT, DI, KPT, FP4>(rows_per_wg, a.scores != nullptr);
     if (lds > 160 * 1024) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: score tile does not fit in LDS");
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI, KPT>,
+        hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI, KPT, FP4>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_index_scores_topk: ") + hipGetErrorString(e));
     }
-    index_score_kernel<MT, DI, KPT><<<dim3((unsigned)(nq * nsplit)), dim3(SCORE_WAVES * 64), lds, stream>>>(
-        q, k, w, m, Hi, n_c, ratio, start_pos, rows_per_wg, nsplit, keys, scores, K, offset, idx, ld, col0);
+    index_score_kernel<MT, DI, KPT, FP4><<<dim3((unsigned)(a.nq * nsplit)), dim3(SCORE_WAVES * 64), lds, a.s>>>(
+        a.q, a.q_scales, a.k, a.k_scales, a.w, a.m, a.Hi, a.n_c, a.ratio, a.start_pos, rows_per_wg, nsplit, keys,
+        a.scores, a.K, a.offset, a.idx, a.ld, a.col0);
     return SCKV_OK;
 }
 
 // Fused scores + top-K for one (MT, DI) with KPT keys per thread for the whole
 // query; SCKV_EUNSUPPORTED (nothing launched) when it does not fit in LDS.
-template <int MT, int DI>
-int launch_fused(const uint16_t* q, const uint16_t* k, const float* w, int64_t nq, int64_t m, int Hi, int64_t n_c,
-                 int ratio, int64_t start_pos, int K, int32_t offset, int32_t* idx, int64_t ld, int64_t col0,
-                 hipStream_t s) {
-    const int rows = (int)((n_c + 127) / 128 * 128);
+template <int MT, int DI, bool FP4>
+int launch_fused(const IndexArgs& a) {
+    const int rows = (int)((a.n_c + 127) / 128 * 128);
     const int need = (rows + SCORE_WAVES * 64 - 1) / (SCORE_WAVES * 64);
-#define SCKV_FUSED(KPT)                                                                                          \
-    (score_lds_bytes<MT, DI, KPT>(rows, false) > 160 * 1024                                                       \
-         ? SCKV_EUNSUPPORTED                                                                                      \
-         : launch_scores<MT, DI, KPT>(q, k, w, nq, m, Hi, n_c, ratio, start_pos, rows, 1, nullptr, nullptr, K, \
-                                      offset, idx, ld, col0, s))
+#define SCKV_FUSED(KPT)                                                                           \
+    (score_lds_bytes<MT, DI, KPT, FP4>(rows, false) > 160 * 1024 ? SCKV_EUNSUPPORTED               \
+                                                                  : launch_scores<MT, DI, KPT, FP4>(a, rows, 1, nullptr))
     if (need <= 8) return SCKV_FUSED(8);
     if (need <= 32) return SCKV_FUSED(32);
     if (need <= 128) return SCKV_FUSED(128);
@@ -535,12 +625,73 @@ int score_rows_per_wg(int64_t nq, int64_t n_c, bool with_scores) {
     return (int)(tiles_per * 128);
 }
 
+// Scores (+ top-K) for one Di and head tiling; the split path then runs the
+// top-k kernel over the keys in the workspace.
+template <int MT, int DI, bool FP4>
+int run_index(const IndexArgs& a, uint16_t* keys) {
+    if (!a.scores && a.nq >= FUSED_MIN_QUERIES && a.n_c <= 32768) {
+        // enough queries to fill the chip with one workgroup each: scores and
+        // top-K in one launch, the keys never leaving LDS
+        const int rc = launch_fused<MT, DI, FP4>(a);
+        if (rc != SCKV_EUNSUPPORTED) return rc ? rc : check_launch("sckv_index_scores_topk (fused)");
+    }
+    const int rpw = score_rows_per_wg(a.nq, a.n_c, a.scores != nullptr);
+    const int nsplit = (int)((a.n_c + rpw - 1) / rpw);
+    if (a.nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: grid too large");
+    int rc = launch_scores<MT, DI, 0, FP4>(a, rpw, nsplit, keys);
+    if (rc) return rc;
+    rc = check_launch("sckv_index_scores_topk (scores)");
+    if (rc) return rc;
+    launch_topk(keys, a.nq, a.n_c, a.m, a.ratio, a.start_pos, a.K, a.offset, a.idx, a.ld, a.col0, a.s);
+    return check_launch("sckv_index_scores_topk (top-k)");
+}
+
+// Host checks shared by both entry points; returns 1 when there is work to do.
+int index_checks(const char* name, int B, int64_t m, int Hi, int Di, int64_t n_c, int ratio, int64_t start_pos, int K,
+                 int32_t offset, int32_t* idx, int64_t ld, int64_t col0, bool fp4) {
+    if (B < 0 || m < 0 || n_c < 0 || ratio <= 0 || start_pos < 0 || K < 0 || col0 < 0 || offset < 0)
+        return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
+    if (Hi <= 0 || (Hi & (Hi - 1)) != 0) return fail(SCKV_EINVAL, std::string(name) + ": Hi must be a power of two");
+    if (Hi > 64) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": Hi > 64");
+    if (fp4 ? (Di != 128 && Di != 256) : (Di != 32 && Di != 64 && Di != 128 && Di != 256))
+        return fail(SCKV_EUNSUPPORTED,
+                    std::string(name) + (fp4 ? ": Di not in {128, 256}" : ": Di not in {32, 64, 128, 256}"));
+    if (B == 0 || m == 0 || K == 0) return 0;
+    if (!idx) return fail(SCKV_EINVAL, std::string(name) + ": null idx");
+    if (ld < col0 + K) return fail(SCKV_EINVAL, std::string(name) + ": ld < col0 + K");
+    if (n_c > 65536 || (int64_t)offset + n_c > 0x7fffffffLL)
+        return fail(SCKV_EUNSUPPORTED, std::string(name) + ": n_c > 65536 or offset + n_c >= 2^31");
+    if ((int64_t)B * m > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": too many queries");
+    return 1;
+}
+
+template <bool FP4>
+int dispatch_index(int Di, bool two, const IndexArgs& a, uint16_t* keys) {
+    if (FP4) {
+        if (Di == 128) return two ? run_index<2, 128, true>(a, keys) : run_index<1, 128, true>(a, keys);
+        return two ? run_index<2, 256, true>(a, keys) : run_index<1, 256, true>(a, keys);
+    }
+    switch (Di) {
+        case 32: return two ? run_index<2, 32, false>(a, keys) : run_index<1, 32, false>(a, keys);
+        case 64: return two ? run_index<2, 64, false>(a, keys) : run_index<1, 64, false>(a, keys);
+        case 128: return two ? run_index<2, 128, false>(a, keys) : run_index<1, 128, false>(a, keys);
+        default: return two ? run_index<2, 256, false>(a, keys) : run_index<1, 256, false>(a, keys);
+    }
+}
+
+size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
 }  // namespace
 
 size_t index_workspace_bytes(int B, int64_t m, int64_t n_c) {
     // one 16-bit key per (query, compressed row), 256-byte aligned
-    const size_t bytes = (size_t)B * (size_t)m * (size_t)n_c * 2u;
-    return (bytes + 255u) & ~(size_t)255u;
+    return align256((size_t)B * (size_t)m * (size_t)n_c * 2u);
+}
+
+size_t index_fp4_workspace_bytes(int B, int64_t m, int Hi, int Di, int64_t n_c) {
+    // the keys, then q_hat packed: codes [B*m*Hi][Di/2] and scales [B*m*Hi][Di/32]
+    const size_t rows = (size_t)B * (size_t)m * (size_t)Hi;
+    return index_workspace_bytes(B, m, n_c) + align256(rows * (size_t)(Di / 2)) + align256(rows * (size_t)(Di / 32));
 }
 
 }  // namespace sckv
@@ -550,17 +701,9 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
                                       int32_t* idx, int64_t ld, int64_t col0, void* scores, void* ws,
                                       size_t ws_bytes, void* stream) {
     using namespace sckv;
-    if (B < 0 || m < 0 || n_c < 0 || ratio <= 0 || start_pos < 0 || K < 0 || col0 < 0 || offset < 0)
-        return fail(SCKV_EINVAL, "sckv_index_scores_topk: bad sizes");
-    if (Hi <= 0 || (Hi & (Hi - 1)) != 0) return fail(SCKV_EINVAL, "sckv_index_scores_topk: Hi must be a power of two");
-    if (Hi > 64) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: Hi > 64");
-    if (Di != 32 && Di != 64 && Di != 128 && Di != 256)
-        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: Di not in {32, 64, 128, 256}");
-    if (B == 0 || m == 0 || K == 0) return SCKV_OK;
-    if (!idx) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null idx");
-    if (ld < col0 + K) return fail(SCKV_EINVAL, "sckv_index_scores_topk: ld < col0 + K");
-    if (n_c > 65536 || (int64_t)offset + n_c > 0x7fffffffLL)
-        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: n_c > 65536 or offset + n_c >= 2^31");
+    const char* name = "sckv_index_scores_topk";
+    const int go = index_checks(name, B, m, Hi, Di, n_c, ratio, start_pos, K, offset, idx, ld, col0, false);
+    if (go <= 0) return go;
     const int64_t nq = (int64_t)B * m;
     hipStream_t s = (hipStream_t)stream;
     // no compressed row is visible to any query: every list is K x -1 (the pages' empty selection)
@@ -568,51 +711,53 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
     vmax = vmax < n_c ? vmax : n_c;
     if (vmax == 0) {
         launch_topk(nullptr, nq, 0, m, ratio, start_pos, K, offset, idx, ld, col0, s);
-        return check_launch("sckv_index_scores_topk");
+        return check_launch(name);
     }
     if (!q || !k || !w) return fail(SCKV_EINVAL, "sckv_index_scores_topk: null input");
     if ((uintptr_t)q % 16 || (uintptr_t)k % 16)
         return fail(SCKV_EINVAL, "sckv_index_scores_topk: q and k must be 16-byte aligned");
     if ((uintptr_t)w % 4 || (uintptr_t)idx % 4) return fail(SCKV_EINVAL, "sckv_index_scores_topk: misaligned w/idx");
     if (scores && (uintptr_t)scores % 2) return fail(SCKV_EINVAL, "sckv_index_scores_topk: misaligned scores");
-    const size_t need = index_workspace_bytes(B, m, n_c);
-    if (!ws || ws_bytes < need) return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk: workspace too small");
-    if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: too many queries");
-    const uint16_t* qq = (const uint16_t*)q;
-    const uint16_t* kk = (const uint16_t*)k;
-    uint16_t* sc = (uint16_t*)scores;
-    const bool two = Hi > 32;
-    int rc;
-    if (!scores && nq >= FUSED_MIN_QUERIES && n_c <= 32768) {
-        // enough queries to fill the chip with one workgroup each: scores and
-        // top-K in one launch, the keys never leaving LDS
-#define SCKV_FUSED(MT, DI) launch_fused<MT, DI>(qq, kk, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx, ld, col0, s)
-        switch (Di) {
-            case 32: rc = two ? SCKV_FUSED(2, 32) : SCKV_FUSED(1, 32); break;
-            case 64: rc = two ? SCKV_FUSED(2, 64) : SCKV_FUSED(1, 64); break;
-            case 128: rc = two ? SCKV_FUSED(2, 128) : SCKV_FUSED(1, 128); break;
-            default: rc = two ? SCKV_FUSED(2, 256) : SCKV_FUSED(1, 256); break;
-        }
-#undef SCKV_FUSED
-        if (rc != SCKV_EUNSUPPORTED) return rc ? rc : check_launch("sckv_index_scores_topk (fused)");
+    if (!ws || ws_bytes < index_workspace_bytes(B, m, n_c))
+        return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk: workspace too small");
+    const IndexArgs a{q, nullptr, k, nullptr, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx, ld, col0,
+                      (uint16_t*)scores, s};
+    return dispatch_index<false>(Di, Hi > 32, a, (uint16_t*)ws);
+}
+
+extern "C" int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, const void* k_scales, const float* w,
+                                          int B, int64_t m, int Hi, int Di, int64_t n_c, int ratio, int64_t start_pos,
+                                          int K, int32_t offset, int32_t* idx, int64_t ld, int64_t col0,
+                                          void* scores, void* ws, size_t ws_bytes, void* stream) {
+    using namespace sckv;
+    const char* name = "sckv_index_scores_topk_fp4";
+    const int go = index_checks(name, B, m, Hi, Di, n_c, ratio, start_pos, K, offset, idx, ld, col0, true);
+    if (go <= 0) return go;
+    const int64_t nq = (int64_t)B * m;
+    hipStream_t s = (hipStream_t)stream;
+    int64_t vmax = (start_pos + m) / ratio;
+    vmax = vmax < n_c ? vmax : n_c;
+    if (vmax == 0) {
+        launch_topk(nullptr, nq, 0, m, ratio, start_pos, K, offset, idx, ld, col0, s);
+        return check_launch(name);
     }
-    const int rpw = score_rows_per_wg(nq, n_c, scores != nullptr);
-    const int nsplit = (int)((n_c + rpw - 1) / rpw);
-    if (nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: grid too large");
-    uint16_t* keys = (uint16_t*)ws;
-#define SCKV_SCORES(MT, DI)                                                                                   \
-    launch_scores<MT, DI, 0>(qq, kk, w, nq, m, Hi, n_c, ratio, start_pos, rpw, nsplit, keys, sc, K, offset, idx, \
-                             ld, col0, s)
-    switch (Di) {
-        case 32: rc = two ? SCKV_SCORES(2, 32) : SCKV_SCORES(1, 32); break;
-        case 64: rc = two ? SCKV_SCORES(2, 64) : SCKV_SCORES(1, 64); break;
-        case 128: rc = two ? SCKV_SCORES(2, 128) : SCKV_SCORES(1, 128); break;
-        default: rc = two ? SCKV_SCORES(2, 256) : SCKV_SCORES(1, 256); break;
-    }
-#undef SCKV_SCORES
+    if (!q || !k_codes || !k_scales || !w) return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: null input");
+    if ((uintptr_t)q % 16 || (uintptr_t)k_codes % 16 || (uintptr_t)k_scales % 4)
+        return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: q / k codes must be 16-byte, k scales 4-byte aligned");
+    if ((uintptr_t)w % 4 || (uintptr_t)idx % 4)
+        return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: misaligned w/idx");
+    if (scores && (uintptr_t)scores % 2) return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: misaligned scores");
+    if (!ws || ws_bytes < index_fp4_workspace_bytes(B, m, Hi, Di, n_c))
+        return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk_fp4: workspace too small");
+    // q_hat of every query, packed, into the workspace (one pass over q)
+    unsigned char* wsb = (unsigned char*)ws;
+    uint16_t* keys = (uint16_t*)wsb;
+    unsigned char* qc = wsb + index_workspace_bytes(B, m, n_c);
+    const size_t qrows = (size_t)nq * (size_t)Hi;
+    unsigned char* qsc = qc + align256(qrows * (size_t)(Di / 2));
+    int rc = quant_pack_impl(q, Di, qc, Di / 2, qsc, Di / 32, (int64_t)qrows, Di, SCKV_FP4_E8M0_B32, stream);
     if (rc) return rc;
-    rc = check_launch("sckv_index_scores_topk (scores)");
-    if (rc) return rc;
-    launch_topk(keys, nq, n_c, m, ratio, start_pos, K, offset, idx, ld, col0, s);
-    return check_launch("sckv_index_scores_topk (top-k)");
+    const IndexArgs a{qc, qsc, k_codes, (const uint8_t*)k_scales, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx,
+                      ld, col0, (uint16_t*)scores, s};
+    return dispatch_index<true>(Di, Hi > 32, a, keys);
 }

@@ -112,7 +112,100 @@ int quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t ro
     return launch_quant<SCKV_FP4_E8M0_B32>((const uint16_t*)x, ldx, (uint16_t*)y, ldy, rows, cols, s);
 }
 
+// ---- packed storage: 4-bit codes (two a byte, the even element low) and one
+// scale byte per block; one lane per block, as above.
+template <int MODE>
+__global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_t* __restrict__ x, int64_t ldx,
+                                                                    uint8_t* __restrict__ codes, int64_t ldc,
+                                                                    uint8_t* __restrict__ scales, int64_t lds,
+                                                                    int64_t blocks_per_row, int64_t nblocks,
+                                                                    bool vec) {
+    constexpr int BLOCK = QuantMode<MODE>::BLOCK;
+    const int64_t gid = (int64_t)blockIdx.x * QUANT_THREADS + threadIdx.x;
+    if (gid >= nblocks) return;
+    const int64_t row = gid / blocks_per_row;
+    const int64_t blk = gid - row * blocks_per_row;
+    const uint16_t* src = x + row * ldx + blk * BLOCK;
+    uint32_t w[BLOCK / 2];
+    if (vec) {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 8; ++i) {
+            const uint4 v = reinterpret_cast<const uint4*>(src)[i];
+            w[4 * i + 0] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+    const float s = block_scale<MODE>(amax);
+    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
+    // BLOCK/2 bytes of codes: byte i holds elements 2i (low) and 2i+1 (high)
+    uint32_t cw[BLOCK / 8];
+#pragma unroll
+    for (int i = 0; i < BLOCK / 8; ++i) cw[i] = 0;
+#pragma unroll
+    for (int i = 0; i < BLOCK; ++i) {
+        const float v = bf16_bits_to_f32((i & 1) ? (w[i / 2] >> 16) : (w[i / 2] & 0xffffu));
+        const float a = (MODE == SCKV_FP4_E8M0_B32) ? fminf(fabsf(v) * inv_s, 6.0f)
+                                                    : fminf(__fdiv_rn(fabsf(v), s), 6.0f);
+        cw[i / 8] |= e2m1_code(e2m1_round_mag(a), v) << (4 * (i % 8));
+    }
+    uint8_t* cdst = codes + row * ldc + blk * (BLOCK / 2);
+    if (vec) {
+        if (BLOCK == 32)
+            *reinterpret_cast<uint4*>(cdst) = make_uint4(cw[0], cw[BLOCK / 8 > 1 ? 1 : 0], cw[BLOCK / 8 > 2 ? 2 : 0],
+                                                         cw[BLOCK / 8 > 3 ? 3 : 0]);
+        else
+            *reinterpret_cast<uint2*>(cdst) = make_uint2(cw[0], cw[BLOCK / 8 > 1 ? 1 : 0]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < BLOCK / 2; ++i) cdst[i] = (uint8_t)(cw[i / 4] >> (8 * (i % 4)));
+    }
+    scales[row * lds + blk] = (uint8_t)scale_byte<MODE>(s);
+}
+
 }  // namespace
+
+int quant_pack_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
+                    int64_t cols, int mode, void* stream) {
+    if (mode != SCKV_FP4_E4M3_B16 && mode != SCKV_FP4_E8M0_B32) return fail(SCKV_EINVAL, "sckv_quant_pack: bad mode");
+    const int block = (mode == SCKV_FP4_E4M3_B16) ? 16 : 32;
+    if (rows < 0 || cols < 0) return fail(SCKV_EINVAL, "sckv_quant_pack: negative size");
+    if (cols % block != 0) return fail(SCKV_EINVAL, "sckv_quant_pack: row length is not a multiple of the block");
+    if (rows == 0 || cols == 0) return SCKV_OK;
+    if (!x || !codes || !scales) return fail(SCKV_EINVAL, "sckv_quant_pack: null pointer");
+    if (ldx < cols || ldc < cols / 2 || lds < cols / block)
+        return fail(SCKV_EINVAL, "sckv_quant_pack: a row stride is shorter than its row");
+    if ((uintptr_t)x % 2) return fail(SCKV_EINVAL, "sckv_quant_pack: x not 2-byte aligned");
+    const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(((rows - 1) * ldx + cols) * 2);
+    const uintptr_t cs = (uintptr_t)codes, ce = cs + (uintptr_t)((rows - 1) * ldc + cols / 2);
+    const uintptr_t ss = (uintptr_t)scales, se = ss + (uintptr_t)((rows - 1) * lds + cols / block);
+    if ((xs < ce && cs < xe) || (xs < se && ss < xe) || (cs < se && ss < ce))
+        return fail(SCKV_EINVAL, "sckv_quant_pack: x, codes and scales overlap");
+    const int64_t bpr = cols / block;
+    const int64_t nblocks = rows * bpr;
+    const int64_t grid = (nblocks + QUANT_THREADS - 1) / QUANT_THREADS;
+    if (grid > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_quant_pack: too many blocks for one launch");
+    const bool vec = (xs % 16 == 0) && (ldx % 8 == 0) && (cs % (block / 2) == 0) && (ldc % (block / 2) == 0);
+    hipStream_t s = (hipStream_t)stream;
+    if (mode == SCKV_FP4_E4M3_B16)
+        quant_pack_kernel<SCKV_FP4_E4M3_B16><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+            (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec);
+    else
+        quant_pack_kernel<SCKV_FP4_E8M0_B32><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+            (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec);
+    return check_launch("sckv_quant_pack");
+}
+
 }  // namespace sckv
 
 extern "C" int sckv_quant(const void* x, void* y, int64_t n, int mode, void* stream) {
@@ -128,4 +221,9 @@ extern "C" int sckv_quant(const void* x, void* y, int64_t n, int mode, void* str
 extern "C" int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
                                int mode, void* stream) {
     return sckv::quant_rows_impl(x, ldx, y, ldy, rows, cols, mode, stream);
+}
+
+extern "C" int sckv_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds,
+                               int64_t rows, int64_t cols, int mode, void* stream) {
+    return sckv::quant_pack_impl(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
 }

@@ -124,6 +124,26 @@ __device__ __forceinline__ uint32_t fp4_value(float v, float s, float inv_s) {
     return fp4_value_bits(v, s);
 }
 
+// ---------------------------------------------------------------- packed storage
+
+// 4-bit code of a value of the round trip: the e2m1 grid index of its
+// magnitude r (r / s, one of 0, .5, 1, 1.5, 2, 3, 4, 6) plus 8 when v is
+// negative (the round trip keeps the sign of v, -0 included).
+__device__ __forceinline__ uint32_t e2m1_code(float r, float v) {
+    const uint32_t idx = (r < 2.0f) ? (uint32_t)(r * 2.0f) : ((r < 4.0f) ? (uint32_t)r + 2u : ((r < 5.0f) ? 6u : 7u));
+    return idx | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// Scale byte of a block: the E8M0 exponent of a power-of-two scale, or the
+// E4M3FN code of an e4m3 scale (s is exactly representable in either case).
+template <int MODE>
+__device__ __forceinline__ uint32_t scale_byte(float s) {
+    const uint32_t u = __float_as_uint(s);
+    if (MODE == SCKV_FP4_E8M0_B32) return (u >> 23) & 0xffu;
+    if (s < 0.015625f) return (uint32_t)(s * 512.0f);  // subnormal: s = code * 2^-9
+    return ((((u >> 23) & 0xffu) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
 template <int MODE>
 struct QuantMode;
 template <>
@@ -138,6 +158,9 @@ struct QuantMode<SCKV_FP4_E8M0_B32> {
 // ---------------------------------------------------------------- host side
 
 void set_error(const std::string& msg);
+// the packed round trip of sckv_quant_pack (also used on q inside the fp4 indexer)
+int quant_pack_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
+                    int64_t cols, int mode, void* stream);
 int fail(int code, const std::string& msg);
 int check_launch(const char* what);
 

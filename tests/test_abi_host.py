@@ -65,6 +65,16 @@ def test_error_paths(L):
     assert L.sckv_quant_rows(fake, 8, fake, 8, 2, 16, sk.SCKV_FP4_E4M3_B16, None) == sk.SCKV_EINVAL  # ld < cols
     assert L.sckv_quant_rows(fake, 16, ctypes.c_void_p(0x1010), 16, 2, 16, sk.SCKV_FP4_E4M3_B16,
                              None) == sk.SCKV_EINVAL  # overlap
+    # packed round trip: block multiple, strides, overlap, mode
+    big = ctypes.c_void_p(0x100000)
+    assert L.sckv_quant_pack(fake, 40, big, 20, ctypes.c_void_p(0x200000), 2, 1, 40, sk.SCKV_FP4_E8M0_B32,
+                             None) == sk.SCKV_EINVAL  # 40 values: not a multiple of 32
+    assert L.sckv_quant_pack(fake, 64, big, 16, ctypes.c_void_p(0x200000), 2, 2, 64, sk.SCKV_FP4_E8M0_B32,
+                             None) == sk.SCKV_EINVAL  # ldc 16 < 32 code bytes
+    assert L.sckv_quant_pack(fake, 64, ctypes.c_void_p(0x1020), 32, ctypes.c_void_p(0x200000), 2, 2, 64,
+                             sk.SCKV_FP4_E8M0_B32, None) == sk.SCKV_EINVAL  # codes overlap x
+    assert L.sckv_quant_pack(fake, 64, big, 32, ctypes.c_void_p(0x200000), 2, 2, 64, 5, None) == sk.SCKV_EINVAL
+    assert L.sckv_quant_pack(fake, 64, big, 32, None, 2, 2, 64, sk.SCKV_FP4_E8M0_B32, None) == sk.SCKV_EINVAL
     # ring
     assert L.sckv_ring_write(fake, 64, fake, 64, 1, 1, 5, 0, 64, None) == sk.SCKV_EINVAL
     assert L.sckv_ring_write(fake, 64, fake, 64 * 16, 1, 1, 5, 16, 64, None) == sk.SCKV_EINVAL  # overlap

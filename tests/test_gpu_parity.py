@@ -119,6 +119,56 @@ def test_quant_rows_strided(sk):
     assert np.array_equal(bits(yv[1:]), oracle.quant(new[0, :64], oracle.E8M0_B32))
 
 
+@pytest.mark.parametrize("mode", [oracle.E8M0_B32, oracle.E4M3_B16], ids=["e8m0_b32", "e4m3_b16"])
+def test_quant_pack_bit_exact(sk, mode):
+    """Packed codes and scale bytes against the oracle's packing, on the scale
+    sweep (every reachable scale, every magnitude through the rounding) and on
+    random rows, read back through the oracle's unpacking as well."""
+    dev_mode = sk.SCKV_FP4_E8M0_B32 if mode == oracle.E8M0_B32 else sk.SCKV_FP4_E4M3_B16
+    block = 32 if mode == oracle.E8M0_B32 else 16
+    x = _scale_sweep_blocks(mode)
+    rng = np.random.default_rng(31)
+    x = np.concatenate([x, bits(bf16_of(rng.standard_normal(block * 4096)))])
+    cols = block * 8
+    pad = (-x.size) % cols
+    x = np.concatenate([x, np.zeros(pad, np.uint16)])
+    rows = x.size // cols
+    xd = from_bits(x, "cuda")
+    codes = torch.zeros(rows * cols // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros(rows * cols // block, dtype=torch.uint8, device="cuda")
+    say(f"quant_pack {mode} rows={rows}")
+    sk.sckv_quant_pack(xd, cols, codes, cols // 2, scales, cols // block, rows, cols, dev_mode)
+    wc, ws = oracle.pack(x, mode)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(gs, ws)
+    assert np.array_equal(gc, wc)
+    assert np.array_equal(oracle.unpack(gc, gs, x.size, mode), oracle.quant(x, mode))
+
+
+def test_quant_pack_strided(sk):
+    """Rows with padded strides on every side (the k-cache row of B caches),
+    and an unaligned source (byte stores)."""
+    B, D = 6, 128
+    rng = np.random.default_rng(32)
+    x = bits(bf16_of(rng.standard_normal((B, D + 8))))
+    codes = torch.full((B, D // 2 + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((B, 8), 0xCD, dtype=torch.uint8, device="cuda")
+    say("quant_pack strided")
+    sk.sckv_quant_pack(from_bits(x, "cuda"), D + 8, codes, D // 2 + 16, scales, 8, B, D, sk.SCKV_FP4_E8M0_B32)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    for b in range(B):
+        wc, ws = oracle.pack(x[b, :D], oracle.E8M0_B32)
+        assert np.array_equal(gc[b, : D // 2], wc) and np.all(gc[b, D // 2:] == 0xAB)
+        assert np.array_equal(gs[b, :4], ws) and np.all(gs[b, 4:] == 0xCD)
+    xs = torch.zeros(1 + 64, dtype=torch.bfloat16, device="cuda")
+    xs[1:] = from_bits(x[0, :64], "cuda")
+    c2 = torch.zeros(33, dtype=torch.uint8, device="cuda")
+    s2 = torch.zeros(5, dtype=torch.uint8, device="cuda")
+    sk.sckv_quant_pack(xs[1:], 64, c2[1:], 32, s2[1:], 4, 1, 64, sk.SCKV_FP4_E4M3_B16)
+    wc, ws = oracle.pack(x[0, :64], oracle.E4M3_B16)
+    assert np.array_equal(c2[1:].cpu().numpy(), wc) and np.array_equal(s2[1:].cpu().numpy(), ws)
+
+
 # --------------------------------------------------------------------- window, visible, ring
 
 @pytest.mark.parametrize("win,m,start_pos", [(16, 1, 255), (128, 1, 32767), (128, 4096, 0), (128, 2048, 63488),
@@ -304,6 +354,83 @@ def test_index_topk_fused_ties(sk):
     for b in (0, 1, 95, 191):
         sc, _ = oracle.index_scores(q[b], kb, w[b], n_c - 1, 1)
         assert np.array_equal(got[b, 0], oracle.topk(sc[0], n_c, K, 0)), b
+
+
+# The packed k cache (4-bit codes + E8M0 bytes) through the scaled fp4 matrix
+# cores must give the very same scores and lists as the bf16 round trip.
+FP4_CASES = [
+    # B, m, Hi, Di, n_c, ratio, start_pos, K, scores
+    (2, 1, 64, 128, 8192, 4, 32767, 512, True),      # decode shape, split path + scores
+    (1, 3, 64, 128, 1000, 4, 3997, 100, True),      # ragged row tail, several queries
+    (1, 4, 16, 256, 129, 2, 254, 128, True),        # head dim 256, one head tile
+    (1, 6, 64, 128, 20, 4, 0, 8, True),             # early positions: 0, 1, 2 see nothing
+    (192, 1, 64, 128, 1024, 4, 4095, 200, False),   # fused path (one workgroup per query)
+    (200, 1, 4, 128, 9000, 1, 8999, 1000, False),   # fused, 128 keys per thread
+    (192, 1, 32, 256, 1500, 1, 1499, 100, False),   # fused, head dim 256
+    (1, 256, 8, 128, 64, 1, 0, 16, False),          # fused, queries that see <= K rows
+]
+
+
+@pytest.mark.parametrize("case", FP4_CASES, ids=lambda c: "B{}m{}Hi{}Di{}nc{}K{}{}".format(
+    *c[:5], c[7], "s" if c[8] else ""))
+def test_index_scores_topk_fp4_bit_exact(sk, case):
+    B, m, Hi, Di, n_c, ratio, start_pos, K, with_scores = case
+    rng = np.random.default_rng(sum(case[:8]) + 3)
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di))))
+    nk = min(B, 2)  # distinct k caches; sequence b uses cache b % nk
+    kraw = bits(bf16_of(rng.standard_normal((nk, n_c, Di))))
+    packs = [oracle.pack(kraw[j].reshape(-1), oracle.E8M0_B32) for j in range(nk)]
+    codes = np.stack([packs[b % nk][0].reshape(n_c, Di // 2) for b in range(B)])
+    scl = np.stack([packs[b % nk][1].reshape(n_c, Di // 32) for b in range(B)])
+    khat = [oracle.quant(kraw[j].reshape(-1), oracle.E8M0_B32).reshape(n_c, Di) for j in range(nk)]
+    w = (rng.standard_normal((B, m, Hi)) * (Hi * Di) ** -0.5).astype(np.float32)
+    col0, off = 1, 555
+    ld = col0 + K + 3
+    idx = torch.full((B, m, ld), -9, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, m, n_c), dtype=torch.bfloat16, device="cuda") if with_scores else None
+    say(f"fp4 indexer case {case}")
+    sk.sckv_index_scores_topk_fp4(from_bits(q, "cuda"), torch.from_numpy(codes).cuda(), torch.from_numpy(scl).cuda(),
+                                  torch.from_numpy(w).cuda(), B, m, Hi, Di, n_c, ratio, start_pos, K, off, idx, ld,
+                                  col0, scores=scores)
+    got = idx.cpu().numpy()
+    assert np.all(got[:, :, :col0] == -9) and np.all(got[:, :, col0 + K:] == -9)
+    got_sc = bits(scores) if with_scores else None
+    bsel = sorted({0, B - 1, *rng.integers(0, B, size=3).tolist()})
+    tsel = np.array(sorted({0, m - 1, *rng.integers(0, m, size=6).tolist()}), dtype=np.int64)
+    if m * n_c <= 20000:
+        tsel = np.arange(m, dtype=np.int64)
+    for b in bsel:
+        sc, bad = oracle.index_scores(q[b], khat[b % nk], w[b], start_pos, ratio, qsel=tsel)
+        assert bad == 0
+        for i, t in enumerate(tsel):
+            v = oracle.visible(start_pos + int(t), ratio, n_c)
+            if with_scores:
+                assert np.array_equal(got_sc[b, t, :v], sc[i, :v]), (b, t)
+            assert np.array_equal(got[b, t, col0:col0 + K], oracle.topk(sc[i], v, K, off)), (b, t)
+
+
+def test_index_topk_fp4_ties(sk):
+    """Forced ties at the K-th place through the fp4 path (fused and split)."""
+    n_c, Di, Hi, K = 500, 128, 4, 64
+    rng = np.random.default_rng(97)
+    base = bits(bf16_of(rng.standard_normal((8, Di))))
+    kraw = base[rng.integers(0, 8, size=n_c)]
+    kc, ks = oracle.pack(kraw.reshape(-1), oracle.E8M0_B32)
+    khat = oracle.quant(kraw.reshape(-1), oracle.E8M0_B32).reshape(n_c, Di)
+    for B in (1, 192):
+        q = bits(bf16_of(rng.standard_normal((B, 1, Hi, Di))))
+        w = np.zeros((B, 1, Hi), np.float32)
+        w[:, :, 0] = 1.0
+        idx = torch.empty((B, 1, K), dtype=torch.int32, device="cuda")
+        say(f"fp4 indexer ties B={B}")
+        sk.sckv_index_scores_topk_fp4(
+            from_bits(q, "cuda"), torch.from_numpy(np.tile(kc.reshape(1, n_c, Di // 2), (B, 1, 1))).cuda(),
+            torch.from_numpy(np.tile(ks.reshape(1, n_c, Di // 32), (B, 1, 1))).cuda(), torch.from_numpy(w).cuda(),
+            B, 1, Hi, Di, n_c, 1, n_c - 1, K, 0, idx, K, 0)
+        got = idx.cpu().numpy()
+        for b in sorted({0, B - 1}):
+            sc, _ = oracle.index_scores(q[b], khat, w[b], n_c - 1, 1)
+            assert np.array_equal(got[b, 0], oracle.topk(sc[0], n_c, K, 0)), b
 
 
 # --------------------------------------------------------------------- attention
