@@ -46,7 +46,7 @@ def describe(w):
     return s
 
 
-def counts(w, B, call):
+def counts(w, B, call, kcache="bf16"):
     """Algorithmic bytes and flops of one library call for one step of B
     sequences: what the method must read and write (bf16 storage, each needed
     row once, valid (query, row) pairs only).  The implementation's workspace
@@ -60,8 +60,9 @@ def counts(w, B, call):
     dense = m > 1
     if call == "quant_latent":
         return {"bytes": B * n_new * D * 4, "flops": 0, "bound": "hbm"}
+    krow = w.Di // 2 + w.Di // 32 if kcache == "fp4" else w.Di * 2  # stored bytes of an indexer k row
     if call == "quant_index_k":
-        return {"bytes": B * n_new * w.Di * 4, "flops": 0, "bound": "hbm"}
+        return {"bytes": B * n_new * (w.Di * 2 + krow), "flops": 0, "bound": "hbm"}
     if call == "ring_write":
         return {"bytes": B * min(m, win) * D * 4, "flops": 0, "bound": "hbm"}
     if call == "window_idx":
@@ -69,7 +70,7 @@ def counts(w, B, call):
     if call == "visible_idx":
         return {"bytes": B * m * w.K * 4, "flops": 0, "bound": "hbm"}
     if call == "index_scores_topk":
-        by = B * (max(V) * w.Di * 2 + m * w.Hi * w.Di * 2 + m * w.Hi * 4 + m * w.K * 4)
+        by = B * (max(V) * krow + m * w.Hi * w.Di * 2 + m * w.Hi * 4 + m * w.K * 4)
         fl = B * sum(V) * w.Hi * w.Di * 2
         return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm"}
     if call == "sparse_attn_sink":
@@ -94,7 +95,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload, B, call):
+def traffic_for(workload, B, call, kcache):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -106,18 +107,18 @@ def traffic_for(workload, B, call):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    entry = rec.get("entries", {}).get(f"{workload}/B{B}/{call}")
+    entry = rec.get("entries", {}).get(f"{workload}/B{B}/{kcache}/{call}")
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 # Library call -> the kernels it launches (demangled-name prefixes).
 CALL_KERNELS = {
     "quant_latent": ["quant_rows_kernel<0,"],
-    "quant_index_k": ["quant_rows_kernel<1,"],
+    "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1,false>"],
     "ring_write": ["ring_write_kernel"],
     "window_idx": ["window_idx_kernel"],
     "visible_idx": ["visible_idx_kernel"],
-    "index_scores_topk": ["index_score_kernel", "topk_kernel"],
+    "index_scores_topk": ["index_score_kernel", "topk_kernel", "quant_pack_kernel<1,true>"],
     "sparse_attn_sink": ["sparse_attn_kernel", "combine_kernel"],
 }
 
@@ -149,7 +150,7 @@ def _csv_rows(folder, suffix):
     return list(csv.DictReader(open(paths[0])))
 
 
-def summarize_profiles(w, B, folder, commands):
+def summarize_profiles(w, B, folder, commands, kcache="bf16"):
     """Turn rocprofv3 output under `folder` (trace/, FETCH_SIZE/, WRITE_SIZE/,
     copy_FETCH_SIZE/, copy_WRITE_SIZE/) into the text summary
     profiles/hot_path_kernels_<workload>_B<B>.txt and the HBM-traffic entries
@@ -176,7 +177,8 @@ def summarize_profiles(w, B, folder, commands):
         copy_bytes = max(float(r["Counter_Value"]) * 1024 for r in cp if "copyBuffer" in r["Kernel_Name"]
                          or "copy" in r["Kernel_Name"].lower())
         scale[c] = (1 << 30) / copy_bytes
-    lines = [f"# rocprofv3 summary: compressed sparse attention hot path, {describe(w)}, B={B}", "#"]
+    lines = [f"# rocprofv3 summary: compressed sparse attention hot path, {describe(w)}, B={B}"
+             + (f", indexer k cache {kcache}" if w.Hi else ""), "#"]
     lines += ["# commands (repo root as working directory):"] + [f"#   {c}" for c in commands]
     lines += [f"# counter scale (1 GiB device copy): FETCH_SIZE x{scale.get('FETCH_SIZE', float('nan')):.3f}, "
               f"WRITE_SIZE x{scale.get('WRITE_SIZE', float('nan')):.3f}",
@@ -199,12 +201,13 @@ def summarize_profiles(w, B, folder, commands):
         if res["FETCH_SIZE"] and res["WRITE_SIZE"] and all(k in res[c] for c in res for k in ks):
             hbm = sum(res["FETCH_SIZE"].get(k, 0) * scale["FETCH_SIZE"] + res["WRITE_SIZE"].get(k, 0)
                       * scale["WRITE_SIZE"] for k in ks)
-        alg = counts(w, B, call)["bytes"]
+        alg = counts(w, B, call, kcache)["bytes"]
         lines.append(f"{call:<20} {us:>9.2f} {alg / 1e6:>9.2f} {'-' if hbm is None else f'{hbm / 1e6:.2f}':>9}")
-        entries[f"{w.name}/B{B}/{call}"] = {"kernels": ks, "avg_us": round(us, 3),
+        entries[f"{w.name}/B{B}/{kcache if w.Hi else 'none'}/{call}"] = {"kernels": ks, "avg_us": round(us, 3),
                                             "hbm_bytes_per_launch": None if hbm is None else int(hbm)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    out = os.path.join(ROOT, "profiles", f"hot_path_kernels_{w.name}_B{B}.txt")
+    kc = f"_kcache_{kcache}" if w.Hi else ""
+    out = os.path.join(ROOT, "profiles", f"hot_path_kernels_{w.name}_B{B}{kc}.txt")
     open(out, "w").write("\n".join(lines) + "\n")
     tj = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(tj)) if os.path.exists(tj) else {}
@@ -255,6 +258,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--instances", type=int, default=None, help="B independent sequences per step")
+    ap.add_argument("--kcache", choices=["fp4", "bf16"], default="fp4",
+                    help="indexer k cache storage: packed fp4 codes + E8M0 bytes (default) or bf16 rows")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single", action="store_true", help="skip the B = 1 latency run (for profiling)")
@@ -268,7 +273,7 @@ def main():
         import sckv_synth as synth  # noqa: PLC0415
 
         w = synth.WORKLOADS[args.workload]
-        summarize_profiles(w, args.instances or DEFAULT_B[args.workload], args.summarize, args.command)
+        summarize_profiles(w, args.instances or DEFAULT_B[args.workload], args.summarize, args.command, args.kcache)
         return
     if args.copy_calibration:
         import torch  # noqa: PLC0415
@@ -297,7 +302,7 @@ def main():
     B = args.instances or DEFAULT_B[args.workload]
     log(f"bench: workload {w.name} B={B}: generating inputs on the device")
     x = synth.make_inputs(w, B, device="cuda")
-    st = PathState(w, x, B)
+    st = PathState(w, x, B, kcache=args.kcache)
     del x
     st.setup()
     calls = st.calls()
@@ -339,7 +344,7 @@ def main():
     single = None
     if B > 1 and not args.no_single:
         x1 = synth.make_inputs(w, 1, device="cuda")
-        s1 = PathState(w, x1, 1)
+        s1 = PathState(w, x1, 1, kcache=args.kcache)
         s1.setup()
         for _ in range(args.warmup):
             s1.step()
@@ -357,7 +362,7 @@ def main():
     tokens = B * w.m
     value = tokens / (ms / 1e3)
     dom = max(per_ms, key=per_ms.get)
-    cnt = counts(w, B, dom)
+    cnt = counts(w, B, dom, args.kcache)
     if cnt["bound"] == "hbm":
         achieved = cnt["bytes"] / (per_ms[dom] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -370,7 +375,7 @@ def main():
     roof["ms_per_launch"] = round(per_ms[dom], 5)
     roof["algorithmic_bytes"] = cnt["bytes"]
     roof["algorithmic_flops"] = cnt["flops"]
-    roof["traffic"] = traffic_for(w.name, B, dom)
+    roof["traffic"] = traffic_for(w.name, B, dom, args.kcache if w.Hi else "none")
 
     line = {
         "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",
@@ -385,7 +390,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), device generator)",
-        "config": {"workload": describe(w), "instances": B, "tokens_per_step": tokens},
+        "config": {"workload": describe(w), "instances": B, "tokens_per_step": tokens,
+                   "indexer_k_cache": args.kcache if w.Hi else None},
         "roofline": roof,
         "per_call_ms": {k: round(v, 5) for k, v in per_ms.items()},
         "single_instance": single,

@@ -755,7 +755,7 @@ extern "C" int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, co
     unsigned char* qc = wsb + index_workspace_bytes(B, m, n_c);
     const size_t qrows = (size_t)nq * (size_t)Hi;
     unsigned char* qsc = qc + align256(qrows * (size_t)(Di / 2));
-    int rc = quant_pack_impl(q, Di, qc, Di / 2, qsc, Di / 32, (int64_t)qrows, Di, SCKV_FP4_E8M0_B32, stream);
+    int rc = quant_pack_q_impl(q, Di, qc, Di / 2, qsc, Di / 32, (int64_t)qrows, Di, SCKV_FP4_E8M0_B32, stream);
     if (rc) return rc;
     const IndexArgs a{qc, qsc, k_codes, (const uint8_t*)k_scales, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx,
                       ld, col0, (uint16_t*)scores, s};

@@ -36,8 +36,13 @@ class PathState:
     raw CPU inputs (see sckv_synth.make_inputs).  setup() round-trips the cache
     rows that existed before this step; step() runs the hot path."""
 
-    def __init__(self, w, inputs: dict, B: int = 1, device="cuda"):
-        self.w, self.B, self.device = w, B, device
+    def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16"):
+        """kcache: "bf16" keeps the indexer k cache as round-tripped bf16 rows
+        (the pages' layout); "fp4" keeps it packed (4-bit codes + one E8M0 byte
+        per 32 values) and scores it on the scaled fp4 matrix cores."""
+        if kcache not in ("bf16", "fp4"):
+            raise ValueError(kcache)
+        self.w, self.B, self.device, self.kcache = w, B, device, kcache
         dev = lambda t: t.to(device).contiguous()  # noqa: E731
         self.q = dev(inputs["q"])
         self.sink = dev(inputs["sink"])
@@ -69,7 +74,12 @@ class PathState:
             self.iw = dev(inputs["iw"])
             self.ik = dev(inputs["ik_raw"])
             self.ik_new = inputs["ik_raw"][:, self.first_new:].to(device).clone()
-            self.ws_index = sk.workspace(sk.SCKV_OP_INDEX_SCORES_TOPK, B, m, w.Hi, w.Di, w.n_c, device=device)
+            if kcache == "fp4":
+                self.ik_codes = torch.zeros((B, w.n_c, w.Di // 2), dtype=torch.uint8, device=device)
+                self.ik_scales = torch.zeros((B, w.n_c, w.Di // 32), dtype=torch.uint8, device=device)
+                self.ws_index = sk.workspace(sk.SCKV_OP_INDEX_SCORES_TOPK_FP4, B, m, w.Hi, w.Di, w.n_c, device=device)
+            else:
+                self.ws_index = sk.workspace(sk.SCKV_OP_INDEX_SCORES_TOPK, B, m, w.Hi, w.Di, w.n_c, device=device)
         self.T = w.T
         self.idx = torch.empty((B, m, self.T), dtype=torch.int32, device=device)
         self.out = torch.empty((B, m, w.H, D), dtype=torch.bfloat16, device=device)
@@ -82,7 +92,11 @@ class PathState:
         if self.first_new > 0:
             sk.sckv_quant_rows(self.latent, w.n_c * w.D, self.latent, w.n_c * w.D, B, self.first_new * w.D,
                                sk.SCKV_FP4_E4M3_B16)
-            if w.Hi:
+            if w.Hi and self.kcache == "fp4":
+                # every row packed (the step's own new rows are packed again by its first calls)
+                sk.sckv_quant_pack(self.ik, w.Di, self.ik_codes, w.Di // 2, self.ik_scales, w.Di // 32, B * w.n_c,
+                                   w.Di, sk.SCKV_FP4_E8M0_B32)
+            elif w.Hi:
                 sk.sckv_quant_rows(self.ik, w.n_c * w.Di, self.ik, w.n_c * w.Di, B, self.first_new * w.Di,
                                    sk.SCKV_FP4_E8M0_B32)
 
@@ -99,18 +113,40 @@ class PathState:
             for b in range(B):
                 sk.sckv_quant_rows(src[b], width, dst[b, self.first_new:], width, self.n_new, width, mode)
 
+    def _pack_new_k(self):
+        """The step's new indexer k rows into the packed cache."""
+        w, B, Di = self.w, self.B, self.w.Di
+        if self.n_new == 0:
+            return
+        f = self.first_new
+        if self.n_new == 1 or B == 1:
+            rows, ldc, lds = (B, w.n_c * Di // 2, w.n_c * Di // 32) if self.n_new == 1 else (self.n_new, Di // 2,
+                                                                                              Di // 32)
+            sk.sckv_quant_pack(self.ik_new, Di, self.ik_codes[:, f], ldc, self.ik_scales[:, f], lds, rows, Di,
+                               sk.SCKV_FP4_E8M0_B32)
+        else:
+            for b in range(B):
+                sk.sckv_quant_pack(self.ik_new[b], Di, self.ik_codes[b, f], Di // 2, self.ik_scales[b, f], Di // 32,
+                                   self.n_new, Di, sk.SCKV_FP4_E8M0_B32)
+
     def calls(self):
         """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
         m, win, D = w.m, w.win, w.D
         out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
-        if w.Hi:
+        if w.Hi and self.kcache == "fp4":
+            out.append(("quant_index_k", self._pack_new_k))
+        elif w.Hi:
             out.append(("quant_index_k", lambda: self._quant_new(self.ik_new, self.ik, w.Di, sk.SCKV_FP4_E8M0_B32)))
         if self.mode == "ring":
             out.append(("ring_write", lambda: sk.sckv_ring_write(self.kv_new, D, self.ring, win * D, B, 1,
                                                                  w.start_pos, win, D)))
         out.append(("window_idx", lambda: sk.sckv_window_idx(B, m, w.start_pos, win, self.idx, self.T)))
-        if w.Hi:
+        if w.Hi and self.kcache == "fp4":
+            out.append(("index_scores_topk", lambda: sk.sckv_index_scores_topk_fp4(
+                self.iq, self.ik_codes, self.ik_scales, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K,
+                self.ra, self.idx, self.T, win, ws=self.ws_index)))
+        elif w.Hi:
             out.append(("index_scores_topk", lambda: sk.sckv_index_scores_topk(
                 self.iq, self.ik, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K, self.ra, self.idx,
                 self.T, win, ws=self.ws_index)))

@@ -499,15 +499,19 @@ def test_sparse_attn_edge_rows(sk):
 
 # --------------------------------------------------------------------- the whole step per workload
 
-@pytest.mark.parametrize("name", list(synth.WORKLOADS))
-def test_step_matches_oracle(sk, name):
+STEP_CASES = [(n, "bf16") for n in synth.WORKLOADS] + [
+    (n, "fp4") for n, w in synth.WORKLOADS.items() if w.Hi and w.Di in (128, 256)]
+
+
+@pytest.mark.parametrize("name,kcache", STEP_CASES, ids=lambda c: c if isinstance(c, str) else None)
+def test_step_matches_oracle(sk, name, kcache):
     from sparse_compressed_kv_e2m1_amd.step import PathState
 
     w = synth.WORKLOADS[name]
     B = 2 if w.m == 1 else 1
-    say(f"step {name} B={B}: generating inputs")
+    say(f"step {name} ({kcache} k cache) B={B}: generating inputs")
     x = synth.make_inputs(w, B)
-    st = PathState(w, x, B)
+    st = PathState(w, x, B, kcache=kcache)
     st.setup()
     say(f"step {name}: running the HIP path")
     st.step()
