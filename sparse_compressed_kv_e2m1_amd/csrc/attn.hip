@@ -49,16 +49,18 @@ struct AttnShape {
     static constexpr int NT = D / 16;       // 16-wide output tiles
     static constexpr int RPW = CHUNK / NHW; // rows a wave copies in per chunk of its set
     static constexpr int NST = 2;           // stages per set
-    // row stride in a stage: RS / 4 is 4 times an odd number, so 16 rows read at one column
-    // (the A operand) and the transposing reads hit every bank evenly
-    static constexpr int RS = 2 * D + 16;
+    // row stride in a stage, 32 bytes of padding: measured on gfx950, the S^T
+    // operand reads (16 rows at one 16-byte column) then run at the full
+    // 256 B/clk and the transposing reads at ~170 B/clk, against 128 B/clk for
+    // both with 16 bytes of padding
+    static constexpr int RS = 2 * D + 32;
     static constexpr int STAGE = CHUNK * RS;
     static constexpr int OFF_IDX = 2 * NST * STAGE;
     static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
     // the second set's O (HP rows of D + 4 floats) and (max, sum) reuse the stages
     static constexpr int OS = D + 4;
     static_assert((size_t)HP * OS * 4 + HP * 8 <= (size_t)OFF_IDX, "merge space");
-    static_assert(RPW % 4 == 0 && ((RS / 4) % 8) == 4, "shape");
+    static_assert(RPW % 4 == 0 && (RS % 16) == 0, "shape");
 };
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (same head in the MFMA
