@@ -32,7 +32,10 @@
 namespace sckv {
 namespace {
 
-constexpr int SCORE_WAVES = 4;
+// waves of a score workgroup: 4 with bf16 k tiles (the LDS holds four
+// 4-deep rings of 8 KiB tiles), 8 with packed fp4 tiles (small tiles; two
+// waves a SIMD hide the w.relu / head-sum vector work behind each other)
+constexpr int score_waves(bool fp4) { return fp4 ? 8 : 4; }
 constexpr int TOPK_THREADS = 512;
 constexpr int FUSED_MIN_QUERIES = 192;  // fused scores + top-K from this many queries on
 
@@ -163,13 +166,14 @@ struct ScoreShape {
     static constexpr int CT = 32 * ROWB;               // bytes of a 32-row tile's rows
     static constexpr int TILE = CT + 32 * SB;          // ... plus its scale bytes
     static constexpr int NINST = CT / 1024 + (FP4 ? 1 : 0);  // copies per tile (the last one: scales)
-    static constexpr int NST = NST_ > 0 ? NST_ : (FP4 ? 8 : ((TILE >= 16384) ? 1 : 4));  // tiles per wave in the ring
+    static constexpr int NST = NST_ > 0 ? NST_ : (FP4 ? (TILE >= 4096 ? 4 : 8) : ((TILE >= 16384) ? 1 : 4));  // tiles per wave in the ring
     static constexpr int PD = NST - 1;                 // tiles requested ahead of the one used
     static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // bf16 chunk swizzle mask
     static constexpr int RPS = 16 / (CPR < 16 ? CPR : 16);  // fp4: rows sharing one swizzle value
     static constexpr int QS = FP4 ? DI / 2 : DI * 2;   // bytes per q row in LDS (fp4: codes)
-    static constexpr int OFF_Q = SCORE_WAVES * NST * TILE;
+    static constexpr int NW = score_waves(FP4);       // waves
+    static constexpr int OFF_Q = NW * NST * TILE;
     static constexpr int OFF_QS = OFF_Q + HP * QS;     // fp4: q scale bytes [HP][SB]
     static constexpr int OFF_W = OFF_QS + HP * SB;     // 64 f32 head weights
     // keys (then scores) reuse the q / w space once q_hat and the weights sit
@@ -201,7 +205,10 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 // Ring depth of the fused kernel: the keys of a whole query share the LDS
 // with the ring (KPT keys per thread, 256 threads).
 constexpr int fused_ring_depth(int DI, int KPT, bool FP4) {
-    return FP4 ? (KPT >= 128 ? 6 : 8) : ((64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4));
+    // fp4, few rows a wave (KPT 8: at most 2048 rows, 8 tiles a wave): a
+    // shallow ring, so that two workgroups share a compute unit
+    return FP4 ? (17 * DI >= 4096 ? (KPT >= 64 || KPT <= 8 ? 2 : 3) : (KPT >= 64 ? 4 : (KPT <= 8 ? 3 : 8)))
+               : ((64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4));
 }
 
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e2m1 (format 4): lane l
@@ -222,7 +229,7 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32
 // the already round-tripped, packed q_hat (codes [Hi][DI/2], scales
 // [Hi][DI/32] per query); otherwise k is bf16 [n_c][DI] and q the raw bf16 q.
 template <int MT, int DI, int KPT, bool FP4>
-__global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
+__global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
     const void* __restrict__ q, const void* __restrict__ q_scales, const void* __restrict__ k,
     const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
     int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
@@ -247,7 +254,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     if (KPT > 0 && vis <= K) {
         // every visible row is selected: no scores needed
         int32_t* out = idx + qi * ld + col0;
-        for (int j = threadIdx.x; j < K; j += SCORE_WAVES * 64) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
+        for (int j = threadIdx.x; j < K; j += S::NW * 64) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
         return;
     }
     // (the split path leaves such queries to the top-k kernel; it still writes
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     // so that the B-operand reads below (32 rows at one chunk) spread over all
     // banks.  FP4: the tile's scale bytes follow its codes.
     const int64_t nrows = row_end - row0;
-    const int64_t per_wave = (((nrows + SCORE_WAVES - 1) / SCORE_WAVES) + 31) / 32 * 32;
+    const int64_t per_wave = (((nrows + S::NW - 1) / S::NW) + 31) / 32 * 32;
     const int64_t w0 = row0 + (int64_t)wave * per_wave;
     int64_t w1 = w0 + per_wave;
     w1 = w1 < row_end ? w1 : row_end;
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     // global load is issued in this kernel, so every vmcnt wait is explicit.
     const int qbytes = Hi * S::QS;
     const unsigned char* qrow = reinterpret_cast<const unsigned char*>(q) + qi * (int64_t)qbytes;
-    for (int j = wave; j * 1024 < qbytes; j += SCORE_WAVES)
+    for (int j = wave; j * 1024 < qbytes; j += S::NW)
         if (j * 1024 + lane * 16 < qbytes) dma16_s(qrow, (uint32_t)(j * 1024 + lane * 16), lds0 + S::OFF_Q + j * 1024);
     if (FP4 && wave == 1) {
         // Hi * SB scale bytes (a multiple of 4, at most 512), 256 bytes a copy
@@ -330,7 +337,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     if constexpr (!FP4) {
         // q_hat = E8M0_B32 round trip of the raw q, one 32-value block per thread
         // and step, in place; padded heads (h >= Hi) become zero rows
-        for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += SCORE_WAVES * 64) {
+        for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += S::NW * 64) {
             const int h = blk / (DI / 32);
             const int c = blk - h * (DI / 32);
             u32x4* qb = reinterpret_cast<u32x4*>(qh_l + h * S::QS + c * 64);
@@ -462,16 +469,16 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
     if (KPT == 0) {
         // ---- flush this workgroup's keys (and scores) with coalesced stores
         uint16_t* kout = keys + qi * n_c + row0;
-        for (int64_t i = threadIdx.x; i < nrows; i += SCORE_WAVES * 64) kout[i] = keys_l[i];
+        for (int64_t i = threadIdx.x; i < nrows; i += S::NW * 64) kout[i] = keys_l[i];
         if (scores) {
             uint16_t* sout = scores + qi * n_c + row0;
-            for (int64_t i = threadIdx.x; i < nrows; i += SCORE_WAVES * 64) sout[i] = sc_l[i];
+            for (int64_t i = threadIdx.x; i < nrows; i += S::NW * 64) sout[i] = sc_l[i];
         }
     } else {
         // ---- fused top-K over the query's keys in LDS (row0 == 0, nrows == vis > K)
         constexpr int KP = KPT > 0 ? KPT : 8;
-        __shared__ uint32_t red[2][SCORE_WAVES];
-        __shared__ uint32_t tot[SCORE_WAVES];
+        __shared__ uint32_t red[2][S::NW];
+        __shared__ uint32_t tot[S::NW];
         const int64_t s0 = (int64_t)threadIdx.x * KP;
         uint32_t key[KP];
 #pragma unroll
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(SCORE_WAVES * 64) void index_score_kernel(
         }
 #pragma unroll
         for (int j = 0; j < KP; ++j) key[j] = (s0 + j < nrows) ? key[j] : 0u;
-        topk_select<KP, SCORE_WAVES>(key, s0, K, offset, idx + qi * ld + col0, red, tot);
+        topk_select<KP, S::NW>(key, s0, K, offset, idx + qi * ld + col0, red, tot);
     }
 }
 
@@ -588,7 +595,7 @@ int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* key
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_index_scores_topk: ") + hipGetErrorString(e));
     }
-    index_score_kernel<MT, DI, KPT, FP4><<<dim3((unsigned)(a.nq * nsplit)), dim3(SCORE_WAVES * 64), lds, a.s>>>(
+    index_score_kernel<MT, DI, KPT, FP4><<<dim3((unsigned)(a.nq * nsplit)), dim3(score_waves(FP4) * 64), lds, a.s>>>(
         a.q, a.q_scales, a.k, a.k_scales, a.w, a.m, a.Hi, a.n_c, a.ratio, a.start_pos, rows_per_wg, nsplit, keys,
         a.scores, a.K, a.offset, a.idx, a.ld, a.col0);
     return SCKV_OK;
@@ -599,13 +606,19 @@ int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* key
 template <int MT, int DI, bool FP4>
 int launch_fused(const IndexArgs& a) {
     const int rows = (int)((a.n_c + 127) / 128 * 128);
-    const int need = (rows + SCORE_WAVES * 64 - 1) / (SCORE_WAVES * 64);
+    const int nth = score_waves(FP4) * 64;
+    const int need = (rows + nth - 1) / nth;
 #define SCKV_FUSED(KPT)                                                                           \
     (score_lds_bytes<MT, DI, KPT, FP4>(rows, false) > 160 * 1024 ? SCKV_EUNSUPPORTED               \
                                                                   : launch_scores<MT, DI, KPT, FP4>(a, rows, 1, nullptr))
     if (need <= 8) return SCKV_FUSED(8);
+    if (need <= 16) return SCKV_FUSED(16);
     if (need <= 32) return SCKV_FUSED(32);
-    if (need <= 128) return SCKV_FUSED(128);
+    if constexpr (FP4) {  // 512 threads: 64 keys a thread cover n_c <= 32768
+        if (need <= 64) return SCKV_FUSED(64);
+    } else {
+        if (need <= 128) return SCKV_FUSED(128);
+    }
 #undef SCKV_FUSED
     return SCKV_EUNSUPPORTED;
 }
