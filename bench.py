@@ -114,11 +114,11 @@ def traffic_for(workload, B, call, kcache):
 # Library call -> the kernels it launches (demangled-name prefixes).
 CALL_KERNELS = {
     "quant_latent": ["quant_rows_kernel<0,"],
-    "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1,false>"],
+    "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1>"],
     "ring_write": ["ring_write_kernel"],
     "window_idx": ["window_idx_kernel"],
     "visible_idx": ["visible_idx_kernel"],
-    "index_scores_topk": ["index_score_kernel", "topk_kernel", "quant_pack_kernel<1,true>"],
+    "index_scores_topk": ["index_score_kernel", "topk_kernel"],
     "sparse_attn_sink": ["sparse_attn_kernel", "combine_kernel"],
 }
 

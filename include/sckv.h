@@ -184,9 +184,9 @@ int sckv_index_scores_topk(const void* q, const void* k, const float* w, int B, 
 /*
  * sckv_index_scores_topk_fp4 -- sckv_index_scores_topk with the k cache
  * stored packed (sckv_quant_pack, SCKV_FP4_E8M0_B32): the same scores, bit for
- * bit, and the same top-K lists.  q is still the raw bf16 q; its round trip
- * is packed into the workspace and both operands go through the gfx950 scaled
- * fp4 matrix cores (e2m1 x e2m1 with one E8M0 scale per 32 values, exact
+ * bit, and the same top-K lists.  q is still the raw bf16 q; each workgroup
+ * takes its query's round trip and packs it in on-chip memory, and both
+ * operands go through the gfx950 scaled fp4 matrix cores (e2m1 x e2m1 with one E8M0 scale per 32 values, exact
  * products; the exactness note above applies unchanged).
  *   k_codes   [B, n_c, Di/2] bytes, contiguous, 16-byte aligned
  *   k_scales  [B, n_c, Di/32] bytes, contiguous, 4-byte aligned

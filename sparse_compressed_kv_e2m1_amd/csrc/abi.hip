@@ -6,7 +6,7 @@
 namespace sckv {
 
 size_t index_workspace_bytes(int B, int64_t m, int64_t n_c);
-size_t index_fp4_workspace_bytes(int B, int64_t m, int Hi, int Di, int64_t n_c);
+size_t index_fp4_workspace_bytes(int B, int64_t m, int64_t n_c);
 size_t attn_workspace_bytes(int B, int64_t m, int H, int D, int64_t T);
 
 namespace {
@@ -32,7 +32,7 @@ extern "C" size_t sckv_workspace_bytes(int op, int B, int64_t m, int H, int D, i
     if (B < 0 || m < 0 || H <= 0 || D <= 0 || n < 0) return (size_t)-1;
     if (op == SCKV_OP_INDEX_SCORES_TOPK) return sckv::index_workspace_bytes(B, m, n);
     if (op == SCKV_OP_SPARSE_ATTN_SINK) return sckv::attn_workspace_bytes(B, m, H, D, n);
-    if (op == SCKV_OP_INDEX_SCORES_TOPK_FP4) return sckv::index_fp4_workspace_bytes(B, m, H, D, n);
+    if (op == SCKV_OP_INDEX_SCORES_TOPK_FP4) return sckv::index_fp4_workspace_bytes(B, m, n);
     return (size_t)-1;
 }
 

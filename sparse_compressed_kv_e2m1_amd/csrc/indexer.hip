@@ -166,7 +166,7 @@ struct ScoreShape {
     static constexpr int CT = 32 * ROWB;               // bytes of a 32-row tile's rows
     static constexpr int TILE = CT + 32 * SB;          // ... plus its scale bytes
     static constexpr int NINST = CT / 1024 + (FP4 ? 1 : 0);  // copies per tile (the last one: scales)
-    static constexpr int NST = NST_ > 0 ? NST_ : (FP4 ? (TILE >= 4096 ? 4 : 8) : ((TILE >= 16384) ? 1 : 4));  // tiles per wave in the ring
+    static constexpr int NST = NST_ > 0 ? NST_ : (FP4 ? (TILE >= 4096 ? 3 : 8) : ((TILE >= 16384) ? 1 : 4));  // tiles per wave in the ring
     static constexpr int PD = NST - 1;                 // tiles requested ahead of the one used
     static constexpr int CPR = ROWB / 16;              // 16-byte chunks per row
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // bf16 chunk swizzle mask
@@ -176,11 +176,12 @@ struct ScoreShape {
     static constexpr int OFF_Q = NW * NST * TILE;
     static constexpr int OFF_QS = OFF_Q + HP * QS;     // fp4: q scale bytes [HP][SB]
     static constexpr int OFF_W = OFF_QS + HP * SB;     // 64 f32 head weights
+    static constexpr int OFF_QR = OFF_W + 64 * 4;      // fp4: the raw bf16 q rows [HP][DI]
     // keys (then scores) reuse the q / w space once q_hat and the weights sit
     // in registers
     static constexpr int OFF_KEYS = OFF_Q;
     static constexpr size_t lds_bytes(int rows_per_wg, bool with_scores) {
-        const size_t qw = (size_t)HP * QS + (size_t)HP * SB + 64 * 4;
+        const size_t qw = (size_t)HP * QS + (size_t)HP * SB + 64 * 4 + (FP4 ? (size_t)HP * DI * 2 : 0);
         const size_t ks = (size_t)rows_per_wg * 2 * (with_scores ? 2 : 1);
         return (size_t)OFF_Q + (qw > ks ? qw : ks);
     }
@@ -225,12 +226,13 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32
 // KPT == 0: scores of a row range, ordered keys flushed to `keys` for the
 // top-k kernel.  KPT > 0 (fused, one workgroup per query, no split): the
 // whole query's keys stay in LDS and the workgroup selects its top-K itself.
-// FP4: k arrives as codes [n_c][DI/2] and scale bytes [n_c][DI/32], and q as
-// the already round-tripped, packed q_hat (codes [Hi][DI/2], scales
-// [Hi][DI/32] per query); otherwise k is bf16 [n_c][DI] and q the raw bf16 q.
+// q is the raw bf16 q [Hi][DI] of each query in both forms; the workgroup
+// takes its round trip in LDS.  FP4: k arrives as codes [n_c][DI/2] and
+// scale bytes [n_c][DI/32], and q_hat is packed the same way in LDS;
+// otherwise k is bf16 [n_c][DI].
 template <int MT, int DI, int KPT, bool FP4>
 __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
-    const void* __restrict__ q, const void* __restrict__ q_scales, const void* __restrict__ k,
+    const void* __restrict__ q, const void* __restrict__ k,
     const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
     int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
     int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0) {
@@ -308,17 +310,12 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
     // ---- prologue.  q and the head weights come in by asynchronous copies, this
     // wave's first k tiles are requested right behind them.  No ordinary
     // global load is issued in this kernel, so every vmcnt wait is explicit.
-    const int qbytes = Hi * S::QS;
+    // the raw bf16 q rows (fp4: into their own region, to be packed there)
+    const int qbytes = Hi * DI * 2;
+    const uint32_t qdst = lds0 + (FP4 ? S::OFF_QR : S::OFF_Q);
     const unsigned char* qrow = reinterpret_cast<const unsigned char*>(q) + qi * (int64_t)qbytes;
     for (int j = wave; j * 1024 < qbytes; j += S::NW)
-        if (j * 1024 + lane * 16 < qbytes) dma16_s(qrow, (uint32_t)(j * 1024 + lane * 16), lds0 + S::OFF_Q + j * 1024);
-    if (FP4 && wave == 1) {
-        // Hi * SB scale bytes (a multiple of 4, at most 512), 256 bytes a copy
-        const uint8_t* qs = reinterpret_cast<const uint8_t*>(q_scales) + qi * (int64_t)(Hi * S::SB);
-        for (int j = 0; j * 256 < Hi * S::SB; ++j)
-            if (j * 256 + lane * 4 < Hi * S::SB)
-                dma4_s(qs, (uint32_t)(j * 256 + lane * 4), lds0 + S::OFF_QS + (uint32_t)(j * 256));
-    }
+        if (j * 1024 + lane * 16 < qbytes) dma16_s(qrow, (uint32_t)(j * 1024 + lane * 16), qdst + j * 1024);
     if (wave == 0 && lane < Hi) dma4_s(w + qi * (int64_t)Hi, (uint32_t)lane * 4u, lds0 + S::OFF_W);
 #pragma unroll
     for (int i = 0; i < S::PD; ++i)
@@ -373,6 +370,44 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
                 qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + (lane & 31)) * S::QS +
                                                               (ks * 16 + (lane >> 5) * 8) * 2);
     } else {
+        // q_hat = E8M0_B32 round trip of the raw q, packed: one 32-value block per
+        // thread and step (codes of values 2j, 2j+1 in byte j, low nibble first;
+        // the block's E8M0 byte); padded heads (h >= Hi) are never read
+        const unsigned char* qr_l = lds + S::OFF_QR;
+        uint8_t* qs_w = lds + S::OFF_QS;
+        for (int blk = threadIdx.x; blk < Hi * (DI / 32); blk += S::NW * 64) {
+            const int h = blk / (DI / 32);
+            const int c = blk - h * (DI / 32);
+            const u32x4* qb = reinterpret_cast<const u32x4*>(qr_l + h * DI * 2 + c * 64);
+            u32x4 raw[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raw[i] = qb[i];
+            float amax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] & 0xffffu)));
+                    amax = fmaxf(amax, fabsf(bf16_bits_to_f32(raw[i][e] >> 16)));
+                }
+            const float sc = block_scale<SCKV_FP4_E8M0_B32>(amax);
+            const float inv_s = pow2_reciprocal(sc);
+            u32x4 cw;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t word = 0;  // the 8 codes of raw[i] (values 8i .. 8i+7)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_bits_to_f32(raw[i][e] & 0xffffu), hi = bf16_bits_to_f32(raw[i][e] >> 16);
+                    word |= e2m1_code(e2m1_round_mag(fminf(fabsf(lo) * inv_s, 6.0f)), lo) << (8 * e);
+                    word |= e2m1_code(e2m1_round_mag(fminf(fabsf(hi) * inv_s, 6.0f)), hi) << (8 * e + 4);
+                }
+                cw[i] = word;
+            }
+            *reinterpret_cast<u32x4*>(qh_l + h * S::QS + c * 16) = cw;
+            qs_w[h * S::SB + c] = (uint8_t)scale_byte<SCKV_FP4_E8M0_B32>(sc);
+        }
+        __syncthreads();
         const uint8_t* qs_l = lds + S::OFF_QS;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -565,11 +600,10 @@ size_t score_lds_bytes(int rows_per_wg, bool with_scores) {
     return Sh::lds_bytes(rows_per_wg, with_scores);
 }
 
-// Operands of one indexer call: q (raw bf16, or packed q_hat codes with
-// q_scales), k (bf16 rows, or codes with k_scales).
+// Operands of one indexer call: q (raw bf16), k (bf16 rows, or codes with
+// k_scales).
 struct IndexArgs {
     const void* q;
-    const void* q_scales;
     const void* k;
     const uint8_t* k_scales;
     const float* w;
@@ -596,7 +630,7 @@ int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* key
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_index_scores_topk: ") + hipGetErrorString(e));
     }
     index_score_kernel<MT, DI, KPT, FP4><<<dim3((unsigned)(a.nq * nsplit)), dim3(score_waves(FP4) * 64), lds, a.s>>>(
-        a.q, a.q_scales, a.k, a.k_scales, a.w, a.m, a.Hi, a.n_c, a.ratio, a.start_pos, rows_per_wg, nsplit, keys,
+        a.q, a.k, a.k_scales, a.w, a.m, a.Hi, a.n_c, a.ratio, a.start_pos, rows_per_wg, nsplit, keys,
         a.scores, a.K, a.offset, a.idx, a.ld, a.col0);
     return SCKV_OK;
 }
@@ -701,10 +735,9 @@ size_t index_workspace_bytes(int B, int64_t m, int64_t n_c) {
     return align256((size_t)B * (size_t)m * (size_t)n_c * 2u);
 }
 
-size_t index_fp4_workspace_bytes(int B, int64_t m, int Hi, int Di, int64_t n_c) {
-    // the keys, then q_hat packed: codes [B*m*Hi][Di/2] and scales [B*m*Hi][Di/32]
-    const size_t rows = (size_t)B * (size_t)m * (size_t)Hi;
-    return index_workspace_bytes(B, m, n_c) + align256(rows * (size_t)(Di / 2)) + align256(rows * (size_t)(Di / 32));
+size_t index_fp4_workspace_bytes(int B, int64_t m, int64_t n_c) {
+    // the keys only: q_hat is packed inside the score kernel
+    return index_workspace_bytes(B, m, n_c);
 }
 
 }  // namespace sckv
@@ -733,7 +766,7 @@ extern "C" int sckv_index_scores_topk(const void* q, const void* k, const float*
     if (scores && (uintptr_t)scores % 2) return fail(SCKV_EINVAL, "sckv_index_scores_topk: misaligned scores");
     if (!ws || ws_bytes < index_workspace_bytes(B, m, n_c))
         return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk: workspace too small");
-    const IndexArgs a{q, nullptr, k, nullptr, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx, ld, col0,
+    const IndexArgs a{q, k, nullptr, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx, ld, col0,
                       (uint16_t*)scores, s};
     return dispatch_index<false>(Di, Hi > 32, a, (uint16_t*)ws);
 }
@@ -760,17 +793,9 @@ extern "C" int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, co
     if ((uintptr_t)w % 4 || (uintptr_t)idx % 4)
         return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: misaligned w/idx");
     if (scores && (uintptr_t)scores % 2) return fail(SCKV_EINVAL, "sckv_index_scores_topk_fp4: misaligned scores");
-    if (!ws || ws_bytes < index_fp4_workspace_bytes(B, m, Hi, Di, n_c))
+    if (!ws || ws_bytes < index_fp4_workspace_bytes(B, m, n_c))
         return fail(SCKV_EWORKSPACE, "sckv_index_scores_topk_fp4: workspace too small");
-    // q_hat of every query, packed, into the workspace (one pass over q)
-    unsigned char* wsb = (unsigned char*)ws;
-    uint16_t* keys = (uint16_t*)wsb;
-    unsigned char* qc = wsb + index_workspace_bytes(B, m, n_c);
-    const size_t qrows = (size_t)nq * (size_t)Hi;
-    unsigned char* qsc = qc + align256(qrows * (size_t)(Di / 2));
-    int rc = quant_pack_q_impl(q, Di, qc, Di / 2, qsc, Di / 32, (int64_t)qrows, Di, SCKV_FP4_E8M0_B32, stream);
-    if (rc) return rc;
-    const IndexArgs a{qc, qsc, k_codes, (const uint8_t*)k_scales, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx,
+    const IndexArgs a{q, k_codes, (const uint8_t*)k_scales, w, nq, m, Hi, n_c, ratio, start_pos, K, offset, idx,
                       ld, col0, (uint16_t*)scores, s};
-    return dispatch_index<true>(Di, Hi > 32, a, keys);
+    return dispatch_index<true>(Di, Hi > 32, a, (uint16_t*)ws);
 }

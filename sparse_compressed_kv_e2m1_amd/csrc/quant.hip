@@ -113,9 +113,8 @@ int quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t ro
 }
 
 // ---- packed storage: 4-bit codes (two a byte, the even element low) and one
-// scale byte per block; one lane per block, as above.  FOR_Q only names the
-// instance the fp4 indexer launches on its q (so profiles tell the two apart).
-template <int MODE, bool FOR_Q>
+// scale byte per block; one lane per block, as above.
+template <int MODE>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     uint8_t* __restrict__ codes, int64_t ldc,
                                                                     uint8_t* __restrict__ scales, int64_t lds,
@@ -176,7 +175,6 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_
 
 }  // namespace
 
-template <bool FOR_Q>
 int quant_pack_launch(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
                       int64_t cols, int mode, void* stream) {
     if (mode != SCKV_FP4_E4M3_B16 && mode != SCKV_FP4_E8M0_B32) return fail(SCKV_EINVAL, "sckv_quant_pack: bad mode");
@@ -200,23 +198,14 @@ int quant_pack_launch(const void* x, int64_t ldx, void* codes, int64_t ldc, void
     const bool vec = (xs % 16 == 0) && (ldx % 8 == 0) && (cs % (block / 2) == 0) && (ldc % (block / 2) == 0);
     hipStream_t s = (hipStream_t)stream;
     if (mode == SCKV_FP4_E4M3_B16)
-        quant_pack_kernel<SCKV_FP4_E4M3_B16, FOR_Q><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+        quant_pack_kernel<SCKV_FP4_E4M3_B16><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
             (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec);
     else
-        quant_pack_kernel<SCKV_FP4_E8M0_B32, FOR_Q><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+        quant_pack_kernel<SCKV_FP4_E8M0_B32><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
             (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec);
     return check_launch("sckv_quant_pack");
 }
 
-int quant_pack_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
-                    int64_t cols, int mode, void* stream) {
-    return quant_pack_launch<false>(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
-}
-
-int quant_pack_q_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
-                      int64_t cols, int mode, void* stream) {
-    return quant_pack_launch<true>(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
-}
 
 }  // namespace sckv
 
@@ -237,5 +226,5 @@ extern "C" int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy,
 
 extern "C" int sckv_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds,
                                int64_t rows, int64_t cols, int mode, void* stream) {
-    return sckv::quant_pack_impl(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
+    return sckv::quant_pack_launch(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
 }

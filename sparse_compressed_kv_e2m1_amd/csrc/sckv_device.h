@@ -158,11 +158,6 @@ struct QuantMode<SCKV_FP4_E8M0_B32> {
 // ---------------------------------------------------------------- host side
 
 void set_error(const std::string& msg);
-// the packed round trip of sckv_quant_pack (also used on q inside the fp4 indexer)
-int quant_pack_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
-                    int64_t cols, int mode, void* stream);
-int quant_pack_q_impl(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
-                      int64_t cols, int mode, void* stream);
 int fail(int code, const std::string& msg);
 int check_launch(const char* what);
 
