@@ -214,6 +214,8 @@ int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, const void* k
  *   q      [B, m, H, D] bf16
  *   rows_a [B, ra, D] bf16     rows_b [B, rb, D] bf16 (NULL allowed when rb == 0)
  *   idx    [B, m, T] int32     sink [H] f32     out [B, m, H, D] bf16
+ *   q, rows_a, rows_b and out 16-byte aligned, idx and sink 4-byte aligned
+ *   (else SCKV_EINVAL)
  *   ws     device workspace of at least
  *          sckv_workspace_bytes(SCKV_OP_SPARSE_ATTN_SINK, B, m, H, D, T).
  * Supported: H <= 64, D in {64, 128, 256, 512}, 1 <= T <= 65536.

@@ -56,22 +56,44 @@ struct AttnShape {
     static constexpr int RS = 2 * D + 32;
     static constexpr int STAGE = CHUNK * RS;
     static constexpr int OFF_IDX = 2 * NST * STAGE;
-    static constexpr size_t LDS_BYTES = (size_t)OFF_IDX + (size_t)MAX_CPS * CHUNK * 4;
-    // the second set's O (HP rows of D + 4 floats) and (max, sum) reuse the stages
-    static constexpr int OS = D + 4;
-    static_assert((size_t)HP * OS * 4 + HP * 8 <= (size_t)OFF_IDX, "merge space");
+    static constexpr int OFF_FLAG = OFF_IDX + MAX_CPS * CHUNK * 4;  // one byte per chunk: names a valid row
+    static constexpr size_t LDS_BYTES = (size_t)OFF_FLAG + MAX_CPS;
+    static constexpr int IPT = MAX_CPS * CHUNK / (WAVES * 64);  // index entries a thread stages
+    // the exchanged halves of O ([D][HP] f32) reuse the stages and both sets'
+    // (max, sum) the index slice; afterwards each wave stages its 16 x D/2
+    // output block (bf16, or f32 partials) in the stages
+    static_assert((size_t)D * HP * 4 <= (size_t)OFF_IDX && 2 * HP * 8 <= MAX_CPS * CHUNK * 4, "merge space");
+    static_assert((size_t)WAVES * 16 * (D / 2) * 4 <= (size_t)OFF_IDX, "output staging");
     static_assert(RPW % 4 == 0 && (RS % 16) == 0, "shape");
 };
 
 // max / sum over the four lanes l, l^16, l^32, l^48 (same head in the MFMA
-// result layout)
-__device__ __forceinline__ float max4x16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 16, 64));
-    return fmaxf(v, __shfl_xor(v, 32, 64));
+// result layout), on the gfx950 lane swaps (v_permlane16_swap /
+// v_permlane32_swap: with both operands v, the pair returned is (v of the
+// lower lane, v of the upper lane) of {l, l^16} or {l, l^32}), so every lane
+// of a group adds the same two values in the same order
+__device__ __forceinline__ float pair_max16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float sum4x16(float v) {
-    v += __shfl_xor(v, 16, 64);
-    return v + __shfl_xor(v, 32, 64);
+__device__ __forceinline__ float pair_sum16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max4x16(float v) { return pair_max32(pair_max16(v)); }
+__device__ __forceinline__ float sum4x16(float v) { return pair_sum32(pair_sum16(v)); }
+
+// the value of lane l ^ 1 (DPP quad permute 1, 0, 3, 2)
+__device__ __forceinline__ float lane_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
 
 template <int D, int NHW>
@@ -100,44 +122,69 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     const int32_t* idx_q = idx + qi * (int64_t)T;
     const uint16_t* qrow = q + qi * (int64_t)H * D;
 
-    // ---- Q^T in B layout: head 16 hw + l16, dims ks*32 + g*8 + 0..7
-    const int head = 16 * hw + l16;  // the head this lane follows in the softmax
-    bf16x8 qb[S::KS];
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks)
-        qb[ks] = as_bf16x8((head < H) ? load16(qrow + (int64_t)head * D + ks * 32 + g * 8) : u32x4{0, 0, 0, 0});
-    float m_run = (head < H) ? sink[head] * LOG2E : 0.0f;  // base-2 running max, starting at the sink
-    // e^(sink - M) at M = sink, counted once: by the first set of an unsplit query
-    float l_run = (nsplit == 1 && set == 0) ? 1.0f : 0.0f;
-
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int c_begin = split * chunks_per_split;
     int c_end = c_begin + chunks_per_split;
     c_end = c_end < nchunks ? c_end : nchunks;
     const int nch = c_end - c_begin;
-    {
-        // this workgroup's slice of the index list, staged once in LDS
-        const int e0 = c_begin * CHUNK;
-        const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
-        for (int i = threadIdx.x; i < nch * CHUNK; i += NTH) idx_l[i] = (i < ne) ? idx_q[e0 + i] : -1;
+    const uint32_t rab = (uint32_t)(ra + rb);
+    // this workgroup's slice of the index list: loaded first (the first row
+    // copies need it), q right behind it, so that q's latency overlaps the
+    // index staging and the first copies
+    const int e0 = c_begin * CHUNK;
+    const int ne = (c_end * CHUNK < T ? c_end * CHUNK : T) - e0;
+    // (every load address is clamped into its array rather than branched
+    // around, so the loads issue back to back and only their consumers wait)
+    int32_t iv_reg[S::IPT];
+#pragma unroll
+    for (int k = 0; k < S::IPT; ++k) {
+        const int i = (int)threadIdx.x + k * NTH;
+        iv_reg[k] = idx_q[e0 + (i < ne ? i : ne - 1)];
     }
-    // Every ordinary global load above is complete before the first row copy is
-    // issued, so no compiler-placed wait inside the loop can stall on the copies.
-    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");  // keep every index load ahead of the q loads
+
+    // ---- Q^T in B layout: head 16 hw + l16, dims ks*32 + g*8 + 0..7.  Lanes
+    // of padding heads (head >= H) follow head H - 1; nothing of theirs is
+    // written out.
+    const int head = 16 * hw + l16;  // the head this lane follows in the softmax
+    const int hq = head < H ? head : H - 1;
+    bf16x8 qb[S::KS];
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) qb[ks] = as_bf16x8(load16(qrow + (int64_t)hq * D + ks * 32 + g * 8));
+    // the sink logits of the wave's 16 heads by uniform (scalar) loads, lane
+    // l16 keeping head 16 hw + l16's
+    float sk = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float si = sink[(16 * hw + i) < H ? (16 * hw + i) : H - 1];
+        sk = (l16 == i) ? si : sk;
+    }
+    float m_run = sk * LOG2E;  // base-2 running max, starting at the sink
+    // e^(sink - M) at M = sink, counted once: by the first set of an unsplit query
+    float l_run = (nsplit == 1 && set == 0) ? 1.0f : 0.0f;
+
+    // the index slice into LDS, with one flag per chunk that names a valid row
+    // (a ballot covers 64 entries, two chunks)
+    uint8_t* flag_l = lds + S::OFF_FLAG;
+#pragma unroll
+    for (int k = 0; k < S::IPT; ++k) {
+        const int i = (int)threadIdx.x + k * NTH;
+        const int32_t v = (i < ne) ? iv_reg[k] : -1;
+        if (i < nch * CHUNK) idx_l[i] = v;
+        const uint64_t bal = __ballot(i < nch * CHUNK && (uint32_t)v < rab);
+        const int c0 = (k * NTH + wave * 64) / CHUNK;
+        if (lane == 0) {
+            flag_l[c0] = (uint8_t)((bal & 0xffffffffull) != 0);
+            flag_l[c0 + 1] = (uint8_t)((bal >> 32) != 0);
+        }
+    }
     __syncthreads();
 
     // Non-empty chunks as a bitmap (uniform): bit j set when chunk c_begin + j
     // names at least one valid row.  Empty chunks are neither copied nor
     // computed.  Non-empty chunk number k goes to set k % 2.
-    const uint32_t rab = (uint32_t)(ra + rb);
-    uint64_t todo = 0;
-    for (int j = 0; j < nch; j += 2) {
-        const int jj = j + (lane >> 5);
-        const bool v = (jj < nch) && ((uint32_t)idx_l[jj * CHUNK + (lane & 31)] < rab);
-        const uint64_t bal = __ballot(v);
-        todo |= (uint64_t)((bal & 0xffffffffull) != 0) << j;
-        todo |= (uint64_t)((bal >> 32) != 0) << (j + 1);
-    }
+    static_assert(MAX_CPS == 64, "one flag per lane");
+    const uint64_t todo = __ballot(lane < nch && flag_l[lane] != 0);
     const int n = __builtin_popcountll(todo);
     const int n_own = (n > set) ? (n - set + 1) / 2 : 0;  // chunks of this wave's set
     const int n_it = (n + 1) / 2;                         // iterations (same in every wave)
@@ -280,68 +327,110 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
         resume = true;
     }
 
-    // ---- epilogue: the second set hands (max, sum, O) to the first through LDS
+    // ---- epilogue: the two sets merge their (max, sum, O) through LDS, each
+    // finishing half of the columns: set 0 tiles nt < NT/2, set 1 the rest.
+    // The exchanged tiles sit column-major, [D][HP] floats, a lane's four
+    // rows as one 16-byte piece whose place in the column is swizzled by the
+    // column (the 16 lanes of a group then cover every bank once).
+    constexpr int NH = S::NT / 2;
+    constexpr int HQ = S::HP / 4;  // 16-byte pieces of a column
     __syncthreads();  // all stages idle
-    float* mo = reinterpret_cast<float*>(lds);           // [HP][OS]
-    float* ml = reinterpret_cast<float*>(lds) + S::HP * S::OS;  // [HP][2]
-    if (set == 1) {
+    unsigned char* xo = lds;                                     // [D][HP] f32
+    float* ml = reinterpret_cast<float*>(lds + S::OFF_IDX);     // [2][HP][2] (the index slice is done)
+    auto xo_at = [&](int col) -> unsigned char* {
+        return xo + (size_t)col * S::HP * 4 + (size_t)(((4 * hw + g) ^ (col % HQ)) * 16);
+    };
 #pragma unroll
-        for (int nt = 0; nt < S::NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mo[(16 * hw + g * 4 + i) * S::OS + nt * 16 + l16] = o[nt][i];
-        if (g == 0) {
-            ml[head * 2 + 0] = m_run;
-            ml[head * 2 + 1] = l_run;
-        }
+    for (int k = 0; k < NH; ++k) {
+        const int nt = (set == 0) ? NH + k : k;  // the other set's tiles
+        *reinterpret_cast<f32x4*>(xo_at(nt * 16 + l16)) = o[nt];
+    }
+    if (g == 0) {
+        ml[(set * S::HP + head) * 2 + 0] = m_run;
+        ml[(set * S::HP + head) * 2 + 1] = l_run;
     }
     __syncthreads();
-    if (set == 0) {
-        const float m1 = ml[head * 2 + 0], l1 = ml[head * 2 + 1];
-        const float M = fmaxf(m_run, m1);
-        const float a0 = __builtin_amdgcn_exp2f(m_run - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
-        const float L = l_run * a0 + l1 * a1;
-        // per O row (head 16 hw + g*4 + i): the factors from lane g*4 + i
-        float f0[4], f1[4], Li[4], Mi[4];
+    const float m1 = ml[((1 - set) * S::HP + head) * 2 + 0], l1 = ml[((1 - set) * S::HP + head) * 2 + 1];
+    const float M = fmaxf(m_run, m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run - M), a1 = __builtin_amdgcn_exp2f(m1 - M);
+    const float L = l_run * a0 + l1 * a1;
+    // per O row (head 16 hw + g*4 + i): the factors from lane g*4 + i
+    float f0[4], f1[4], fin[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f0[i] = __shfl(a0, g * 4 + i, 64);
-            f1[i] = __shfl(a1, g * 4 + i, 64);
-            Li[i] = __shfl(L, g * 4 + i, 64);
-            Mi[i] = __shfl(M, g * 4 + i, 64);
+    for (int i = 0; i < 4; ++i) {
+        f0[i] = __shfl(a0, g * 4 + i, 64);
+        f1[i] = __shfl(a1, g * 4 + i, 64);
+        fin[i] = (nsplit == 1) ? 1.0f / __shfl(L, g * 4 + i, 64) : 1.0f;
+    }
+    float fo[NH][4];  // this wave's finished tiles
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+        const int nt = (set == 0) ? k : NH + k;
+        const f32x4 ot = *reinterpret_cast<const f32x4*>(xo_at(nt * 16 + l16));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fo[k][i] = (o[nt][i] * f0[i] + ot[i] * f1[i]) * fin[i];
+    }
+    __syncthreads();  // every read of the exchanged tiles is done
+    // stage the 16 x D/2 block in LDS (wave-private space), then write it out
+    // 16 bytes a lane
+    const int nrow = (H - 16 * hw) < 16 ? (H - 16 * hw) : 16;  // rows that are real heads
+    const int col0 = set * (D / 2);
+    if (nsplit == 1) {
+        // bf16 rows of D bytes at a pitch of D + 32 (the 8 rows one write
+        // touches fall on distinct banks); lanes l16 and l16 ^ 1 pair up
+        // adjacent columns, so that each writes two values (4 bytes)
+        constexpr int P = D + 32;
+        unsigned char* stg = lds + (size_t)wave * (16 * P);
+        const bool odd = (l16 & 1) != 0;
+#pragma unroll
+        for (int k = 0; k < NH; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float other = lane_xor1(odd ? fo[k][i] : fo[k][i + 1]);
+                const f32x2 pr = odd ? f32x2{other, fo[k][i + 1]} : f32x2{fo[k][i], other};
+                const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                const int r = g * 4 + i + (odd ? 1 : 0);
+                const int c = k * 16 + (l16 & ~1);
+                *reinterpret_cast<uint32_t*>(stg + r * P + c * 2) = pb;
+            }
+        wave_lds_sync();
+        constexpr int CPRW = D / 16;  // 16-byte pieces of a half row
+#pragma unroll
+        for (int k = 0; k < 16 * CPRW / 64; ++k) {
+            const int piece = k * 64 + lane;
+            const int r = piece / CPRW, c = piece % CPRW;
+            if (r < nrow) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * P + c * 16);
+                store16(reinterpret_cast<unsigned char*>(out + (qi * H + 16 * hw + r) * (int64_t)D + col0) + c * 16, v);
+            }
         }
-        if (nsplit == 1) {
-            float inv[4];
+    } else {
+        // f32 partial half rows (2 D bytes each, 16-byte pieces swizzled by
+        // the row), then (max, sum) per head
+        constexpr int CPRW = 2 * D / 16;  // 16-byte pieces of a half row
+        constexpr int SWR = CPRW < 16 ? CPRW : 16;
+        unsigned char* stg = lds + (size_t)wave * (16 * 2 * D);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) inv[i] = 1.0f / Li[i];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = 16 * hw + g * 4 + i;
-                if (h < H) {
-                    uint16_t* orow = out + (qi * H + h) * (int64_t)D;
-                    const float* prow = mo + h * S::OS;
-#pragma unroll
-                    for (int nt = 0; nt < S::NT; ++nt) {
-                        const float v = (o[nt][i] * f0[i] + prow[nt * 16 + l16] * f1[i]) * inv[i];
-                        orow[nt * 16 + l16] = (uint16_t)f32_to_bf16_bits(v);
-                    }
-                }
-            }
-        } else {
-            const int64_t pbase = (qi * nsplit + split) * (int64_t)H;
+        for (int k = 0; k < NH; ++k)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int h = 16 * hw + g * 4 + i;
-                if (h < H) {
-                    float* orow = part_o + (pbase + h) * D;
-                    const float* prow = mo + h * S::OS;
-#pragma unroll
-                    for (int nt = 0; nt < S::NT; ++nt) orow[nt * 16 + l16] = o[nt][i] * f0[i] + prow[nt * 16 + l16] * f1[i];
-                    if (l16 == 0) {
-                        part_ml[(pbase + h) * 2 + 0] = Mi[i];
-                        part_ml[(pbase + h) * 2 + 1] = Li[i];
-                    }
-                }
+                const int r = g * 4 + i, c = k * 16 + l16;
+                *reinterpret_cast<float*>(stg + r * (2 * D) + (((c >> 2) ^ (r % SWR)) << 4) + (c & 3) * 4) = fo[k][i];
             }
+        wave_lds_sync();
+        const int64_t pbase = (qi * nsplit + split) * (int64_t)H + 16 * hw;
+#pragma unroll
+        for (int k = 0; k < 16 * CPRW / 64; ++k) {
+            const int piece = k * 64 + lane;
+            const int r = piece / CPRW, c = piece % CPRW;
+            if (r < nrow) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * (2 * D) + ((c ^ (r % SWR)) << 4));
+                store16(reinterpret_cast<unsigned char*>(part_o + (pbase + r) * D + col0) + c * 16, v);
+            }
+        }
+        if (set == 0 && g == 0 && l16 < nrow) {
+            part_ml[(pbase + l16) * 2 + 0] = M;
+            part_ml[(pbase + l16) * 2 + 1] = L;
         }
     }
 }
@@ -445,9 +534,9 @@ extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t 
     if (T == 0) return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: T == 0");
     if (!q || !idx || !sink || !out || (ra > 0 && !rows_a) || (rb > 0 && !rows_b))
         return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: null pointer");
-    if ((uintptr_t)q % 16 || (uintptr_t)rows_a % 16 || (uintptr_t)rows_b % 16 || (uintptr_t)out % 2 ||
+    if ((uintptr_t)q % 16 || (uintptr_t)rows_a % 16 || (uintptr_t)rows_b % 16 || (uintptr_t)out % 16 ||
         (uintptr_t)idx % 4 || (uintptr_t)sink % 4)
-        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: q / rows must be 16-byte aligned");
+        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: q / rows / out must be 16-byte aligned");
     if (ra + rb > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: ra + rb >= 2^31");
     if (!(scale > 0.0f) || !(scale < INFINITY)) return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: bad scale");
     const int64_t nq = (int64_t)B * m;
