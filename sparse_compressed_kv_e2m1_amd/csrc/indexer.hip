@@ -462,14 +462,16 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
                 for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma_fp4(qc[mt][ks], qsc[mt][ks], kc, ksc, acc[mt]);
             }
         }
-        // r_h = fl32(w_h * relu(d_h)); relu maps every d <= 0 (and -0) to +0
+        // r_h = fl32(w_h * relu(d_h)); relu maps every d <= 0 (and -0) to +0:
+        // as a signed integer a float with the sign bit set is negative, so the
+        // integer max with 0 is that relu in one operation
         float v[MT * 16];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const float d = acc[mt][i];
-                v[mt * 16 + i] = wd[mt][i] * ((d > 0.0f) ? d : 0.0f);
+                const int db = __float_as_int(acc[mt][i]);
+                v[mt * 16 + i] = wd[mt][i] * __int_as_float(db > 0 ? db : 0);
             }
         // pairwise head sum, stride Hi/2 first (h and h + stride)
         if (MT == 2 && Hi > 32) {
@@ -485,8 +487,14 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
             for (int i = 0; i < 4; ++i) v[i] = v[i] + v[i + 4];
         }
         if (Hi > 4) {
+            // heads h and h + 4 sit in lanes l and l ^ 32: the lane swap hands
+            // both lanes (v of the lower lane, v of the upper lane)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = v[i] + shfl_xor32(v[i]);
+            for (int i = 0; i < 4; ++i) {
+                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i]), false,
+                                                                 false);
+                v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+            }
         }
         if (Hi > 2) {
             v[0] = v[0] + v[2];
