@@ -409,6 +409,40 @@ def test_index_scores_topk_fp4_bit_exact(sk, case):
             assert np.array_equal(got[b, t, col0:col0 + K], oracle.topk(sc[i], v, K, off)), (b, t)
 
 
+@pytest.mark.parametrize("B,n_c", [(2, 700), (192, 600)], ids=["split", "fused"])
+def test_index_scores_topk_fp4_extreme_q_scales(sk, B, n_c):
+    """q rows scaled by powers of two from 2^-140 (subnormal bf16) to 2^100:
+    the in-kernel q round trip and packing then meets every kind of block
+    scale, from the 2^-126 floor up."""
+    m, Hi, Di, K, ratio = 2, 64, 128, 64, 1
+    start_pos = n_c - m
+    rng = np.random.default_rng(4242 + B)
+    exps = rng.choice(np.array([-140, -128, -110, -60, -8, 0, 8, 60, 100]), size=(B, m, Hi, 1))
+    q = bits(bf16_of(rng.standard_normal((B, m, Hi, Di)) * np.exp2(exps)))
+    kraw = bits(bf16_of(rng.standard_normal((n_c, Di))))
+    kc, ks = oracle.pack(kraw.reshape(-1), oracle.E8M0_B32)
+    khat = oracle.quant(kraw.reshape(-1), oracle.E8M0_B32).reshape(n_c, Di)
+    codes = np.broadcast_to(kc.reshape(1, n_c, Di // 2), (B, n_c, Di // 2)).copy()
+    scl = np.broadcast_to(ks.reshape(1, n_c, Di // 32), (B, n_c, Di // 32)).copy()
+    w = (rng.standard_normal((B, m, Hi)) * (Hi * Di) ** -0.5).astype(np.float32)
+    idx = torch.full((B, m, K), -9, dtype=torch.int32, device="cuda")
+    scores = torch.zeros((B, m, n_c), dtype=torch.bfloat16, device="cuda") if B < 192 else None
+    say(f"fp4 indexer, extreme q scales, B={B} n_c={n_c}")
+    sk.sckv_index_scores_topk_fp4(from_bits(q, "cuda"), torch.from_numpy(codes).cuda(), torch.from_numpy(scl).cuda(),
+                                  torch.from_numpy(w).cuda(), B, m, Hi, Di, n_c, ratio, start_pos, K, 0, idx, K, 0,
+                                  scores=scores)
+    got = idx.cpu().numpy()
+    got_sc = bits(scores) if scores is not None else None
+    for b in sorted({0, B - 1, B // 2}):
+        sc, bad = oracle.index_scores(q[b], khat, w[b], start_pos, ratio)
+        assert bad == 0
+        for t in range(m):
+            v = oracle.visible(start_pos + t, ratio, n_c)
+            if got_sc is not None:
+                assert np.array_equal(got_sc[b, t, :v], sc[t, :v]), (b, t)
+            assert np.array_equal(got[b, t], oracle.topk(sc[t], v, K, 0)), (b, t)
+
+
 def test_index_topk_fp4_ties(sk):
     """Forced ties at the K-th place through the fp4 path (fused and split)."""
     n_c, Di, Hi, K = 500, 128, 4, 64
