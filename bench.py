@@ -67,6 +67,10 @@ def counts(w, B, call, kcache="bf16"):
         return {"bytes": B * min(m, win) * D * 4, "flops": 0, "bound": "hbm"}
     if call == "window_idx":
         return {"bytes": B * m * win * 4, "flops": 0, "bound": "hbm"}
+    if call == "decode_prepare":  # the four set-up calls of a decode step in one launch
+        return {"bytes": sum(counts(w, B, c, kcache)["bytes"]
+                             for c in ("quant_latent", "quant_index_k", "ring_write", "window_idx")),
+                "flops": 0, "bound": "hbm"}
     if call == "visible_idx":
         return {"bytes": B * m * w.K * 4, "flops": 0, "bound": "hbm"}
     if call == "index_scores_topk":
@@ -116,6 +120,7 @@ CALL_KERNELS = {
     "quant_latent": ["quant_rows_kernel<0,"],
     "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1>"],
     "ring_write": ["ring_write_kernel"],
+    "decode_prepare": ["decode_prepare_kernel"],
     "window_idx": ["window_idx_kernel"],
     "visible_idx": ["visible_idx_kernel"],
     "index_scores_topk": ["index_score_kernel", "topk_kernel"],

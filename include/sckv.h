@@ -136,6 +136,36 @@ int64_t sckv_rows_a_len(int win, int64_t m, int64_t start_pos);
 int sckv_window_idx(int B, int64_t m, int64_t start_pos, int win, int32_t* idx, int64_t ld, void* stream);
 
 /*
+ * sckv_decode_prepare -- the set-up calls of a decode step (m = 1, start_pos
+ * > 0) for B sequences in one launch (forward.rs AttnV41::forward: the fp4
+ * round trip of a completed latent group before its cache copy, the ring copy
+ * at slot start_pos mod win before attention, window_topk_idxs; compress.rs
+ * fp4_quant_e4m3_inplace, fp4_quant_e8m0_inplace).  The result is exactly
+ * that of, in any order (the four write disjoint memory):
+ *   sckv_quant_rows(lat_new, ld_lat_new, lat_dst, ld_lat_dst, B, D, SCKV_FP4_E4M3_B16)
+ *   sckv_quant_pack(k_new, ld_k_new, k_codes, ld_codes, k_scales, ld_scales, B, Di, SCKV_FP4_E8M0_B32)
+ *   sckv_ring_write(kv_new, ld_kv_new, ring, ld_ring, B, 1, start_pos, win, D)
+ *   sckv_window_idx(B, 1, start_pos, win, idx, ld_idx)
+ *   lat_new    [B] raw latent rows of D bf16, stride ld_lat_new (elements), or
+ *              NULL when no compressed row completes at this step (then
+ *              lat_dst is not touched)
+ *   lat_dst    the B destination rows in the latent cache, stride ld_lat_dst
+ *   k_new      [B] raw indexer k rows of Di bf16, stride ld_k_new, or NULL
+ *   k_codes    destination code rows (Di/2 bytes), stride ld_codes (bytes)
+ *   k_scales   destination scale bytes (Di/32), stride ld_scales (bytes)
+ *   kv_new     [B] new kv rows of D bf16, stride ld_kv_new
+ *   ring       [B, win, D] bf16, stride ld_ring per sequence (>= win*D)
+ *   idx        [B, 1, ld_idx] int32; columns 0 .. win-1 written
+ * D % 16 == 0, Di % 32 == 0; every row pointer 16-byte aligned and every
+ * stride a multiple of 16 bytes (ld_scales excepted), else SCKV_EINVAL.
+ */
+int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, int64_t ld_lat_dst,
+                        const void* k_new, int64_t ld_k_new, void* k_codes, int64_t ld_codes, void* k_scales,
+                        int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new, void* ring,
+                        int64_t ld_ring, int B, int D, int win, int64_t start_pos, int32_t* idx, int64_t ld_idx,
+                        void* stream);
+
+/*
  * sckv_visible_idx -- the compressed part of every query's index list when
  * every causally visible compressed row is attended (a layer without an
  * indexer): offset + j for j < V_p, then -1 up to K, where compressed row j is

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     SckvError,
     lib,
     sckv_abi_version,
+    sckv_decode_prepare,
     sckv_index_scores_topk,
     sckv_index_scores_topk_fp4,
     sckv_last_error,

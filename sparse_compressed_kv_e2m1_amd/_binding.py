@@ -44,6 +44,8 @@ def _load():
     L.sckv_quant_rows.argtypes = [vp, i64, vp, i64, i64, i64, i32, vp]
     L.sckv_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, vp]
     L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
+    L.sckv_decode_prepare.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i32,
+                                      i32, i64, vp, i64, vp]
     L.sckv_rows_a_len.argtypes = [i32, i64, i64]
     L.sckv_rows_a_len.restype = i64
     L.sckv_window_idx.argtypes = [i32, i64, i64, i32, vp, i64, vp]
@@ -59,7 +61,8 @@ def _load():
     L.sckv_last_error.argtypes = []
     L.sckv_last_error.restype = ctypes.c_char_p
     L.sckv_abi_version.argtypes = []
-    for name in ("sckv_quant", "sckv_quant_rows", "sckv_quant_pack", "sckv_ring_write", "sckv_window_idx",
+    for name in ("sckv_quant", "sckv_quant_rows", "sckv_quant_pack", "sckv_ring_write", "sckv_decode_prepare",
+                 "sckv_window_idx",
                  "sckv_visible_idx", "sckv_index_scores_topk", "sckv_index_scores_topk_fp4", "sckv_sparse_attn_sink",
                  "sckv_abi_version"):
         getattr(L, name).restype = ctypes.c_int
@@ -149,6 +152,26 @@ def sckv_ring_write(rows: torch.Tensor, rows_bstride: int, ring: torch.Tensor, r
             raise ValueError(f"{n}: expected a bf16 device tensor")
     _check("sckv_ring_write", lib.sckv_ring_write(rows.data_ptr(), rows_bstride, ring.data_ptr(), ring_bstride, B, m,
                                                   start_pos, win, D, _stream(stream)))
+
+
+def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_new, ld_k_new: int, k_codes,
+                        ld_codes: int, k_scales, ld_scales: int, Di: int, kv_new: torch.Tensor, ld_kv_new: int,
+                        ring: torch.Tensor, ld_ring: int, B: int, D: int, win: int, start_pos: int,
+                        idx: torch.Tensor, ld_idx: int, stream=None):
+    """Row arguments: device tensors whose data pointers start the first row
+    (lat_new / lat_dst / k_new / k_codes / k_scales may be None)."""
+    def p(t, dtype, name):
+        if t is None:
+            return None
+        if not t.is_cuda or t.dtype != dtype:
+            raise ValueError(f"{name}: expected a {dtype} device tensor")
+        return t.data_ptr()
+    _check("sckv_decode_prepare", lib.sckv_decode_prepare(
+        p(lat_new, torch.bfloat16, "lat_new"), ld_lat_new, p(lat_dst, torch.bfloat16, "lat_dst"), ld_lat_dst,
+        p(k_new, torch.bfloat16, "k_new"), ld_k_new, p(k_codes, torch.uint8, "k_codes"), ld_codes,
+        p(k_scales, torch.uint8, "k_scales"), ld_scales, Di, p(kv_new, torch.bfloat16, "kv_new"), ld_kv_new,
+        p(ring, torch.bfloat16, "ring"), ld_ring, B, D, win, start_pos, p(idx, torch.int32, "idx"), ld_idx,
+        _stream(stream)))
 
 
 def sckv_rows_a_len(win: int, m: int, start_pos: int) -> int:

@@ -1,0 +1,144 @@
+// decode.hip -- the set-up of a decode step (m = 1) in one launch: the fp4
+// round trip of the completed latent row into the latent cache, the packed
+// indexer k row, the new kv row into its ring slot and the window columns of
+// the index list.
+//
+// Page "metrale_model_arch/attn_v41/forward.rs" (AttnV41::forward: the fp4
+// round trip of a completed latent group before its cache copy, the ring copy
+// at slot start_pos mod window before attention, window_topk_idxs) and page
+// "metrale_model_arch/deepseek_v41_ref/compress.rs" (fp4_quant_e4m3_inplace,
+// fp4_quant_e8m0_inplace).  Each part computes exactly what the separate calls
+// sckv_quant_rows, sckv_quant_pack, sckv_ring_write and sckv_window_idx compute
+// (the same device code); they write disjoint memory, so one launch with a
+// workgroup per sequence replaces four launches whose cost at decode size is
+// almost all launch and drain time.
+#include "sckv_device.h"
+
+namespace sckv {
+namespace {
+
+constexpr int PREP_THREADS = 256;
+
+struct PrepArgs {
+    const uint16_t* lat_new;
+    int64_t ld_lat_new;
+    uint16_t* lat_dst;
+    int64_t ld_lat_dst;
+    const uint16_t* k_new;
+    int64_t ld_k_new;
+    uint8_t* k_codes;
+    int64_t ld_codes;
+    uint8_t* k_scales;
+    int64_t ld_scales;
+    int Di;
+    const uint16_t* kv_new;
+    int64_t ld_kv_new;
+    uint16_t* ring;
+    int64_t ld_ring;
+    int D, win;
+    int64_t start_pos;
+    int32_t* idx;
+    int64_t ld_idx;
+};
+
+// Workgroup b = sequence b.  Every row pointer is 16-byte aligned and every
+// stride a multiple of 16 bytes (checked on the host), so all row traffic is
+// 16-byte vectors.
+__global__ __launch_bounds__(PREP_THREADS) void decode_prepare_kernel(PrepArgs a) {
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    // latent row: one lane per 16-value block (E4M3_B16 round trip, bf16 out)
+    if (a.lat_new) {
+        const uint16_t* src = a.lat_new + b * a.ld_lat_new;
+        uint16_t* dst = a.lat_dst + b * a.ld_lat_dst;
+        for (int blk = t; blk < a.D / 16; blk += PREP_THREADS) {
+            uint32_t w[8];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const uint4 v = reinterpret_cast<const uint4*>(src + blk * 16)[i];
+                w[4 * i + 0] = v.x;
+                w[4 * i + 1] = v.y;
+                w[4 * i + 2] = v.z;
+                w[4 * i + 3] = v.w;
+            }
+            quant_block<SCKV_FP4_E4M3_B16>(w);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                reinterpret_cast<uint4*>(dst + blk * 16)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        }
+    }
+    // indexer k row: one lane per 32-value block (E8M0_B32, packed)
+    if (a.k_new) {
+        const uint16_t* src = a.k_new + b * a.ld_k_new;
+        uint8_t* codes = a.k_codes + b * a.ld_codes;
+        uint8_t* scales = a.k_scales + b * a.ld_scales;
+        for (int blk = t; blk < a.Di / 32; blk += PREP_THREADS) {
+            uint32_t w[16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint4 v = reinterpret_cast<const uint4*>(src + blk * 32)[i];
+                w[4 * i + 0] = v.x;
+                w[4 * i + 1] = v.y;
+                w[4 * i + 2] = v.z;
+                w[4 * i + 3] = v.w;
+            }
+            uint32_t cw[4];
+            const uint32_t sbyte = pack_block<SCKV_FP4_E8M0_B32>(w, cw);
+            *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+            scales[blk] = (uint8_t)sbyte;
+        }
+    }
+    // the new kv row into ring slot start_pos mod win
+    {
+        const uint4* src = reinterpret_cast<const uint4*>(a.kv_new + b * a.ld_kv_new);
+        uint4* dst = reinterpret_cast<uint4*>(a.ring + b * a.ld_ring + (a.start_pos % a.win) * a.D);
+        for (int i = t; i < a.D / 8; i += PREP_THREADS) dst[i] = src[i];
+    }
+    // window columns of the query at p = start_pos: the n_w = min(win, p + 1)
+    // newest positions, oldest first, then -1
+    {
+        const int64_t p = a.start_pos;
+        const int64_t n_w = (p + 1 < a.win) ? (p + 1) : a.win;
+        int32_t* row = a.idx + b * a.ld_idx;
+        for (int j = t; j < a.win; j += PREP_THREADS)
+            row[j] = (j < n_w) ? (int32_t)window_row(a.win, 1, p, p - n_w + 1 + j) : -1;
+    }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p % 16) == 0; }
+
+}  // namespace
+}  // namespace sckv
+
+extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, int64_t ld_lat_dst,
+                                   const void* k_new, int64_t ld_k_new, void* k_codes, int64_t ld_codes,
+                                   void* k_scales, int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new,
+                                   void* ring, int64_t ld_ring, int B, int D, int win, int64_t start_pos,
+                                   int32_t* idx, int64_t ld_idx, void* stream) {
+    using namespace sckv;
+    const char* name = "sckv_decode_prepare";
+    if (B < 0 || D <= 0 || win <= 0 || start_pos < 0) return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
+    if (D % 16 != 0) return fail(SCKV_EINVAL, std::string(name) + ": D is not a multiple of 16");
+    if (lat_new && (!lat_dst || ld_lat_new < D || ld_lat_dst < D))
+        return fail(SCKV_EINVAL, std::string(name) + ": latent rows: null destination or stride below D");
+    if (k_new && (!k_codes || !k_scales || Di <= 0 || Di % 32 != 0 || ld_k_new < Di || ld_codes < Di / 2 ||
+                  ld_scales < Di / 32))
+        return fail(SCKV_EINVAL, std::string(name) + ": k rows: null destination, Di not a multiple of 32 or short stride");
+    if (!kv_new || !ring || !idx) return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
+    if (ld_kv_new < D || ld_ring < (int64_t)win * D || ld_idx < win)
+        return fail(SCKV_EINVAL, std::string(name) + ": a stride is shorter than its row");
+    if (B == 0) return SCKV_OK;
+    if (B > 0x7fffffff / 2) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": B too large");
+    if (start_pos + win > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": positions past 2^31");
+    // 16-byte vectors throughout
+    const bool ok = aligned16(kv_new) && aligned16(ring) && (ld_kv_new % 8 == 0) && (ld_ring % 8 == 0) &&
+                    (!lat_new || (aligned16(lat_new) && aligned16(lat_dst) && ld_lat_new % 8 == 0 &&
+                                  ld_lat_dst % 8 == 0)) &&
+                    (!k_new || (aligned16(k_new) && aligned16(k_codes) && ld_k_new % 8 == 0 && ld_codes % 16 == 0));
+    if (!ok) return fail(SCKV_EINVAL, std::string(name) + ": rows must be 16-byte aligned with 16-byte strides");
+    PrepArgs a{(const uint16_t*)lat_new, ld_lat_new, (uint16_t*)lat_dst, ld_lat_dst, (const uint16_t*)k_new, ld_k_new,
+               (uint8_t*)k_codes, ld_codes, (uint8_t*)k_scales, ld_scales, Di, (const uint16_t*)kv_new, ld_kv_new,
+               (uint16_t*)ring, ld_ring, D, win, start_pos, idx, ld_idx};
+    decode_prepare_kernel<<<dim3((unsigned)B), dim3(PREP_THREADS), 0, (hipStream_t)stream>>>(a);
+    return check_launch(name);
+}

@@ -41,20 +41,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < BLOCK / 2; ++i) {
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
-    }
-    const float s = block_scale<MODE>(amax);
-    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
-#pragma unroll
-    for (int i = 0; i < BLOCK / 2; ++i) {
-        uint32_t lo = fp4_value<MODE>(bf16_bits_to_f32(w[i] & 0xffffu), s, inv_s);
-        uint32_t hi = fp4_value<MODE>(bf16_bits_to_f32(w[i] >> 16), s, inv_s);
-        w[i] = lo | (hi << 16);
-    }
+    quant_block<MODE>(w);
     if (VEC) {
 #pragma unroll
         for (int i = 0; i < BLOCK / 8; ++i)
@@ -140,25 +127,9 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < BLOCK / 2; ++i) {
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
-        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
-    }
-    const float s = block_scale<MODE>(amax);
-    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
     // BLOCK/2 bytes of codes: byte i holds elements 2i (low) and 2i+1 (high)
     uint32_t cw[BLOCK / 8];
-#pragma unroll
-    for (int i = 0; i < BLOCK / 8; ++i) cw[i] = 0;
-#pragma unroll
-    for (int i = 0; i < BLOCK; ++i) {
-        const float v = bf16_bits_to_f32((i & 1) ? (w[i / 2] >> 16) : (w[i / 2] & 0xffffu));
-        const float a = (MODE == SCKV_FP4_E8M0_B32) ? fminf(fabsf(v) * inv_s, 6.0f)
-                                                    : fminf(__fdiv_rn(fabsf(v), s), 6.0f);
-        cw[i / 8] |= e2m1_code(e2m1_round_mag(a), v) << (4 * (i % 8));
-    }
+    const uint32_t sbyte = pack_block<MODE>(w, cw);
     uint8_t* cdst = codes + row * ldc + blk * (BLOCK / 2);
     if (vec) {
         if (BLOCK == 32)
@@ -170,7 +141,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) cdst[i] = (uint8_t)(cw[i / 4] >> (8 * (i % 4)));
     }
-    scales[row * lds + blk] = (uint8_t)scale_byte<MODE>(s);
+    scales[row * lds + blk] = (uint8_t)sbyte;
 }
 
 }  // namespace

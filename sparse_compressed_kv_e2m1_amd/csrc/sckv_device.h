@@ -155,6 +155,60 @@ struct QuantMode<SCKV_FP4_E8M0_B32> {
     static constexpr int BLOCK = 32;
 };
 
+// The round trip of one block held as bf16 pairs (w[i]: value 2i in the low
+// half, 2i + 1 in the high half), in place.
+template <int MODE>
+__device__ __forceinline__ void quant_block(uint32_t (&w)[QuantMode<MODE>::BLOCK / 2]) {
+    constexpr int BLOCK = QuantMode<MODE>::BLOCK;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+    const float s = block_scale<MODE>(amax);
+    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        const uint32_t lo = fp4_value<MODE>(bf16_bits_to_f32(w[i] & 0xffffu), s, inv_s);
+        const uint32_t hi = fp4_value<MODE>(bf16_bits_to_f32(w[i] >> 16), s, inv_s);
+        w[i] = lo | (hi << 16);
+    }
+}
+
+// The packed form of one block (same input layout): BLOCK/8 code words (byte
+// j holds the codes of values 2j, low nibble, and 2j + 1) and the scale byte,
+// returned.
+template <int MODE>
+__device__ __forceinline__ uint32_t pack_block(const uint32_t (&w)[QuantMode<MODE>::BLOCK / 2],
+                                               uint32_t (&cw)[QuantMode<MODE>::BLOCK / 8]) {
+    constexpr int BLOCK = QuantMode<MODE>::BLOCK;
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 2; ++i) {
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xffffu)));
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+    const float s = block_scale<MODE>(amax);
+    const float inv_s = (MODE == SCKV_FP4_E8M0_B32) ? pow2_reciprocal(s) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < BLOCK / 8; ++i) cw[i] = 0;
+#pragma unroll
+    for (int i = 0; i < BLOCK; ++i) {
+        const float v = bf16_bits_to_f32((i & 1) ? (w[i / 2] >> 16) : (w[i / 2] & 0xffffu));
+        const float a = (MODE == SCKV_FP4_E8M0_B32) ? fminf(fabsf(v) * inv_s, 6.0f) : fminf(__fdiv_rn(fabsf(v), s), 6.0f);
+        cw[i / 8] |= e2m1_code(e2m1_round_mag(a), v) << (4 * (i % 8));
+    }
+    return scale_byte<MODE>(s);
+}
+
+// Row of position q inside rows_a (the layout sckv_rows_a_len describes).
+__device__ __forceinline__ int64_t window_row(int win, int64_t m, int64_t start_pos, int64_t q) {
+    if (start_pos == 0) return q;
+    if (m == 1) return q % win;
+    return (q < start_pos) ? (q % win) : (win + (q - start_pos));
+}
+
 // ---------------------------------------------------------------- host side
 
 void set_error(const std::string& msg);

@@ -34,13 +34,6 @@ __global__ __launch_bounds__(RING_THREADS) void ring_write_kernel(const uint16_t
     (void)m;
 }
 
-// Row of position q inside rows_a (see sckv_rows_a_len).
-__device__ __forceinline__ int64_t window_row(int win, int64_t m, int64_t start_pos, int64_t q) {
-    if (start_pos == 0) return q;
-    if (m == 1) return q % win;
-    return (q < start_pos) ? (q % win) : (win + (q - start_pos));
-}
-
 // idx[b, t, j] for j < win: the j-th oldest of the n_w = min(win, p + 1)
 // positions ending at p = start_pos + t, then -1.
 __global__ __launch_bounds__(IDX_THREADS) void window_idx_kernel(int64_t m, int64_t start_pos, int win,

@@ -133,6 +133,17 @@ class PathState:
         """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
         m, win, D = w.m, w.win, w.D
+        if self.mode == "ring" and w.Hi and self.kcache == "fp4" and self.n_new <= 1:
+            # decode: the latent and k rows, the ring slot and the window
+            # columns in one launch (the same results as the four calls below)
+            f = self.first_new
+            new = self.n_new == 1
+            out = [("decode_prepare", lambda: sk.sckv_decode_prepare(
+                self.latent_new if new else None, D, self.latent[:, f] if new else None, w.n_c * D,
+                self.ik_new if new else None, w.Di, self.ik_codes[:, f] if new else None, w.n_c * w.Di // 2,
+                self.ik_scales[:, f] if new else None, w.n_c * w.Di // 32, w.Di, self.kv_new, D, self.ring, win * D,
+                B, D, win, w.start_pos, self.idx, self.T))]
+            return out + self._score_and_attend_calls()
         out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
         if w.Hi and self.kcache == "fp4":
             out.append(("quant_index_k", self._pack_new_k))
@@ -142,6 +153,13 @@ class PathState:
             out.append(("ring_write", lambda: sk.sckv_ring_write(self.kv_new, D, self.ring, win * D, B, 1,
                                                                  w.start_pos, win, D)))
         out.append(("window_idx", lambda: sk.sckv_window_idx(B, m, w.start_pos, win, self.idx, self.T)))
+        return out + self._score_and_attend_calls()
+
+    def _score_and_attend_calls(self):
+        """Steps 4-6 of the module doc as (name, thunk) pairs."""
+        w, B = self.w, self.B
+        m, win, D = w.m, w.win, w.D
+        out = []
         if w.Hi and self.kcache == "fp4":
             out.append(("index_scores_topk", lambda: sk.sckv_index_scores_topk_fp4(
                 self.iq, self.ik_codes, self.ik_scales, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K,

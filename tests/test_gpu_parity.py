@@ -223,6 +223,48 @@ def test_ring_write_bit_exact(sk, win, m, start_pos, D):
         assert np.array_equal(got[b, win:], rows[b])
 
 
+@pytest.mark.parametrize("B,D,Di,win,start_pos,new", [(3, 512, 128, 128, 32767, True), (2, 64, 32, 16, 5, True),
+                                                       (4, 512, 128, 128, 1000, False), (2, 256, 64, 8, 7, True)])
+def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new):
+    """The one-launch decode set-up against the oracle: the latent row's
+    E4M3_B16 round trip into the cache, the packed E8M0_B32 k row, the ring
+    slot and the window columns; nothing else in the buffers changes."""
+    n_c = 6
+    f = 4  # cache row of the completed group
+    rng = np.random.default_rng(B * 1000 + start_pos)
+    lat_new = bits(bf16_of(rng.standard_normal((B, D))))
+    k_new = bits(bf16_of(rng.standard_normal((B, Di))))
+    kv_new = bits(bf16_of(rng.standard_normal((B, D))))
+    latent = rng.integers(0, 65535, size=(B, n_c, D)).astype(np.uint16)
+    codes = rng.integers(0, 255, size=(B, n_c, Di // 2)).astype(np.uint8)
+    scales = rng.integers(0, 255, size=(B, n_c, Di // 32)).astype(np.uint8)
+    ring = rng.integers(0, 65535, size=(B, win, D)).astype(np.uint16)
+    ld_idx = win + 5
+    lat_d, ring_d = from_bits(latent, "cuda"), from_bits(ring, "cuda")
+    codes_d, scales_d = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    idx = torch.full((B, 1, ld_idx), 77, dtype=torch.int32, device="cuda")
+    say(f"decode prepare B={B} D={D} Di={Di} win={win} start_pos={start_pos} new={new}")
+    sk.sckv_decode_prepare(from_bits(lat_new, "cuda") if new else None, D, lat_d[:, f] if new else None, n_c * D,
+                           from_bits(k_new, "cuda") if new else None, Di, codes_d[:, f] if new else None,
+                           n_c * Di // 2, scales_d[:, f] if new else None, n_c * Di // 32, Di,
+                           from_bits(kv_new, "cuda"), D, ring_d, win * D, B, D, win, start_pos, idx, ld_idx)
+    want_lat, want_codes, want_scales = latent.copy(), codes.copy(), scales.copy()
+    if new:
+        for b in range(B):
+            want_lat[b, f] = oracle.quant(lat_new[b], oracle.E4M3_B16)
+            c, sc = oracle.pack(k_new[b], oracle.E8M0_B32)
+            want_codes[b, f], want_scales[b, f] = c, sc
+    assert np.array_equal(bits(lat_d), want_lat)
+    assert np.array_equal(codes_d.cpu().numpy(), want_codes)
+    assert np.array_equal(scales_d.cpu().numpy(), want_scales)
+    got_ring = bits(ring_d)
+    want_idx, _ = oracle.window_idx(win, 1, start_pos)
+    got_idx = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got_ring[b], oracle.ring_write(ring[b], kv_new[b][None], start_pos))
+        assert np.array_equal(got_idx[b, :, :win], want_idx) and np.all(got_idx[b, :, win:] == 77)
+
+
 # --------------------------------------------------------------------- indexer
 
 INDEXER_CASES = [
