@@ -189,6 +189,11 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
               f"WRITE_SIZE x{scale.get('WRITE_SIZE', float('nan')):.3f}",
               "# steady-state dispatches only (most frequent grid size per kernel)", "#",
               f"{'kernel':<44} {'calls':>5} {'avg_us':>9} {'read_MB':>9} {'write_MB':>9}"]
+    # only the kernels of the step's own calls (set-up launches are left out)
+    from sparse_compressed_kv_e2m1_amd.step import step_call_names  # noqa: PLC0415
+    names = step_call_names(w, kcache)
+    mine = lambda k: any(k.startswith(p.replace(" ", "")) for c in names for p in CALL_KERNELS[c])  # noqa: E731
+    dur = {k: v for k, v in dur.items() if mine(k)}
     for k in sorted(dur, key=lambda k: -dur[k]):
         rd = res["FETCH_SIZE"].get(k) if res["FETCH_SIZE"] else None
         wr = res["WRITE_SIZE"].get(k) if res["WRITE_SIZE"] else None
@@ -197,7 +202,8 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
         lines.append(f"{k[:44]:<44} {calls[k]:>5} {dur[k]:>9.2f} {rd:>9} {wr:>9}")
     lines += ["#", f"{'library call':<20} {'avg_us':>9} {'alg_MB':>9} {'hbm_MB':>9}"]
     entries = {}
-    for call, pre in CALL_KERNELS.items():
+    for call in dict.fromkeys(names):
+        pre = CALL_KERNELS[call]
         ks = [k for k in dur if any(k.startswith(p.replace(" ", "")) for p in pre)]
         if not ks:
             continue

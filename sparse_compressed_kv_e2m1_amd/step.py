@@ -31,6 +31,27 @@ import torch
 from . import _binding as sk
 
 
+def uses_decode_prepare(w, kcache: str) -> bool:
+    """A decode step (m == 1 at start_pos > 0) with an indexer over the packed
+    k cache sets up with the one-launch sckv_decode_prepare."""
+    return w.start_pos > 0 and w.m == 1 and bool(w.Hi) and kcache == "fp4" and w.n_c - w.first_new_row <= 1
+
+
+def step_call_names(w, kcache: str) -> list:
+    """Names of a step's library calls, in order (the names PathState.calls
+    gives them)."""
+    if uses_decode_prepare(w, kcache):
+        names = ["decode_prepare"]
+    else:
+        names = ["quant_latent"] + (["quant_index_k"] if w.Hi else [])
+        names += (["ring_write"] if (w.start_pos > 0 and w.m == 1) else []) + ["window_idx"]
+    names += ["index_scores_topk"] if w.Hi else ["visible_idx"]
+    names += ["sparse_attn_sink"]
+    if not (w.start_pos > 0 and w.m == 1):
+        names += ["ring_write"]
+    return names
+
+
 class PathState:
     """Device buffers of one step for B sequences of a workload, built from
     raw CPU inputs (see sckv_synth.make_inputs).  setup() round-trips the cache
@@ -133,7 +154,7 @@ class PathState:
         """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
         m, win, D = w.m, w.win, w.D
-        if self.mode == "ring" and w.Hi and self.kcache == "fp4" and self.n_new <= 1:
+        if uses_decode_prepare(w, self.kcache):
             # decode: the latent and k rows, the ring slot and the window
             # columns in one launch (the same results as the four calls below)
             f = self.first_new
@@ -186,6 +207,7 @@ class PathState:
         """One pass of the hot path (steps 1-6 of the module doc)."""
         if not hasattr(self, "_calls"):
             self._calls = self.calls()
+            assert [n for n, _ in self._calls] == step_call_names(self.w, self.kcache)
         for _, f in self._calls:
             f()
         return self.out
