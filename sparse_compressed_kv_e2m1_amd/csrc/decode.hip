@@ -41,51 +41,53 @@ struct PrepArgs {
     int64_t ld_idx;
 };
 
+// Max over aligned groups of 8 or 16 lanes by DPP (every lane of the group
+// gets it): lane pairs, quads, then the half-row and row mirrors.
+__device__ __forceinline__ float group_max(float v, int lanes) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, false)));  // quad_perm 1,0,3,2
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, false)));  // quad_perm 2,3,0,1
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, false)));  // row_half_mirror
+    if (lanes == 16) v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, false)));  // row_mirror
+    return v;
+}
+
 // Workgroup b = sequence b.  Every row pointer is 16-byte aligned and every
-// stride a multiple of 16 bytes (checked on the host), so all row traffic is
-// 16-byte vectors.
+// stride a multiple of 16 bytes (checked on the host).  The rows are spread
+// over the lanes two values a lane, so a block's 16 (latent) or 32 (k) values
+// sit in 8 or 16 neighbouring lanes, which share the block amax by DPP; each
+// value then goes through the same device code as in sckv_quant_rows /
+// sckv_quant_pack.
 __global__ __launch_bounds__(PREP_THREADS) void decode_prepare_kernel(PrepArgs a) {
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
-    // latent row: one lane per 16-value block (E4M3_B16 round trip, bf16 out)
+    // latent row: values 2p, 2p + 1 in lane p (E4M3_B16 round trip, bf16 out)
     if (a.lat_new) {
-        const uint16_t* src = a.lat_new + b * a.ld_lat_new;
-        uint16_t* dst = a.lat_dst + b * a.ld_lat_dst;
-        for (int blk = t; blk < a.D / 16; blk += PREP_THREADS) {
-            uint32_t w[8];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint4 v = reinterpret_cast<const uint4*>(src + blk * 16)[i];
-                w[4 * i + 0] = v.x;
-                w[4 * i + 1] = v.y;
-                w[4 * i + 2] = v.z;
-                w[4 * i + 3] = v.w;
-            }
-            quant_block<SCKV_FP4_E4M3_B16>(w);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                reinterpret_cast<uint4*>(dst + blk * 16)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.lat_new + b * a.ld_lat_new);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(a.lat_dst + b * a.ld_lat_dst);
+        for (int p = t; p < a.D / 2; p += PREP_THREADS) {
+            const uint32_t w = src[p];
+            const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
+            const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 8);
+            const float s = block_scale<SCKV_FP4_E4M3_B16>(amax);
+            dst[p] = fp4_value<SCKV_FP4_E4M3_B16>(lo, s, 0.0f) | (fp4_value<SCKV_FP4_E4M3_B16>(hi, s, 0.0f) << 16);
         }
     }
-    // indexer k row: one lane per 32-value block (E8M0_B32, packed)
+    // indexer k row: values 2p, 2p + 1 in lane p (E8M0_B32, packed: one code
+    // byte a lane, the scale byte from the block's first lane)
     if (a.k_new) {
-        const uint16_t* src = a.k_new + b * a.ld_k_new;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_new + b * a.ld_k_new);
         uint8_t* codes = a.k_codes + b * a.ld_codes;
         uint8_t* scales = a.k_scales + b * a.ld_scales;
-        for (int blk = t; blk < a.Di / 32; blk += PREP_THREADS) {
-            uint32_t w[16];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 v = reinterpret_cast<const uint4*>(src + blk * 32)[i];
-                w[4 * i + 0] = v.x;
-                w[4 * i + 1] = v.y;
-                w[4 * i + 2] = v.z;
-                w[4 * i + 3] = v.w;
-            }
-            uint32_t cw[4];
-            const uint32_t sbyte = pack_block<SCKV_FP4_E8M0_B32>(w, cw);
-            *reinterpret_cast<uint4*>(codes + blk * 16) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-            scales[blk] = (uint8_t)sbyte;
+        for (int p = t; p < a.Di / 2; p += PREP_THREADS) {
+            const uint32_t w = src[p];
+            const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
+            const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 16);
+            const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
+            const float inv_s = pow2_reciprocal(s);
+            const uint32_t clo = e2m1_code(e2m1_round_mag(fminf(fabsf(lo) * inv_s, 6.0f)), lo);
+            const uint32_t chi = e2m1_code(e2m1_round_mag(fminf(fabsf(hi) * inv_s, 6.0f)), hi);
+            codes[p] = (uint8_t)(clo | (chi << 4));
+            if ((p & 15) == 0) scales[p / 16] = (uint8_t)scale_byte<SCKV_FP4_E8M0_B32>(s);
         }
     }
     // the new kv row into ring slot start_pos mod win
