@@ -410,6 +410,7 @@ FP4_CASES = [
     (200, 1, 4, 128, 9000, 1, 8999, 1000, False),   # fused, 128 keys per thread
     (192, 1, 32, 256, 1500, 1, 1499, 100, False),   # fused, head dim 256
     (1, 256, 8, 128, 64, 1, 0, 16, False),          # fused, queries that see <= K rows
+    (192, 1, 64, 128, 32768, 4, 131071, 2048, False),  # fused, long decode shape (64 keys a thread)
 ]
 
 
@@ -546,6 +547,33 @@ def test_sparse_attn_sink_tolerance(sk, case):
     bsel = range(B) if B <= 4 else [0, B // 2, B - 1]
     for b in bsel:
         ref = oracle.sparse_attn(q[b], A[b], Rb[b] if rb else None, idx[b], sink, scale)
+        ok, worst = attn_tolerance_ok(got[b], ref)
+        assert ok, (b, worst)
+
+
+def test_sparse_attn_long_list_one_workgroup(sk):
+    """256 queries of 2176 entries (68 chunks of 32) are each taken by one
+    workgroup (no split): chunks past the 64th, and whole empty chunks on both
+    sides of it, go through the chunk bitmap's second word."""
+    B, m, H, D, ra, rb, T = 256, 1, 64, 512, 128, 512, 2176
+    rng = np.random.default_rng(2176)
+    q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, ra, D))))
+    Rb = bits(bf16_of(rng.standard_normal((B, rb, D))))
+    idx = rng.integers(0, ra + rb, size=(B, m, T)).astype(np.int32)
+    idx[rng.random((B, m, T)) < 0.1] = -1
+    idx[:, :, 60 * 32:62 * 32] = -1   # empty chunks below 64
+    idx[:, :, 64 * 32:66 * 32] = -1   # and above
+    idx[:, :, T - 7:] = -1             # a ragged, partly valid last chunk
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(D ** -0.5))
+    out = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    say("attention, 68-chunk lists in one workgroup each")
+    sk.sckv_sparse_attn_sink(from_bits(q, "cuda"), from_bits(A, "cuda"), ra, from_bits(Rb, "cuda"), rb,
+                             torch.from_numpy(idx).cuda(), T, torch.from_numpy(sink).cuda(), scale, B, m, H, D, out)
+    got = vals(bits(out))
+    for b in (0, 77, B - 1):
+        ref = oracle.sparse_attn(q[b], A[b], Rb[b], idx[b], sink, scale)
         ok, worst = attn_tolerance_ok(got[b], ref)
         assert ok, (b, worst)
 
