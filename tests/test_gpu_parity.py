@@ -607,6 +607,39 @@ STEP_CASES = [(n, "bf16") for n in synth.WORKLOADS] + [
     (n, "fp4") for n, w in synth.WORKLOADS.items() if w.Hi and w.Di in (128, 256)]
 
 
+@pytest.mark.parametrize("name", ["decode", "long_decode"])
+def test_step_bench_launch_config_matches_oracle(sk, name):
+    """A whole decode step at the batch the bench times (B = 256, packed k
+    cache: the one-launch set-up, one score + top-K workgroup per query, one
+    attention workgroup per query), inputs drawn on the device, checked
+    against the oracle on sampled sequences."""
+    from sparse_compressed_kv_e2m1_amd.step import PathState
+
+    w = synth.WORKLOADS[name]
+    B = 256
+    say(f"step {name} B={B} (packed k cache): generating inputs on the device")
+    x = synth.make_inputs(w, B, device="cuda")
+    # the sampled sequences' inputs, copied before the step (the path works in
+    # place on the caches and the ring)
+    sampled = (0, 131, B - 1)
+    xs = {b: {k: (v.cpu() if k == "sink" else v[b:b + 1].cpu()) for k, v in x.items()} for b in sampled}
+    st = PathState(w, x, B, kcache="fp4")
+    st.setup()
+    say(f"step {name} B={B}: running the HIP path")
+    st.step()
+    torch.cuda.synchronize()
+    idx = st.idx.cpu().numpy()
+    out = vals(bits(st.out))
+    for b in sampled:
+        say(f"step {name}: oracle for instance {b}")
+        ref_idx, ref_out = oracle_step(w, xs[b], 0)
+        assert np.array_equal(idx[b], ref_idx), f"index lists differ ({name}, b={b})"
+        ok, worst = attn_tolerance_ok(out[b], ref_out)
+        assert ok, (name, b, worst)
+    del st, x
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,kcache", STEP_CASES, ids=lambda c: c if isinstance(c, str) else None)
 def test_step_matches_oracle(sk, name, kcache):
     from sparse_compressed_kv_e2m1_amd.step import PathState
