@@ -38,6 +38,7 @@ namespace {
 constexpr int score_waves(bool fp4) { return fp4 ? 8 : 4; }
 constexpr int TOPK_THREADS = 512;
 constexpr int FUSED_MIN_QUERIES = 192;  // fused scores + top-K from this many queries on
+constexpr size_t SCORE_STATIC_LDS = 2112;  // the score kernel's static LDS (histogram, scan words), rounded up
 
 // Ordered 16-bit key of a bf16 score: -0 counts as +0; a larger key is a
 // larger score.
@@ -136,6 +137,75 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[KPT], int64_t 
     }
     const uint32_t gt_total = block_sum<NWAVES>(gt, red[rb]);
     const uint32_t need_eq = (uint32_t)K - gt_total;  // >= 1 by the choice of tau
+    const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
+    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
+    take_eq = take_eq < eq ? take_eq : eq;
+    uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
+    uint32_t eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        const uint32_t k = key[j];
+        bool take = k > tau;
+        if (k == tau) {
+            take = eq_seen < take_eq;
+            ++eq_seen;
+        }
+        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s0 + j);
+    }
+}
+
+// The bin b of a 256-bin histogram with (keys in bins above b) < k <= (keys
+// in bins b and above), and the count of keys in bins above b; every wave
+// computes the same (uniform) answer from LDS.  Needs 1 <= k <= total.
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t k, uint32_t& bin, uint32_t& above) {
+    const int lane = threadIdx.x & 63;
+    const u32x4 c = *reinterpret_cast<const u32x4*>(h + 4 * lane);  // bins 4 lane .. 4 lane + 3
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(s);                       // keys in bins < 4 (lane + 1)
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t ge = total - incl + s;                           // keys in bins >= 4 lane
+    const uint32_t gt = ge - s;                                     // keys in bins >= 4 (lane + 1)
+    const bool mine = gt < k && ge >= k;                            // exactly one lane
+    const int L = __builtin_ctzll(__ballot(mine));
+    uint32_t b = 4 * lane, run = gt;
+    if (mine) {
+#pragma unroll
+        for (int i = 3; i >= 1; --i) {
+            if (run + c[i] >= k) {
+                b = 4 * lane + i;
+                break;
+            }
+            run += c[i];
+        }
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)b, L);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)run, L);
+}
+
+// topk_select for a block that already holds the histogram of its keys' high
+// bytes (hist[0..256), built while the keys were produced): the K-th largest
+// key tau is the high-byte bin found there plus the low-byte bin found in a
+// second histogram (hist[256..512), zero on entry) over the keys of that bin
+// only; then the same ordered compaction.
+template <int KPT, int NWAVES>
+__device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int64_t s0, int K, int32_t offset,
+                                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* tot) {
+    uint32_t hi_bin, above_hi;
+    find_bin(hist, (uint32_t)K, hi_bin, above_hi);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+        if ((key[j] >> 8) == hi_bin) atomicAdd(&hist[256 + (key[j] & 0xffu)], 1u);
+    __syncthreads();
+    uint32_t lo_bin, above_lo;
+    find_bin(hist + 256, (uint32_t)K - above_hi, lo_bin, above_lo);
+    const uint32_t tau = (hi_bin << 8) | lo_bin;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gt += key[j] > tau;
+        eq += key[j] == tau;
+    }
+    const uint32_t need_eq = (uint32_t)K - (above_hi + above_lo);  // keys == tau to take, >= 1
     const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
     uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
     take_eq = take_eq < eq ? take_eq : eq;
@@ -320,6 +390,11 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
 #pragma unroll
     for (int i = 0; i < S::PD; ++i)
         if (i < ntiles) issue(i);
+    // fused top-K: the high-byte histogram of the keys fills while they are
+    // produced (hist[0..256)); hist[256..512) serves the second pass
+    __shared__ uint32_t hist[KPT > 0 ? 512 : 1];
+    if (KPT > 0)
+        for (int i = threadIdx.x; i < 512; i += S::NW * 64) hist[i] = 0u;
     // q and w landed (only the tile copies may still be in flight), in every wave
     if (ntiles >= S::PD)
         wait_vmcnt<S::PD * S::NINST>();
@@ -515,7 +590,9 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
         const int64_t s = w0 + (int64_t)tile * 32 + r;
         if (lane < 32 && s < w1) {
             const uint32_t bits = f32_to_bf16_bits(v[0]);
-            keys_l[s - row0] = (uint16_t)score_key(bits);
+            const uint32_t key = score_key(bits);
+            keys_l[s - row0] = (uint16_t)key;
+            if (KPT > 0) atomicAdd(&hist[key >> 8], 1u);
             if (scores) sc_l[s - row0] = (uint16_t)bits;
         }
     }
@@ -531,7 +608,6 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
     } else {
         // ---- fused top-K over the query's keys in LDS (row0 == 0, nrows == vis > K)
         constexpr int KP = KPT > 0 ? KPT : 8;
-        __shared__ uint32_t red[2][S::NW];
         __shared__ uint32_t tot[S::NW];
         const int64_t s0 = (int64_t)threadIdx.x * KP;
         uint32_t key[KP];
@@ -547,7 +623,7 @@ __global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
         }
 #pragma unroll
         for (int j = 0; j < KP; ++j) key[j] = (s0 + j < nrows) ? key[j] : 0u;
-        topk_select<KP, S::NW>(key, s0, K, offset, idx + qi * ld + col0, red, tot);
+        topk_select_hist<KP, S::NW>(key, s0, K, offset, idx + qi * ld + col0, hist, tot);
     }
 }
 
@@ -642,7 +718,8 @@ struct IndexArgs {
 template <int MT, int DI, int KPT, bool FP4>
 int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* keys) {
     const size_t lds = score_lds_bytes<MT, DI, KPT, FP4>(rows_per_wg, a.scores != nullptr);
-    if (lds > 160 * 1024) return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: score tile does not fit in LDS");
+    if (lds + SCORE_STATIC_LDS > 160 * 1024)
+        return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: score tile does not fit in LDS");
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI, KPT, FP4>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -662,7 +739,7 @@ int launch_fused(const IndexArgs& a) {
     const int nth = score_waves(FP4) * 64;
     const int need = (rows + nth - 1) / nth;
 #define SCKV_FUSED(KPT)                                                                           \
-    (score_lds_bytes<MT, DI, KPT, FP4>(rows, false) > 160 * 1024 ? SCKV_EUNSUPPORTED               \
+    (score_lds_bytes<MT, DI, KPT, FP4>(rows, false) + SCORE_STATIC_LDS > 160 * 1024 ? SCKV_EUNSUPPORTED \
                                                                   : launch_scores<MT, DI, KPT, FP4>(a, rows, 1, nullptr))
     if (need <= 8) return SCKV_FUSED(8);
     if (need <= 16) return SCKV_FUSED(16);
