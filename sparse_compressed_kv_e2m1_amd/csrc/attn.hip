@@ -25,9 +25,13 @@
 //   4. the probabilities are already the A operand of O += P . R (16x16x32
 //      again, K = the chunk's rows), whose B operand comes from the same stage
 //      through the transposing LDS read (ds_read_b64_tr_b16).
-// One barrier per pair of chunks (one per set).  At the end the second set
-// hands its (max, sum, O) to the first through LDS.  A query's chunks may
-// also be split over several workgroups; their partials are merged by a small
+// One barrier per pair of chunks (one per set).  The index slice is staged in
+// LDS once (up to 64 or 128 chunks, two kernel variants) with a bitmap of the
+// chunks that name a valid row; empty chunks are skipped.  At the end the two
+// sets exchange half of O each through LDS, each finishes half of the
+// columns, and the rows leave as 16-byte pieces through an LDS staging area.
+// A query's chunks may also be split over several workgroups (when the
+// queries alone do not fill the chip); their partials are merged by a small
 // combine kernel that adds the sink once.
 #include "mfma.h"
 #include "sckv_device.h"

@@ -20,7 +20,8 @@ def test_header_declares_the_calls():
     names = declared_calls()
     for n in ["sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_rows_a_len", "sckv_window_idx",
               "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
-              "sckv_last_error", "sckv_abi_version"]:
+              "sckv_last_error", "sckv_abi_version", "sckv_quant_pack", "sckv_index_scores_topk_fp4",
+              "sckv_decode_prepare"]:
         assert n in names
 
 
@@ -116,6 +117,31 @@ def test_error_paths(L):
     assert at(scale=0.0) == sk.SCKV_EINVAL
     assert at(ws=None) == sk.SCKV_EWORKSPACE  # decode at B = 1 splits rows over workgroups
     assert at(B=0) == sk.SCKV_OK
+    assert at(out=ctypes.c_void_p(0x1008)) == sk.SCKV_EINVAL  # rows leave as 16-byte pieces
+
+    # decode set-up: sizes, strides, alignment, missing destinations
+    def dp(**kw):
+        a = dict(ld_lat_new=512, ld_lat_dst=512, ld_k_new=128, ld_codes=64, ld_scales=4, Di=128, ld_kv_new=512,
+                 ld_ring=128 * 512, B=2, D=512, win=128, start_pos=1000, ld_idx=640)
+        a.update({k: v for k, v in kw.items() if k in a})
+        return L.sckv_decode_prepare(kw.get("lat_new", fake), a["ld_lat_new"], kw.get("lat_dst", fake),
+                                     a["ld_lat_dst"], kw.get("k_new", fake), a["ld_k_new"], kw.get("k_codes", fake),
+                                     a["ld_codes"], kw.get("k_scales", fake), a["ld_scales"], a["Di"],
+                                     kw.get("kv_new", fake), a["ld_kv_new"], kw.get("ring", fake), a["ld_ring"],
+                                     a["B"], a["D"], a["win"], a["start_pos"], kw.get("idx", fake), a["ld_idx"], None)
+
+    assert dp(D=520) == sk.SCKV_EINVAL                 # not a multiple of 16
+    assert dp(Di=100) == sk.SCKV_EINVAL                # not a multiple of 32
+    assert dp(lat_dst=None) == sk.SCKV_EINVAL
+    assert dp(k_codes=None) == sk.SCKV_EINVAL
+    assert dp(kv_new=None) == sk.SCKV_EINVAL
+    assert dp(idx=None) == sk.SCKV_EINVAL
+    assert dp(ld_ring=1000) == sk.SCKV_EINVAL          # shorter than win * D
+    assert dp(ld_idx=100) == sk.SCKV_EINVAL            # shorter than win
+    assert dp(ring=ctypes.c_void_p(0x1004)) == sk.SCKV_EINVAL  # not 16-byte aligned
+    assert dp(ld_codes=72) == sk.SCKV_EINVAL           # code rows not 16-byte strided
+    assert dp(start_pos=-1) == sk.SCKV_EINVAL
+    assert dp(B=0) == sk.SCKV_OK
 
 
 def test_workspace_sizes(L):
