@@ -121,9 +121,9 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     const int hw = wave % NHW;   // heads 16 hw .. 16 hw + 15
     const int l16 = lane & 15;
     const int g = lane >> 4;
-    const int64_t qi = blockIdx.x / nsplit;
+    const int64_t qi = blockIdx.x / (uint32_t)nsplit;
     const int split = (int)(blockIdx.x - qi * nsplit);
-    const int64_t b = qi / m;
+    const int64_t b = (uint32_t)qi / (uint32_t)m;  // query counts are below 2^31 (checked at launch)
     const uint16_t* rows_a_b = rows_a + b * ra * D;
     const uint16_t* rows_b_b = rows_b ? rows_b + b * rb * D : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
@@ -143,11 +143,24 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     // (every load address is clamped into its array rather than branched
     // around, so the loads issue back to back and only their consumers wait)
     // (only the rounds of NTH entries that reach into this slice: a uniform bound)
+    // (16-byte pieces when T is a multiple of 4: the slice then starts and
+    // ends on a piece boundary; else one entry a load)
+    const bool vec4 = (T & 3) == 0;
+    constexpr int IPT4 = (S::IPT + 3) / 4;
     int32_t iv_reg[S::IPT];
+    int4 iv4[IPT4];
+    if (vec4) {
 #pragma unroll
-    for (int k = 0; k < S::IPT; ++k) {
-        const int i = (int)threadIdx.x + k * NTH;
-        if (k * NTH < nch * CHUNK) iv_reg[k] = idx_q[e0 + (i < ne ? i : ne - 1)];
+        for (int k = 0; k < IPT4; ++k) {
+            const int i0 = ((int)threadIdx.x + k * NTH) * 4;
+            if (k * NTH * 4 < nch * CHUNK) iv4[k] = *reinterpret_cast<const int4*>(idx_q + e0 + (i0 < ne ? i0 : ne - 4));
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < S::IPT; ++k) {
+            const int i = (int)threadIdx.x + k * NTH;
+            if (k * NTH < nch * CHUNK) iv_reg[k] = idx_q[e0 + (i < ne ? i : ne - 1)];
+        }
     }
     asm volatile("" ::: "memory");  // keep every index load ahead of the q loads
 
@@ -174,9 +187,25 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     // the index slice into LDS, with one flag per chunk that names a valid row
     // (a ballot covers 64 entries, two chunks)
     uint8_t* flag_l = lds + S::OFF_FLAG;
+    if (vec4) {
+        // a wave's 64 pieces are 8 chunks; a chunk's flag is the OR of its 8 pieces
+#pragma unroll
+        for (int k = 0; k < IPT4; ++k) {
+            if (k * NTH * 4 >= nch * CHUNK) break;
+            const int i0 = ((int)threadIdx.x + k * NTH) * 4;
+            int4 v = iv4[k];
+            if (i0 >= ne) v = int4{-1, -1, -1, -1};
+            if (i0 < nch * CHUNK) *reinterpret_cast<int4*>(idx_l + i0) = v;
+            const bool any = i0 < nch * CHUNK && ((uint32_t)v.x < rab || (uint32_t)v.y < rab ||
+                                                   (uint32_t)v.z < rab || (uint32_t)v.w < rab);
+            const uint64_t bal = __ballot(any);
+            const int c0 = (k * NTH + wave * 64) / 8;
+            if (lane < 8 && c0 + lane < CPS) flag_l[c0 + lane] = (uint8_t)(((bal >> (8 * lane)) & 0xffull) != 0);
+        }
+    }
 #pragma unroll
     for (int k = 0; k < S::IPT; ++k) {
-        if (k * NTH >= nch * CHUNK) break;  // chunks past nch: their flags are never read
+        if (vec4 || k * NTH >= nch * CHUNK) break;  // chunks past nch: their flags are never read
         const int i = (int)threadIdx.x + k * NTH;
         const int32_t v = (i < ne) ? iv_reg[k] : -1;
         if (i < nch * CHUNK) idx_l[i] = v;
@@ -320,11 +349,15 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
             if (it < n_own) {
                 // O[heads, :] += P . R: k = g*8 + 0..3 are rows g*4 + 0..3, k = g*8 + 4..7
                 // rows 16 + g*4 + 0..3 (the order the probabilities sit in)
+                // accumulator nt of set 1 holds the 16 columns of tile nt ^ NT/2
+                // (so that both sets finish accumulators 0 .. NT/2 - 1 at the end)
                 const int jj = l16 >> 2;
                 const int c4 = 4 * (l16 & 3);
+                const unsigned char* pv_lo = stp + set * (S::NT / 2) * 32;        // nt < NT/2
+                const unsigned char* pv_hi = stp + (1 - set) * (S::NT / 2) * 32;  // nt >= NT/2
 #pragma unroll
                 for (int nt = 0; nt < S::NT; ++nt) {
-                    const unsigned char* pc = stp + (nt * 16 + c4) * 2;
+                    const unsigned char* pc = (nt < S::NT / 2 ? pv_lo + nt * 32 : pv_hi + (nt - S::NT / 2) * 32) + c4 * 2;
                     const i16x4 lo = lds_read_tr16(pc + (g * 4 + jj) * S::RS);
                     const i16x4 hi = lds_read_tr16(pc + (16 + g * 4 + jj) * S::RS);
                     const bf16x8 bv =
@@ -348,6 +381,9 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
 
     // ---- epilogue: the two sets merge their (max, sum, O) through LDS, each
     // finishing half of the columns: set 0 tiles nt < NT/2, set 1 the rest.
+    // Both hold the tiles they finish in accumulators 0 .. NT/2 - 1 and hand
+    // over accumulators NT/2 .. NT - 1 (set 1 keeps tile nt ^ NT/2 in
+    // accumulator nt), so no accumulator is chosen at run time.
     // The exchanged tiles sit column-major, [D][HP] floats, a lane's four
     // rows as one 16-byte piece whose place in the column is swizzled by the
     // column (the 16 lanes of a group then cover every bank once).
@@ -361,8 +397,8 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     };
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
-        const int nt = (set == 0) ? NH + k : k;  // the other set's tiles
-        *reinterpret_cast<f32x4*>(xo_at(nt * 16 + l16)) = o[nt];
+        const int tile = (set == 0) ? NH + k : k;  // the other set's tiles
+        *reinterpret_cast<f32x4*>(xo_at(tile * 16 + l16)) = o[NH + k];
     }
     if (g == 0) {
         ml[(set * S::HP + head) * 2 + 0] = m_run;
@@ -384,10 +420,10 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     float fo[NH][4];  // this wave's finished tiles
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
-        const int nt = (set == 0) ? k : NH + k;
-        const f32x4 ot = *reinterpret_cast<const f32x4*>(xo_at(nt * 16 + l16));
+        const int tile = (set == 0) ? k : NH + k;
+        const f32x4 ot = *reinterpret_cast<const f32x4*>(xo_at(tile * 16 + l16));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) fo[k][i] = (o[nt][i] * f0[i] + ot[i] * f1[i]) * fin[i];
+        for (int i = 0; i < 4; ++i) fo[k][i] = (o[k][i] * f0[i] + ot[i] * f1[i]) * fin[i];
     }
     __syncthreads();  // every read of the exchanged tiles is done
     // stage the 16 x D/2 block in LDS (wave-private space), then write it out

@@ -522,6 +522,8 @@ ATTN_CASES = [
     (1, 1, 64, 512, 128, 1024, 2176, 0.5),
     (1, 3, 1, 64, 10, 10, 5, 0.0),
     (300, 1, 64, 512, 128, 200, 64, 0.1),    # many queries: no split
+    (2, 2, 40, 512, 60, 90, 200, 0.2),       # 33..63 heads at D = 512: padded second head group
+    (260, 1, 48, 512, 128, 300, 130, 0.1),   # the same, unsplit
 ]
 
 
@@ -547,6 +549,31 @@ def test_sparse_attn_sink_tolerance(sk, case):
     bsel = range(B) if B <= 4 else [0, B // 2, B - 1]
     for b in bsel:
         ref = oracle.sparse_attn(q[b], A[b], Rb[b] if rb else None, idx[b], sink, scale)
+        ok, worst = attn_tolerance_ok(got[b], ref)
+        assert ok, (b, worst)
+
+
+@pytest.mark.parametrize("B,H,D,qsd", [(1, 64, 512, 6.0), (300, 64, 512, 6.0), (1, 8, 64, 12.0), (2, 40, 512, 6.0)])
+def test_sparse_attn_wide_logits(sk, B, H, D, qsd):
+    """Logits spread over many units (q ~ N(0, qsd^2)): the running max moves
+    by more than its slack on many chunks, so the accumulated output is
+    rescaled mid-list."""
+    m, ra, rb, T = 1, 128, 700, 640
+    rng = np.random.default_rng(int(qsd) * 1000 + B + H)
+    q = bits(bf16_of(qsd * rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, ra, D))))
+    Rb = bits(bf16_of(rng.standard_normal((B, rb, D))))
+    idx = rng.integers(0, ra + rb, size=(B, m, T)).astype(np.int32)
+    idx[rng.random((B, m, T)) < 0.05] = -1
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(D ** -0.5))
+    out = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    say(f"attention wide logits B={B} H={H} D={D} qsd={qsd}")
+    sk.sckv_sparse_attn_sink(from_bits(q, "cuda"), from_bits(A, "cuda"), ra, from_bits(Rb, "cuda"), rb,
+                             torch.from_numpy(idx).cuda(), T, torch.from_numpy(sink).cuda(), scale, B, m, H, D, out)
+    got = vals(bits(out))
+    for b in sorted({0, B // 2, B - 1}):
+        ref = oracle.sparse_attn(q[b], A[b], Rb[b], idx[b], sink, scale)
         ok, worst = attn_tolerance_ok(got[b], ref)
         assert ok, (b, worst)
 
