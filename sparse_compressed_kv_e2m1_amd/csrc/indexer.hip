@@ -276,9 +276,10 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 // Ring depth of the fused kernel: the keys of a whole query share the LDS
 // with the ring (KPT keys per thread, 256 threads).
 constexpr int fused_ring_depth(int DI, int KPT, bool FP4) {
-    // fp4, few rows a wave (KPT 8: at most 2048 rows, 8 tiles a wave): a
-    // shallow ring, so that two workgroups share a compute unit
-    return FP4 ? (17 * DI >= 4096 ? (KPT >= 64 || KPT <= 8 ? 2 : 3) : (KPT >= 64 ? 4 : (KPT <= 8 ? 3 : 8)))
+    // fp4, up to 16 keys a thread (at most 8192 rows, 16 tiles a wave): a
+    // shallow ring, so that two workgroups share a compute unit and one's
+    // prologue and top-K overlap the other's stream
+    return FP4 ? (17 * DI >= 4096 ? (KPT >= 64 || KPT <= 8 ? 2 : 3) : (KPT >= 64 ? 4 : (KPT <= 16 ? 3 : 8)))
                : ((64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4));
 }
 
