@@ -578,6 +578,40 @@ def test_sparse_attn_wide_logits(sk, B, H, D, qsd):
         assert ok, (b, worst)
 
 
+@pytest.mark.parametrize("B,m", [(600, 1), (2, 300)])
+def test_sparse_attn_more_queries_than_compute_units(sk, B, m):
+    """More queries than compute units (workgroups run in several rounds),
+    ragged T, lists with no valid entry, lists with empty leading or middle
+    chunks, and m > 1 (several queries per sequence)."""
+    H, D, ra, rb, T = 64, 512, 64, 300, 100
+    rng = np.random.default_rng(B * 1000 + m)
+    q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, ra, D))))
+    Rb = bits(bf16_of(rng.standard_normal((B, rb, D))))
+    idx = rng.integers(0, ra + rb, size=(B, m, T)).astype(np.int32)
+    idx[rng.random((B, m, T)) < 0.2] = -1
+    flat = idx.reshape(B * m, T)
+    flat[5] = -1                 # nothing valid
+    flat[7, :64] = -1            # two empty leading chunks
+    flat[256 + 5, 32:96] = -1    # empty middle chunks
+    flat[B * m - 1, T - 3:] = -1
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(D ** -0.5))
+    out = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    say(f"attention, {B * m} queries over the compute units (B={B}, m={m})")
+    sk.sckv_sparse_attn_sink(from_bits(q, "cuda"), from_bits(A, "cuda"), ra, from_bits(Rb, "cuda"), rb,
+                             torch.from_numpy(idx).cuda(), T, torch.from_numpy(sink).cuda(), scale, B, m, H, D, out)
+    got = vals(bits(out)).reshape(B * m, H, D)
+    qf = q.reshape(B * m, H, D)
+    for t in sorted({0, 5, 7, 255, 256, 257, 256 + 5, 511, B * m - 2, B * m - 1}):
+        bb = t // m
+        ref = oracle.sparse_attn(qf[t:t + 1], A[bb], Rb[bb], flat[t:t + 1], sink, scale)
+        if t == 5:
+            assert np.all(got[t] == 0)
+        ok, worst = attn_tolerance_ok(got[t:t + 1], ref)
+        assert ok, (t, worst)
+
+
 def test_sparse_attn_long_list_one_workgroup(sk):
     """256 queries of 2176 entries (68 chunks of 32) are each taken by one
     workgroup (no split): chunks past the 64th, and whole empty chunks on both
