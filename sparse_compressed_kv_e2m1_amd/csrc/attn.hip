@@ -47,9 +47,9 @@ constexpr int MAX_CPS = 128;       // chunks one workgroup handles at most (its 
 // Head dim D, NHW head waves per set (16 heads each): 2 * NHW waves; CPS
 // chunks of the index list at most (64 or MAX_CPS; the smaller variant stages
 // less of the list and runs the short lists ~7% faster, measured).
-template <int D, int NHW, int CPS>
+template <int D, int NHW, int CPS, int NS = 2>
 struct AttnShape {
-    static constexpr int WAVES = 2 * NHW;
+    static constexpr int WAVES = NS * NHW;
     static constexpr int HP = 16 * NHW;     // padded heads
     static constexpr int KS = D / 32;       // k-steps of S^T = R . Q^T
     static constexpr int NT = D / 16;       // 16-wide output tiles
@@ -61,16 +61,18 @@ struct AttnShape {
     // both with 16 bytes of padding
     static constexpr int RS = 2 * D + 32;
     static constexpr int STAGE = CHUNK * RS;
-    static constexpr int OFF_IDX = 2 * NST * STAGE;
+    static constexpr int OFF_IDX = NS * NST * STAGE;
     static constexpr int OFF_FLAG = OFF_IDX + CPS * CHUNK * 4;  // one byte per chunk: names a valid row
     static constexpr size_t LDS_BYTES = (size_t)OFF_FLAG + CPS;
     static constexpr int IPT = CPS * CHUNK / (WAVES * 64);  // index entries a thread stages
     // the exchanged halves of O ([D][HP] f32) reuse the stages and both sets'
     // (max, sum) the index slice; afterwards each wave stages its 16 x D/2
     // output block (bf16, or f32 partials) in the stages
-    static_assert((size_t)D * HP * 4 <= (size_t)OFF_IDX && 2 * HP * 8 <= CPS * CHUNK * 4, "merge space");
+    static_assert(NS == 1 || ((size_t)D * HP * 4 <= (size_t)OFF_IDX && 2 * HP * 8 <= CPS * CHUNK * 4), "merge space");
     static_assert(CPS == 64 || CPS == 128, "one or two flag words");
-    static_assert((size_t)WAVES * 16 * (D / 2) * 4 <= (size_t)OFF_IDX, "output staging");
+    static_assert(NS == 1 || (size_t)WAVES * 16 * (D / 2) * 4 <= (size_t)OFF_IDX, "output staging");
+    // one set: unsplit lists only; each wave stages its 16 full bf16 rows
+    static_assert(NS == 2 || (size_t)WAVES * 16 * (2 * D + 32) <= (size_t)OFF_IDX, "output staging (one set)");
     static_assert(RPW % 4 == 0 && (RS % 16) == 0, "shape");
 };
 
@@ -103,13 +105,13 @@ __device__ __forceinline__ float lane_xor1(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
 
-template <int D, int NHW, int CPS>
-__global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
+template <int D, int NHW, int CPS, int NS>
+__global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    using S = AttnShape<D, NHW, CPS>;
+    using S = AttnShape<D, NHW, CPS, NS>;
     constexpr int NTH = S::WAVES * 64;
     extern __shared__ __align__(16) unsigned char lds[];
     int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int set = wave / NHW;  // chunk parity this wave computes
+    const int set = NS == 2 ? wave / NHW : 0;  // chunk parity this wave computes
     const int hw = wave % NHW;   // heads 16 hw .. 16 hw + 15
     const int l16 = lane & 15;
     const int g = lane >> 4;
@@ -228,8 +230,8 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     const Bits todo = {__ballot(lane < nch && flag_l[lane] != 0),
                        CPS > 64 ? __ballot(lane + 64 < nch && flag_l[lane + 64] != 0) : 0ull};
     const int n = __builtin_popcountll(todo.lo) + __builtin_popcountll(todo.hi);
-    const int n_own = (n > set) ? (n - set + 1) / 2 : 0;  // chunks of this wave's set
-    const int n_it = (n + 1) / 2;                         // iterations (same in every wave)
+    const int n_own = NS == 1 ? n : ((n > set) ? (n - set + 1) / 2 : 0);  // chunks of this wave's set
+    const int n_it = NS == 1 ? n : (n + 1) / 2;                           // iterations (same in every wave)
     auto drop_lowest = [](Bits& bits) {
         if (bits.lo)
             bits.lo &= bits.lo - 1;
@@ -240,11 +242,11 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
     auto next_own = [&](Bits& bits) -> int {
         const int j = bits.lo ? __builtin_ctzll(bits.lo) : 64 + __builtin_ctzll(bits.hi);
         drop_lowest(bits);
-        if (bits.lo | bits.hi) drop_lowest(bits);
+        if (NS == 2 && (bits.lo | bits.hi)) drop_lowest(bits);
         return j;
     };
     Bits ib = todo, cb = todo;
-    if (set == 1 && (ib.lo | ib.hi)) {
+    if (NS == 2 && set == 1 && (ib.lo | ib.hi)) {
         drop_lowest(ib);
         drop_lowest(cb);
     }
@@ -377,6 +379,45 @@ __global__ __launch_bounds__(2 * NHW * 64) void sparse_attn_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) o[nt][i] *= a4[i];
         resume = true;
+    }
+
+    if constexpr (NS == 1) {
+        // ---- epilogue, one set (unsplit lists only): no merge; each wave
+        // normalizes its 16 heads over the whole head dim and writes them
+        // through its own staging rows (bf16, pitch 2 D + 32 bytes) as
+        // 16-byte pieces.  Lanes l16 and l16 ^ 1 pair up adjacent columns.
+        __syncthreads();  // all stages idle
+        float fin[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fin[i] = 1.0f / __shfl(l_run, g * 4 + i, 64);
+        constexpr int PF = 2 * D + 32;
+        unsigned char* stg = lds + (size_t)wave * (16 * PF);
+        const bool odd = (l16 & 1) != 0;
+#pragma unroll
+        for (int k = 0; k < S::NT; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float a = o[k][i] * fin[i], b2 = o[k][i + 1] * fin[i + 1];
+                const float other = lane_xor1(odd ? a : b2);
+                const f32x2 pr = odd ? f32x2{other, b2} : f32x2{a, other};
+                const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                const int r = g * 4 + i + (odd ? 1 : 0);
+                const int c = k * 16 + (l16 & ~1);
+                *reinterpret_cast<uint32_t*>(stg + r * PF + c * 2) = pb;
+            }
+        wave_lds_sync();
+        constexpr int CPR = 2 * D / 16;  // 16-byte pieces of a row
+        const int nrow1 = (H - 16 * hw) < 16 ? (H - 16 * hw) : 16;
+#pragma unroll
+        for (int k = 0; k < 16 * CPR / 64; ++k) {
+            const int piece = k * 64 + lane;
+            const int r = piece / CPR, c = piece % CPR;
+            if (r < nrow1) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PF + c * 16);
+                store16(reinterpret_cast<unsigned char*>(out + (qi * H + 16 * hw + r) * (int64_t)D) + c * 16, v);
+            }
+        }
+        return;
     }
 
     // ---- epilogue: the two sets merge their (max, sum, O) through LDS, each
@@ -531,17 +572,17 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     *nsplit = (nchunks + cps - 1) / cps;
 }
 
-template <int D, int NHW, int CPS>
+template <int D, int NHW, int CPS, int NS = 2>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                 int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
-    using Sh = AttnShape<D, NHW, CPS>;
+    using Sh = AttnShape<D, NHW, CPS, NS>;
     if (Sh::LDS_BYTES > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS>,
+        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<D, NHW, CPS><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
+    sparse_attn_kernel<D, NHW, CPS, NS><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
         q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps, nsplit, out, part_o, part_ml);
     return check_launch("sckv_sparse_attn_sink");
 }
@@ -550,6 +591,14 @@ template <int D, int NHW>
 int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                   int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
+    if constexpr (D == 512 && NHW == 4) {
+        // unsplit lists of up to 64 chunks: one set of 4 waves (76 KB of LDS),
+        // so that two workgroups (two queries) share a compute unit and one's
+        // start and finish overlap the other's chunk loop
+        if (cps <= 64 && nsplit == 1)
+            return launch_attn<D, NHW, 64, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
+                                              nsplit, out, part_o, part_ml, s);
+    }
     if (cps <= 64)
         return launch_attn<D, NHW, 64>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
                                        out, part_o, part_ml, s);
