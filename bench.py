@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
 
-DEFAULT_B = {"tiny_decode": 1, "decode": 1024, "long_decode": 256, "causal_prefill": 1, "chunked_prefill": 1}
+DEFAULT_B = {"tiny_decode": 1, "decode": 1024, "long_decode": 512, "causal_prefill": 1, "chunked_prefill": 1}
 
 
 def log(*a):

@@ -44,9 +44,11 @@ constexpr float LOG2E = 1.4426950408889634f;
 constexpr float STALE_MAX = 8.0f;  // base-2 slack before the running max moves
 constexpr int MAX_CPS = 128;       // chunks one workgroup handles at most (its index range sits in LDS)
 
-// Head dim D, NHW head waves per set (16 heads each): 2 * NHW waves; CPS
-// chunks of the index list at most (64 or MAX_CPS; the smaller variant stages
-// less of the list and runs the short lists ~7% faster, measured).
+// Head dim D, NHW head waves per set (16 heads each), NS sets (2: the sets
+// take alternate chunks of one query; 1: unsplit lists only, so that two
+// workgroups share a compute unit); CPS chunks of the index list at most (64,
+// 72 or MAX_CPS; the smaller variants stage less of the list and run the short
+// lists ~7% faster, measured).
 template <int D, int NHW, int CPS, int NS = 2>
 struct AttnShape {
     static constexpr int WAVES = NS * NHW;
@@ -69,7 +71,8 @@ struct AttnShape {
     // (max, sum) the index slice; afterwards each wave stages its 16 x D/2
     // output block (bf16, or f32 partials) in the stages
     static_assert(NS == 1 || ((size_t)D * HP * 4 <= (size_t)OFF_IDX && 2 * HP * 8 <= CPS * CHUNK * 4), "merge space");
-    static_assert(CPS == 64 || CPS == 128, "one or two flag words");
+    static_assert(CPS % 8 == 0 && CPS >= 64 && CPS <= 128, "one or two flag words");
+    static_assert((CPS * CHUNK) % (WAVES * 64) == 0, "index staging rounds");
     static_assert(NS == 1 || (size_t)WAVES * 16 * (D / 2) * 4 <= (size_t)OFF_IDX, "output staging");
     // one set: unsplit lists only; each wave stages its 16 full bf16 rows
     static_assert(NS == 2 || (size_t)WAVES * 16 * (2 * D + 32) <= (size_t)OFF_IDX, "output staging (one set)");
@@ -559,6 +562,19 @@ __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const float* _
     }
 }
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // Chunks per workgroup: split a query's chunks only when the queries alone do
 // not give about one workgroup per compute unit.
 void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
@@ -592,11 +608,20 @@ int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                   int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
     if constexpr (D == 512 && NHW == 4) {
-        // unsplit lists of up to 64 chunks: one set of 4 waves (76 KB of LDS),
-        // so that two workgroups (two queries) share a compute unit and one's
-        // start and finish overlap the other's chunk loop
-        if (cps <= 64 && nsplit == 1)
+        // unsplit lists of up to 64 chunks and at least two queries per
+        // compute unit: one set of 4 waves (76 KB of LDS), so that two
+        // workgroups (two queries) share a compute unit and one's start and
+        // finish overlap the other's chunk loop (with fewer queries the
+        // two-set workgroup keeps 8 waves on each compute unit)
+        const int ncu = compute_units();
+        const bool one_set = nsplit == 1 && ncu > 0 && nq >= 2 * (int64_t)ncu;
+        if (cps <= 64 && one_set)
             return launch_attn<D, NHW, 64, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
+                                              nsplit, out, part_o, part_ml, s);
+        // (up to 72 chunks, e.g. a 128-row window plus a top-2048 list: the
+        // index buffer still leaves room for two workgroups)
+        if (cps <= 72 && one_set)
+            return launch_attn<D, NHW, 72, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
                                               nsplit, out, part_o, part_ml, s);
     }
     if (cps <= 64)
