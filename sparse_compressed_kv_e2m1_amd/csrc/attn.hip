@@ -49,7 +49,7 @@ constexpr int MAX_CPS = 128;       // chunks one workgroup handles at most (its 
 // workgroups share a compute unit); CPS chunks of the index list at most (64,
 // 72 or MAX_CPS; the smaller variants stage less of the list and run the short
 // lists ~7% faster, measured).
-template <int D, int NHW, int CPS, int NS = 2>
+template <int D, int NHW, int CPS, int NS = 2, bool CS = false>
 struct AttnShape {
     static constexpr int WAVES = NS * NHW;
     static constexpr int HP = 16 * NHW;     // padded heads
@@ -64,8 +64,16 @@ struct AttnShape {
     static constexpr int RS = 2 * D + 32;
     static constexpr int STAGE = CHUNK * RS;
     static constexpr int OFF_IDX = NS * NST * STAGE;
-    static constexpr int OFF_FLAG = OFF_IDX + CPS * CHUNK * 4;  // one byte per chunk: names a valid row
-    static constexpr size_t LDS_BYTES = (size_t)OFF_FLAG + CPS;
+    static constexpr int IDXB = CPS * CHUNK * 4;  // bytes of the index slice
+    static constexpr int NIB = 1;
+    static constexpr int OFF_FLAG = OFF_IDX + NIB * IDXB;  // one byte per chunk: names a valid row
+    // CS (column split of P . R, one set only): every wave's probabilities
+    // [NHW][64 lanes] x 16 bytes, the running-max factors [HP] f32 and one
+    // "moved" byte per head wave
+    static constexpr int OFF_P = (OFF_FLAG + CPS + 15) / 16 * 16;
+    static constexpr int OFF_ALPHA = OFF_P + NHW * 64 * 16;
+    static constexpr int OFF_MOVED = OFF_ALPHA + HP * 4;
+    static constexpr size_t LDS_BYTES = CS ? (size_t)OFF_MOVED + 16 : (size_t)OFF_FLAG + CPS;
     static constexpr int IPT = CPS * CHUNK / (WAVES * 64);  // index entries a thread stages
     // the exchanged halves of O ([D][HP] f32) reuse the stages and both sets'
     // (max, sum) the index slice; afterwards each wave stages its 16 x D/2
@@ -76,6 +84,8 @@ struct AttnShape {
     static_assert(NS == 1 || (size_t)WAVES * 16 * (D / 2) * 4 <= (size_t)OFF_IDX, "output staging");
     // one set: unsplit lists only; each wave stages its 16 full bf16 rows
     static_assert(NS == 2 || (size_t)WAVES * 16 * (2 * D + 32) <= (size_t)OFF_IDX, "output staging (one set)");
+    static_assert(!CS || (NS == 1 && D == 512 && NHW == 4 && (size_t)WAVES * HP * (D / NHW) * 2 <= (size_t)OFF_IDX),
+                  "column split: one set of 4 head waves at D = 512");
     static_assert(RPW % 4 == 0 && (RS % 16) == 0, "shape");
 };
 
@@ -108,13 +118,13 @@ __device__ __forceinline__ float lane_xor1(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
 
-template <int D, int NHW, int CPS, int NS>
+template <int D, int NHW, int CPS, int NS, bool CS>
 __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
-    using S = AttnShape<D, NHW, CPS, NS>;
+    using S = AttnShape<D, NHW, CPS, NS, CS>;
     constexpr int NTH = S::WAVES * 64;
     extern __shared__ __align__(16) unsigned char lds[];
     int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
@@ -344,14 +354,59 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
                     const bool moved = __ballot(m_new != m_run) != 0;
                     m_run = m_new;
                     pa = as_bf16x8(u32x4{pk[0], pk[1], pk[2], pk[3]});
-                    if (moved) {
+                    if constexpr (CS) {
+                        // publish this wave's probabilities and, when one of its
+                        // heads moved its running max, the factors (lanes 0..15
+                        // hold heads 16 hw + l16)
+                        *reinterpret_cast<bf16x8*>(lds + S::OFF_P + (hw * 64 + lane) * 16) = pa;
+                        if (lane == 0) lds[S::OFF_MOVED + hw] = moved ? 1 : 0;
+                        if (moved && g == 0)
+                            reinterpret_cast<float*>(lds + S::OFF_ALPHA)[16 * hw + l16] = alpha;
+                    } else if (moved) {
                         rescale = true;
                         break;
                     }
                 }
             }
             resume = false;
-            if (it < n_own) {
+            if (CS && it < n_own) {
+                // column split: after every wave has published its
+                // probabilities, wave hw accumulates O for all 64 heads over
+                // columns 128 hw .. 128 hw + 127 (accumulator 8 hg + ct: heads
+                // 16 hg + g*4 + i, columns 128 hw + 16 ct + l16)
+                __syncthreads();
+                const uint32_t mv = *reinterpret_cast<const uint32_t*>(lds + S::OFF_MOVED);
+                if (mv) {  // rare: rescale the head groups whose running max moved
+                    const float* al = reinterpret_cast<const float*>(lds + S::OFF_ALPHA);
+#pragma unroll
+                    for (int hg = 0; hg < NHW; ++hg) {
+                        if (((mv >> (8 * hg)) & 0xffu) == 0) continue;
+                        float a4[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) a4[i] = al[16 * hg + g * 4 + i];
+#pragma unroll
+                        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[hg * 8 + ct][i] *= a4[i];
+                    }
+                }
+                bf16x8 pall[NHW];
+#pragma unroll
+                for (int hg = 0; hg < NHW; ++hg)
+                    pall[hg] = *reinterpret_cast<const bf16x8*>(lds + S::OFF_P + (hg * 64 + lane) * 16);
+                const int jj = l16 >> 2;
+                const int c4 = 4 * (l16 & 3);
+#pragma unroll
+                for (int ct = 0; ct < 8; ++ct) {
+                    const unsigned char* pc = stp + (hw * 128 + ct * 16 + c4) * 2;
+                    const i16x4 lo = lds_read_tr16(pc + (g * 4 + jj) * S::RS);
+                    const i16x4 hi = lds_read_tr16(pc + (16 + g * 4 + jj) * S::RS);
+                    const bf16x8 bv =
+                        __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                    for (int hg = 0; hg < NHW; ++hg) o[hg * 8 + ct] = mfma16x16x32(pall[hg], bv, o[hg * 8 + ct]);
+                }
+            } else if (it < n_own) {
                 // O[heads, :] += P . R: k = g*8 + 0..3 are rows g*4 + 0..3, k = g*8 + 4..7
                 // rows 16 + g*4 + 0..3 (the order the probabilities sit in)
                 // accumulator nt of set 1 holds the 16 columns of tile nt ^ NT/2
@@ -384,6 +439,50 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
         resume = true;
     }
 
+    if constexpr (CS) {
+        // ---- epilogue, column split: 1/sum of each head from its owner
+        // wave, then each wave normalizes its 64 heads x 128 columns and
+        // writes them through its own staging rows (bf16, 256 bytes a row,
+        // 16-byte pieces swizzled by the row) as 16-byte pieces
+        __syncthreads();  // all stages idle
+        float* il = reinterpret_cast<float*>(lds + S::OFF_ALPHA);
+        if (g == 0) il[16 * hw + l16] = 1.0f / l_run;
+        __syncthreads();
+        constexpr int PR = (D / NHW) * 2;  // bytes of a staged row (128 columns)
+        constexpr int NPC = PR / 16;       // 16-byte pieces a row
+        unsigned char* stg = lds + (size_t)wave * (S::HP * PR);
+        const bool odd = (l16 & 1) != 0;
+#pragma unroll
+        for (int hg = 0; hg < NHW; ++hg) {
+            float fin[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fin[i] = il[16 * hg + g * 4 + i];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; i += 2) {
+                    const float a = o[hg * 8 + ct][i] * fin[i], b2 = o[hg * 8 + ct][i + 1] * fin[i + 1];
+                    const float other = lane_xor1(odd ? a : b2);
+                    const f32x2 pr = odd ? f32x2{other, b2} : f32x2{a, other};
+                    const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                    const int r = 16 * hg + g * 4 + i + (odd ? 1 : 0);
+                    const int c = ct * 16 + (l16 & ~1);  // column within the wave's 128
+                    const int pc = (c >> 3) ^ (r % NPC);
+                    *reinterpret_cast<uint32_t*>(stg + r * PR + pc * 16 + (c & 7) * 2) = pb;
+                }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int k = 0; k < S::HP * NPC / 64; ++k) {
+            const int piece = k * 64 + lane;
+            const int r = piece / NPC, c = piece % NPC;
+            if (r < H) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PR + ((c ^ (r % NPC)) << 4));
+                store16(reinterpret_cast<unsigned char*>(out + (qi * H + r) * (int64_t)D + hw * (D / NHW)) + c * 16, v);
+            }
+        }
+        return;
+    }
     if constexpr (NS == 1) {
         // ---- epilogue, one set (unsplit lists only): no merge; each wave
         // normalizes its 16 heads over the whole head dim and writes them
@@ -588,17 +687,17 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     *nsplit = (nchunks + cps - 1) / cps;
 }
 
-template <int D, int NHW, int CPS, int NS = 2>
+template <int D, int NHW, int CPS, int NS = 2, bool CS = false>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                 int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
-    using Sh = AttnShape<D, NHW, CPS, NS>;
+    using Sh = AttnShape<D, NHW, CPS, NS, CS>;
     if (Sh::LDS_BYTES > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS>,
+        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS, CS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<D, NHW, CPS, NS><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
+    sparse_attn_kernel<D, NHW, CPS, NS, CS><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
         q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps, nsplit, out, part_o, part_ml);
     return check_launch("sckv_sparse_attn_sink");
 }
@@ -616,12 +715,12 @@ int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
         const int ncu = compute_units();
         const bool one_set = nsplit == 1 && ncu > 0 && nq >= 2 * (int64_t)ncu;
         if (cps <= 64 && one_set)
-            return launch_attn<D, NHW, 64, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
+            return launch_attn<D, NHW, 64, 1, true>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
                                               nsplit, out, part_o, part_ml, s);
         // (up to 72 chunks, e.g. a 128-row window plus a top-2048 list: the
         // index buffer still leaves room for two workgroups)
         if (cps <= 72 && one_set)
-            return launch_attn<D, NHW, 72, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
+            return launch_attn<D, NHW, 72, 1, true>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
                                               nsplit, out, part_o, part_ml, s);
     }
     if (cps <= 64)
