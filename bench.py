@@ -8,10 +8,10 @@ workload, every input resident in HBM before the timed region.
 
 Default workload: decode, m = 1 at start_pos = 32767, 64 heads x 512, window
 128, ratio 4 (8192 compressed rows), indexer 64 x 128 with top-512, batched
-over B = 1024 independent sequences (four attention workgroups per compute
-unit and call, one after the other, so that the launch, dispatch and
+over B = 2048 independent sequences (eight attention workgroups per compute
+unit and call, two at a time, so that the launch, dispatch and
 per-workgroup start-up cost is spread over more queries); one step streams
-~1.4 GB, far past the 256 MB last-level cache.
+~2.8 GB, far past the 256 MB last-level cache.
 
 Prints ONE JSON line (stdout): metric tokens/s, roofline of the dominant
 kernel (HIP-event time on the library's stream), and the oracle timed on the
@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
 
-DEFAULT_B = {"tiny_decode": 1, "decode": 1024, "long_decode": 512, "causal_prefill": 1, "chunked_prefill": 1}
+DEFAULT_B = {"tiny_decode": 1, "decode": 2048, "long_decode": 512, "causal_prefill": 1, "chunked_prefill": 1}
 
 
 def log(*a):

@@ -668,7 +668,7 @@ STEP_CASES = [(n, "bf16") for n in synth.WORKLOADS] + [
     (n, "fp4") for n, w in synth.WORKLOADS.items() if w.Hi and w.Di in (128, 256)]
 
 
-@pytest.mark.parametrize("name,B", [("decode", 1024), ("long_decode", 512)])
+@pytest.mark.parametrize("name,B", [("decode", 2048), ("long_decode", 512)])
 def test_step_bench_launch_config_matches_oracle(sk, name, B):
     """A whole decode step at the batch the bench times (packed k cache: the
     one-launch set-up, one score + top-K workgroup per query, one attention
