@@ -26,13 +26,23 @@
 //      again, K = the chunk's rows), whose B operand comes from the same stage
 //      through the transposing LDS read (ds_read_b64_tr_b16).
 // One barrier per pair of chunks (one per set).  The index slice is staged in
-// LDS once (up to 64 or 128 chunks, two kernel variants) with a bitmap of the
-// chunks that name a valid row; empty chunks are skipped.  At the end the two
-// sets exchange half of O each through LDS, each finishes half of the
+// LDS once (up to 64, 72 or 128 chunks, three kernel variants) with a bitmap
+// of the chunks that name a valid row; empty chunks are skipped.  At the end
+// the two sets exchange half of O each through LDS, each finishes half of the
 // columns, and the rows leave as 16-byte pieces through an LDS staging area.
 // A query's chunks may also be split over several workgroups (when the
 // queries alone do not fill the chip); their partials are merged by a small
 // combine kernel that adds the sink once.
+//
+// One-set variant (D = 512, 33..64 heads, unsplit lists of at most 72
+// chunks, at least two queries per compute unit): a workgroup is one set of
+// 4 waves with half the LDS, so two workgroups (two queries) share a compute
+// unit and one's start and finish overlap the other's chunk loop.  In it
+// P . R is split by columns: after S^T and the softmax each wave publishes
+// its 16 heads' probabilities (and, when its running max moved, the rescale
+// factors) in LDS, and after one more barrier every wave accumulates O for
+// all 64 heads over its own 128 columns, which reads each row byte once per
+// wave instead of once per head group.
 #include "mfma.h"
 #include "sckv_device.h"
 
