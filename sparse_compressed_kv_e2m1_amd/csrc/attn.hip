@@ -281,6 +281,26 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
     auto issue = [&](int slot, int j) {
         const int32_t* ic = idx_l + j * CHUNK + hw * S::RPW;
         const uint32_t st = lds0 + (uint32_t)((set * S::NST + slot) * S::STAGE);
+        if constexpr (D == 512) {
+            // the rows' source addresses as a lane vector (lane r < RPW holds
+            // row r's), computed once; each copy then takes two lane reads, its
+            // LDS address and the copy (5 wait states between a lane read
+            // writing a scalar register and a memory instruction reading it)
+            const uint32_t iv = (uint32_t)ic[lane & (S::RPW - 1)];
+            const uint16_t* base = (iv < (uint32_t)ra) ? rows_a_b : rows_b_sh;
+            const uint64_t addr = (uint64_t)((iv < rab) ? base + (size_t)iv * D : qrow);
+#pragma unroll
+            for (int rr = 0; rr < S::RPW; ++rr) {
+                const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)addr, rr);
+                const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), rr);
+                const uint32_t lb = st + (uint32_t)((hw * S::RPW + rr) * S::RS);
+                asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                             :
+                             : "v"((uint32_t)lane * 16u), "s"((const void*)(((uint64_t)hi << 32) | lo)), "s"(lb)
+                             : "memory", "m0");
+            }
+            return;
+        }
         int32_t ivv[S::RPW];
 #pragma unroll
         for (int v4 = 0; v4 < S::RPW / 4; ++v4) {
