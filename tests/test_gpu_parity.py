@@ -553,11 +553,13 @@ def test_sparse_attn_sink_tolerance(sk, case):
         assert ok, (b, worst)
 
 
-@pytest.mark.parametrize("B,H,D,qsd", [(1, 64, 512, 6.0), (300, 64, 512, 6.0), (1, 8, 64, 12.0), (2, 40, 512, 6.0)])
+@pytest.mark.parametrize("B,H,D,qsd", [(1, 64, 512, 6.0), (300, 64, 512, 6.0), (600, 64, 512, 6.0), (600, 40, 512, 6.0),
+                                          (1, 8, 64, 12.0), (2, 40, 512, 6.0)])
 def test_sparse_attn_wide_logits(sk, B, H, D, qsd):
     """Logits spread over many units (q ~ N(0, qsd^2)): the running max moves
     by more than its slack on many chunks, so the accumulated output is
-    rescaled mid-list."""
+    rescaled mid-list (at B = 600 in the one-set workgroup, whose waves share
+    the rescale factors)."""
     m, ra, rb, T = 1, 128, 700, 640
     rng = np.random.default_rng(int(qsd) * 1000 + B + H)
     q = bits(bf16_of(qsd * rng.standard_normal((B, m, H, D))))
@@ -578,13 +580,15 @@ def test_sparse_attn_wide_logits(sk, B, H, D, qsd):
         assert ok, (b, worst)
 
 
-@pytest.mark.parametrize("B,m", [(600, 1), (2, 300)])
-def test_sparse_attn_more_queries_than_compute_units(sk, B, m):
-    """More queries than compute units (workgroups run in several rounds),
-    ragged T, lists with no valid entry, lists with empty leading or middle
-    chunks, and m > 1 (several queries per sequence)."""
-    H, D, ra, rb, T = 64, 512, 64, 300, 100
-    rng = np.random.default_rng(B * 1000 + m)
+@pytest.mark.parametrize("B,m,H,T", [(600, 1, 64, 100), (2, 300, 64, 100), (600, 1, 40, 130), (1100, 1, 64, 2176)])
+def test_sparse_attn_more_queries_than_compute_units(sk, B, m, H, T):
+    """More queries than compute units (workgroups run in several rounds;
+    from two queries per compute unit on, the one-set workgroup), ragged T
+    (also not a multiple of 4), 33..63 heads, lists of up to 72 chunks, lists
+    with no valid entry, lists with empty leading or middle chunks, and m > 1
+    (several queries per sequence)."""
+    D, ra, rb = 512, 64, 300
+    rng = np.random.default_rng(B * 1000 + m + H + T)
     q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
     A = bits(bf16_of(rng.standard_normal((B, ra, D))))
     Rb = bits(bf16_of(rng.standard_normal((B, rb, D))))
