@@ -355,15 +355,16 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
                             sp[mt] = mfma16x16x32(rk, qb[ks], sp[mt]);
                         }
                     if constexpr (CS) {
-                        // schedule: four operand reads ahead of the products, then
+                        // schedule: SA operand reads ahead of the products, then
                         // one read per product
-                        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+                        constexpr int SA = 6;
+                        __builtin_amdgcn_sched_group_barrier(0x100, SA, 0);
 #pragma unroll
-                        for (int k2 = 0; k2 < 2 * S::KS - 4; ++k2) {
+                        for (int k2 = 0; k2 < 2 * S::KS - SA; ++k2) {
                             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                         }
-                        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, SA, 0);
                     }
                     float x[8];
                     float cmax = -INFINITY;
