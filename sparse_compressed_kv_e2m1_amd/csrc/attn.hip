@@ -354,10 +354,10 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
                                                                                ks * 64 + g * 16);
                             sp[mt] = mfma16x16x32(rk, qb[ks], sp[mt]);
                         }
-                    if constexpr (CS) {
+                    {
                         // schedule: SA operand reads ahead of the products, then
                         // one read per product
-                        constexpr int SA = 6;
+                        constexpr int SA = 2 * S::KS < 6 ? 2 * S::KS : 6;
                         __builtin_amdgcn_sched_group_barrier(0x100, SA, 0);
 #pragma unroll
                         for (int k2 = 0; k2 < 2 * S::KS - SA; ++k2) {
