@@ -203,6 +203,21 @@ class PathState:
                                                                  (win + m) * D, B, m, w.start_pos, win, D)))
         return out
 
+    def capture_graph(self):
+        """One step (the same library calls on torch's current stream) captured
+        into a HIP graph; replaying it runs the step without per-launch host
+        work.  The library records no memset, allocation or synchronization,
+        and every buffer the step uses is allocated here beforehand."""
+        side = torch.cuda.Stream(device=self.device)  # default priority
+        side.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream(self.device).wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        return graph
+
     def step(self):
         """One pass of the hot path (steps 1-6 of the module doc)."""
         if not hasattr(self, "_calls"):

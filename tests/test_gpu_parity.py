@@ -704,6 +704,38 @@ def test_step_bench_launch_config_matches_oracle(sk, name, B):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("name,B", [("tiny_decode", 8), ("decode", 16), ("causal_prefill", 1)])
+def test_step_graph_replays_match_eager(sk, name, B):
+    """The step captured in a HIP graph (as the bench times it): every replay,
+    with eager work and synchronizations between replays, gives the eager
+    step's index lists and outputs bit for bit (these steps are idempotent:
+    a decode step rewrites the same ring slot and cache rows, a fresh prefill
+    step reads the fresh kv, not the ring it writes)."""
+    from sparse_compressed_kv_e2m1_amd.step import PathState
+
+    w = synth.WORKLOADS[name]
+    say(f"graph replays: {name} B={B}")
+    x = synth.make_inputs(w, B, device="cuda")
+    st = PathState(w, x, B, kcache="fp4" if w.Di in (128, 256) else "bf16")
+    st.setup()
+    st.step()
+    torch.cuda.synchronize()
+    ref_idx, ref_out = st.idx.clone(), st.out.clone()
+    graph = st.capture_graph()
+    for r in range(3):
+        st.idx.fill_(-7)
+        st.out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.idx, ref_idx), (name, r)
+        assert torch.equal(st.out.view(torch.int16), ref_out.view(torch.int16)), (name, r)
+        st.step()  # eager work between replays
+        torch.cuda.synchronize()
+    del graph, st, x
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,kcache", STEP_CASES, ids=lambda c: c if isinstance(c, str) else None)
 def test_step_matches_oracle(sk, name, kcache):
     from sparse_compressed_kv_e2m1_amd.step import PathState
