@@ -336,50 +336,61 @@ void sckvo_visible_idx(int64_t m, int64_t start_pos, int ratio, int64_t n_c, int
 /* trip with power-of-two scales in blocks of 32; scores are bf16 values]    */
 /* ------------------------------------------------------------------------ */
 
-/* Exact dot product of two bf16 vectors.  Every bf16 value is M * 2^E with an
- * integer |M| < 2^8; the products are summed as integers over a common
- * exponent, so the sum is exact.  *exact_f32 is set to 1 when that exact sum is
- * a binary32 value (then every order of f32 accumulation without overflow gives
- * it bit for bit).  Returns the exact sum rounded to binary64. */
-static double oracle_exact_dot(const uint16_t* a, const uint16_t* b, int n, int* exact_f32) {
-    int e_min = 1 << 30;
-    int ma[4096], mb[4096], ea[4096], eb[4096];
-    if (n > 4096) abort();
-    for (int i = 0; i < n; ++i) {
-        float fa = sckvo_bf16_to_f32(a[i]), fb = sckvo_bf16_to_f32(b[i]);
-        int xa, xb;
-        /* fa = fr * 2^xa with 0.5 <= |fr| < 1, so fa = (fr * 2^8) * 2^(xa-8) and
-         * fr * 2^8 is an integer because bf16 keeps 8 significant bits. */
-        double fra = frexp((double)fa, &xa), frb = frexp((double)fb, &xb);
-        ma[i] = (int)ldexp(fra, 8);
-        mb[i] = (int)ldexp(frb, 8);
-        ea[i] = xa - 8;
-        eb[i] = xb - 8;
-        if (ma[i] != 0 && mb[i] != 0 && ea[i] + eb[i] < e_min) e_min = ea[i] + eb[i];
+/* A bf16 value as an integer significand and a power of two: v = m * 2^e
+ * with |m| < 2^8, because bf16 keeps 8 significant bits (v = fr * 2^x with
+ * 0.5 <= |fr| < 1 from frexp, so m = fr * 2^8 is an integer and e = x - 8).
+ * Zero gives m = 0. */
+static void oracle_split_bf16(const uint16_t* a, int64_t n, int* m, int* e) {
+    for (int64_t i = 0; i < n; ++i) {
+        int x;
+        double fr = frexp((double)sckvo_bf16_to_f32(a[i]), &x);
+        m[i] = (int)ldexp(fr, 8);
+        e[i] = x - 8;
     }
-    __int128 acc = 0;
+}
+
+/* Exact dot product of two bf16 vectors given as oracle_split_bf16 pairs.
+ * The products are summed as integers over their smallest exponent, so the
+ * sum is exact.  *exact_f32 is set to 1 when every partial sum of the
+ * products, taken in ANY order, is a binary32 value -- then any binary32
+ * accumulation (matrix cores included) gives the exact value bit for bit.
+ * That holds when all products are integer multiples of 2^g (g = the lowest
+ * set bit over all of them), sum |product| < 2^(g+24) (24 significant bits),
+ * g >= -149 (the binary32 subnormal quantum) and g + 24 <= 128 (no overflow).
+ * Returns the exact sum rounded to binary64. */
+static double oracle_exact_dot(const int* ma, const int* ea, const int* mb, const int* eb, int n, int* exact_f32) {
+    int e_min = 1 << 30;
+    for (int i = 0; i < n; ++i)
+        if (ma[i] != 0 && mb[i] != 0 && ea[i] + eb[i] < e_min) e_min = ea[i] + eb[i];
+    __int128 acc = 0, sum_abs = 0, bits_or = 0;
     for (int i = 0; i < n; ++i) {
         if (ma[i] == 0 || mb[i] == 0) continue;
         int sh = ea[i] + eb[i] - e_min;
         if (sh > 100) abort(); /* outside what this oracle can sum exactly */
-        acc += ((__int128)((int64_t)ma[i] * mb[i])) << sh;
+        __int128 p = ((__int128)((int64_t)ma[i] * mb[i])) << sh;
+        __int128 ap = p < 0 ? -p : p;
+        acc += p;
+        sum_abs += ap;
+        bits_or |= ap;
     }
-    if (acc == 0) {
+    if (bits_or == 0) {
         *exact_f32 = 1;
         return 0.0;
     }
-    /* The sum is acc * 2^e_min.  Drop trailing zero bits; it is a binary32
-     * value when at most 24 significant bits remain (the exponents here are
-     * far inside the normal range). */
+    int g = 0; /* products are multiples of 2^(e_min + g) */
+    while (((bits_or >> g) & 1) == 0) ++g;
+    int e_low = e_min + g;
+    *exact_f32 = ((sum_abs >> g) < ((__int128)1 << 24)) && e_low >= -149 && e_low + 24 <= 128;
+    if (acc == 0) return 0.0;
+    /* the exact sum acc * 2^e_min, rounded to binary64 (exact when at most 53
+     * significant bits, which exactness above implies) */
     while ((acc & 1) == 0) {
         acc /= 2;
         ++e_min;
     }
     __int128 mag = acc < 0 ? -acc : acc;
     if (mag >= ((__int128)1 << 53)) abort(); /* beyond an exact binary64 */
-    double d = ldexp((double)(int64_t)acc, e_min);
-    *exact_f32 = (mag < ((__int128)1 << 24));
-    return d;
+    return ldexp((double)(int64_t)acc, e_min);
 }
 
 /* Indexer scores for the queries listed in qsel (reading of the indexer, whose
@@ -399,12 +410,18 @@ int64_t sckvo_index_scores(const uint16_t* q_raw, const uint16_t* k_hat, const f
                            uint16_t* scores) {
     int64_t inexact = 0;
     uint16_t* qh = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)Hi * Di);
+    int* qm = (int*)malloc(sizeof(int) * (size_t)Hi * Di);
+    int* qe = (int*)malloc(sizeof(int) * (size_t)Hi * Di);
+    int* km = (int*)malloc(sizeof(int) * (size_t)(n_c > 0 ? n_c : 1) * Di);
+    int* ke = (int*)malloc(sizeof(int) * (size_t)(n_c > 0 ? n_c : 1) * Di);
     float* r = (float*)malloc(sizeof(float) * (size_t)Hi);
+    oracle_split_bf16(k_hat, n_c * (int64_t)Di, km, ke);
     for (int64_t i = 0; i < nsel; ++i) {
         int64_t t = qsel[i];
         if (t < 0 || t >= m) abort();
         const uint16_t* qrow = q_raw + t * (int64_t)Hi * Di;
         sckvo_quant_e8m0(qrow, qh, (int64_t)Hi * Di, 32);
+        oracle_split_bf16(qh, (int64_t)Hi * Di, qm, qe);
         int64_t vis = sckvo_visible(start_pos + t, ratio, n_c);
         for (int64_t s = 0; s < n_c; ++s) {
             if (s >= vis) {
@@ -413,7 +430,8 @@ int64_t sckvo_index_scores(const uint16_t* q_raw, const uint16_t* k_hat, const f
             }
             for (int h = 0; h < Hi; ++h) {
                 int ex = 0;
-                double d = oracle_exact_dot(qh + (int64_t)h * Di, k_hat + s * (int64_t)Di, Di, &ex);
+                double d = oracle_exact_dot(qm + (int64_t)h * Di, qe + (int64_t)h * Di, km + s * (int64_t)Di,
+                                            ke + s * (int64_t)Di, Di, &ex);
                 if (!ex) ++inexact;
                 float df = (float)d;
                 float relu = (df > 0.0f) ? df : 0.0f;
@@ -424,6 +442,10 @@ int64_t sckvo_index_scores(const uint16_t* q_raw, const uint16_t* k_hat, const f
             scores[i * n_c + s] = sckvo_f32_to_bf16(r[0]);
         }
     }
+    free(qm);
+    free(qe);
+    free(km);
+    free(ke);
     free(qh);
     free(r);
     return inexact;

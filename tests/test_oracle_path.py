@@ -29,31 +29,21 @@ def vals(bits):
 # Ring (forward.rs: the window ring's stream-ordered copies)
 # --------------------------------------------------------------------------
 
-def _page_split_copy(ring, kv, win):
-    """The page's two bulk copies at start_pos 0 with m > win: the last win
-    rows, split at cutoff = m mod win (an independent formulation)."""
-    m = kv.shape[0]
-    cutoff = m % win
-    tail = kv[m - win:]
-    ring = ring.copy()
-    ring[cutoff:win] = tail[: win - cutoff]
-    ring[:cutoff] = tail[win - cutoff:]
-    return ring
-
-
 @pytest.mark.parametrize("m", [1, 5, 16, 17, 40, 48, 131])
-def test_ring_prefill_matches_page_copies(m):
+def test_ring_prefill_slots_closed_form(m):
+    """start_pos 0: the ring holds the last min(m, win) rows, the row of
+    position p in slot p mod win; slots no position reached keep their old rows."""
     win, D = 16, 4
     rng = np.random.default_rng(m)
     kv = rng.integers(0, 60000, size=(m, D)).astype(np.uint16)
-    ring0 = np.zeros((win, D), np.uint16)
+    ring0 = rng.integers(0, 60000, size=(win, D)).astype(np.uint16)
     got = oracle.ring_write(ring0, kv, 0)
-    if m <= win:
-        want = ring0.copy()
-        want[:m] = kv
-    else:
-        want = _page_split_copy(ring0, kv, win)
-    assert np.array_equal(got, want)
+    written = set()
+    for p in range(max(0, m - win), m):
+        assert np.array_equal(got[p % win], kv[p]), p
+        written.add(p % win)
+    for j in set(range(win)) - written:
+        assert np.array_equal(got[j], ring0[j]), j
 
 
 def test_ring_against_deque():
@@ -252,6 +242,29 @@ def test_score_visibility_and_exactness_flag():
     ki[0, 0], ki[0, 32] = 1.0, 1.0
     _, bad = oracle.index_scores(bf16_of(qi), bf16_of(ki), np.ones((1, 1), np.float32), start_pos=0, ratio=1)
     assert bad == 1
+
+
+def test_score_exactness_flag_counts_partial_sums():
+    """Exactness is a property of every partial sum, not only of the final
+    value: q blocks of 2^24, 1 and -2^24 against a row of ones give the exact
+    dot 1 (a binary32 value), but the partial sum 2^24 + 1 is not one, so a
+    binary32 accumulation in that order returns 0.  The dot must be flagged."""
+    qi = np.zeros((1, 1, 128), np.float32)
+    qi[0, 0, 0], qi[0, 0, 32], qi[0, 0, 64] = 2.0**24, 1.0, -(2.0**24)
+    ki = np.ones((1, 128), np.float32)
+    qb, kb = bf16_of(qi), bf16_of(ki)
+    assert np.array_equal(oracle.quant(qb.reshape(-1), oracle.E8M0_B32), qb.reshape(-1))  # on the fp4 grid
+    assert np.array_equal(oracle.quant(kb.reshape(-1), oracle.E8M0_B32), kb.reshape(-1))
+    acc = np.float32(0)
+    for v in (2.0**24, 1.0, -(2.0**24)):
+        acc = np.float32(acc + np.float32(v))
+    assert acc == 0.0  # the in-order binary32 sum loses the 1
+    _, bad = oracle.index_scores(qb, kb, np.ones((1, 1), np.float32), start_pos=0, ratio=1)
+    assert bad == 1
+    # the same magnitudes without cancellation (2^23 + 1 + 2^23 < 2^24 units) are exact in every order
+    qi[0, 0, 0], qi[0, 0, 64] = 2.0**22, 2.0**22
+    _, bad = oracle.index_scores(bf16_of(qi), kb, np.ones((1, 1), np.float32), start_pos=0, ratio=1)
+    assert bad == 0
 
 
 def test_score_dots_exact_on_workload_shapes():
