@@ -3,6 +3,9 @@
 The reference step calls only oracle/ (plain C, CPU) on the raw seeded inputs;
 it never sees a value produced by the HIP path.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -35,26 +38,53 @@ def oracle_rows_a(w, x, b: int) -> np.ndarray:
     return np.concatenate([ring, kv], axis=0)
 
 
-def oracle_step(w, x, b: int = 0, qsel=None):
-    """The oracle's index lists [len(qsel), T] and float64 outputs
-    [len(qsel), H, D] for instance b of a step of workload w."""
+def oracle_threads() -> int:
+    """Worker threads for oracle calls over many queries (the oracle releases
+    the GIL inside its C calls; each query's result is independent of the
+    others, so splitting the queries changes nothing)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _chunked(fn, qsel, threads):
+    """fn(sub-array of qsel) over contiguous chunks, results concatenated."""
+    if threads <= 1 or qsel.size < 2 * threads:
+        return fn(qsel)
+    parts = np.array_split(qsel, threads * 4)
+    with ThreadPoolExecutor(threads) as ex:
+        res = list(ex.map(fn, [p for p in parts if p.size]))
+    return np.concatenate(res, axis=0)
+
+
+def oracle_step(w, x, b: int = 0, qsel=None, attn_qsel=None, threads: int = 1):
+    """The oracle's index lists [len(qsel), T] and float64 attention outputs
+    [len(attn_qsel), H, D] (attn_qsel defaults to qsel) for instance b of a
+    step of workload w; threads > 1 splits the queries over worker threads."""
     qsel = np.arange(w.m, dtype=np.int64) if qsel is None else np.asarray(qsel, dtype=np.int64)
+    attn_qsel = qsel if attn_qsel is None else np.asarray(attn_qsel, dtype=np.int64)
     latent = oracle.quant(bits(x["latent_raw"][b]).reshape(-1), oracle.E4M3_B16).reshape(w.n_c, w.D)
     rows_a = oracle_rows_a(w, x, b)
     widx, ra = oracle.window_idx(w.win, w.m, w.start_pos)
     assert ra == rows_a.shape[0]
+    need = np.union1d(qsel, attn_qsel)
     if w.Hi:
         k = oracle.quant(bits(x["ik_raw"][b]).reshape(-1), oracle.E8M0_B32).reshape(w.n_c, w.Di)
-        cidx, inexact = oracle.compressed_idx(bits(x["iq"][b]), k, x["iw"][b].numpy(), w.start_pos, w.ratio, w.K, ra,
-                                              qsel)
-        assert inexact == 0, "indexer dot outside the exactness condition"
+        iq, iw = bits(x["iq"][b]), x["iw"][b].numpy()
+
+        def comp(sel):
+            c, inexact = oracle.compressed_idx(iq, k, iw, w.start_pos, w.ratio, w.K, ra, sel)
+            assert inexact == 0, "indexer dot outside the exactness condition"
+            return c
+
+        cidx = _chunked(comp, need, threads)
     else:
-        cidx = oracle.visible_idx(w.m, w.start_pos, w.ratio, w.n_c, w.K, ra)[qsel]
-    idx_sel = np.concatenate([widx[qsel], cidx], axis=1).astype(np.int32)
+        cidx = oracle.visible_idx(w.m, w.start_pos, w.ratio, w.n_c, w.K, ra)[need]
+    idx_need = np.concatenate([widx[need], cidx], axis=1).astype(np.int32)
     idx_full = np.full((w.m, w.T), -1, dtype=np.int32)
-    idx_full[qsel] = idx_sel
-    out = oracle.sparse_attn(bits(x["q"][b]), rows_a, latent, idx_full, x["sink"].numpy(), w.scale, qsel)
-    return idx_sel, out
+    idx_full[need] = idx_need
+    q, sink = bits(x["q"][b]), x["sink"].numpy()
+    out = _chunked(lambda sel: oracle.sparse_attn(q, rows_a, latent, idx_full, sink, w.scale, sel), attn_qsel,
+                   threads)
+    return idx_full[qsel], out
 
 
 def attn_tolerance_ok(gpu: np.ndarray, ref: np.ndarray):
@@ -63,6 +93,13 @@ def attn_tolerance_ok(gpu: np.ndarray, ref: np.ndarray):
     bound = 1e-2 * np.abs(ref).max() + 1e-3
     err = np.abs(gpu.astype(np.float64) - ref)
     return bool(np.all(err <= bound)), float(err.max() / bound)
+
+
+def spread_queries(w, n: int = 256):
+    """About n queries spread evenly over the step (first and last included),
+    plus the edge cases of sample_queries."""
+    grid = np.unique(np.linspace(0, w.m - 1, min(n, w.m)).round().astype(np.int64))
+    return np.union1d(grid, sample_queries(w))
 
 
 def sample_queries(w, extra: int = 4, seed: int = 0):
