@@ -255,6 +255,28 @@ int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const v
                           void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sckv_sparse_attn_sink_noalloc -- sckv_sparse_attn_sink for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same arguments without the
+ * workspace, the same kernels and the same results bit for bit.  The split
+ * partials that sckv_sparse_attn_sink keeps in the caller's workspace live in
+ * a static device array of sckv_sparse_attn_sink_noalloc_max_bytes() bytes
+ * (32 MiB) that the library holds on each GPU it runs on until the process
+ * ends; the call allocates nothing.  Shapes whose partials need more than
+ * that (sckv_workspace_bytes(SCKV_OP_SPARSE_ATTN_SINK, ...) above the
+ * maximum, e.g. 64 heads x 512 at fewer than 256 queries with long lists)
+ * return SCKV_EUNSUPPORTED with nothing enqueued.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller.
+ */
+int sckv_sparse_attn_sink_noalloc(const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
+                                  const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m, int H,
+                                  int D, void* out, void* stream);
+
+/* Bytes of the static scratch of sckv_sparse_attn_sink_noalloc. */
+size_t sckv_sparse_attn_sink_noalloc_max_bytes(void);
+
+/*
  * sckv_workspace_bytes -- device workspace an operation needs for the given
  * shape: op = SCKV_OP_INDEX_SCORES_TOPK or SCKV_OP_INDEX_SCORES_TOPK_FP4 with
  * (H, D, n) = (Hi, Di, n_c), or SCKV_OP_SPARSE_ATTN_SINK with (H, D, n) =

@@ -31,6 +31,8 @@ from ._binding import (  # noqa: F401
     sckv_ring_write,
     sckv_rows_a_len,
     sckv_sparse_attn_sink,
+    sckv_sparse_attn_sink_noalloc,
+    sckv_sparse_attn_sink_noalloc_max_bytes,
     sckv_visible_idx,
     sckv_window_idx,
     sckv_workspace_bytes,

@@ -56,6 +56,10 @@ def _load():
                                              vp, i64, i64, vp, vp, sz, vp]
     L.sckv_sparse_attn_sink.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32, vp,
                                         vp, sz, vp]
+    L.sckv_sparse_attn_sink_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32,
+                                                i32, vp, vp]
+    L.sckv_sparse_attn_sink_noalloc_max_bytes.argtypes = []
+    L.sckv_sparse_attn_sink_noalloc_max_bytes.restype = sz
     L.sckv_workspace_bytes.argtypes = [i32, i32, i64, i32, i32, i64]
     L.sckv_workspace_bytes.restype = sz
     L.sckv_last_error.argtypes = []
@@ -224,3 +228,17 @@ def sckv_sparse_attn_sink(q: torch.Tensor, rows_a: torch.Tensor, ra: int, rows_b
         _ptr(rows_b, torch.bfloat16, "rows_b"), rb, _ptr(idx, torch.int32, "idx"), T,
         _ptr(sink, torch.float32, "sink"), float(scale), B, m, H, D, _ptr(out, torch.bfloat16, "out"),
         _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sckv_sparse_attn_sink_noalloc(q: torch.Tensor, rows_a: torch.Tensor, ra: int, rows_b: torch.Tensor | None,
+                                  rb: int, idx: torch.Tensor, T: int, sink: torch.Tensor, scale: float, B: int, m: int,
+                                  H: int, D: int, out: torch.Tensor, stream=None):
+    _check("sckv_sparse_attn_sink_noalloc", lib.sckv_sparse_attn_sink_noalloc(
+        _ptr(q, torch.bfloat16, "q"), _ptr(rows_a, torch.bfloat16, "rows_a"), ra,
+        _ptr(rows_b, torch.bfloat16, "rows_b"), rb, _ptr(idx, torch.int32, "idx"), T,
+        _ptr(sink, torch.float32, "sink"), float(scale), B, m, H, D, _ptr(out, torch.bfloat16, "out"),
+        _stream(stream)))
+
+
+def sckv_sparse_attn_sink_noalloc_max_bytes() -> int:
+    return int(lib.sckv_sparse_attn_sink_noalloc_max_bytes())

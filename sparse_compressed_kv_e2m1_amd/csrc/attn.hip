@@ -43,6 +43,9 @@
 // factors) in LDS, and after one more barrier every wave accumulates O for
 // all 64 heads over its own 128 columns, which reads each row byte once per
 // wave instead of once per head group.
+#include <mutex>
+#include <string>
+
 #include "mfma.h"
 #include "sckv_device.h"
 
@@ -801,31 +804,35 @@ size_t attn_workspace_bytes(int B, int64_t m, int H, int D, int64_t T) {
 
 }  // namespace sckv
 
-extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
-                                     const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m,
-                                     int H, int D, void* out, void* ws, size_t ws_bytes, void* stream) {
-    using namespace sckv;
+namespace sckv {
+namespace {
+
+// The whole call (checks, attention launch, combine of split partials) with
+// the partials in ws; `name` prefixes error messages.
+int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
+             const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m, int H, int D, void* out,
+             void* ws, size_t ws_bytes, void* stream) {
     if (B < 0 || m < 0 || ra < 0 || rb < 0 || H <= 0 || D <= 0 || T < 0)
-        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: bad sizes");
-    if (H > 64) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: H > 64");
+        return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
+    if (H > 64) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": H > 64");
     if (D != 64 && D != 128 && D != 256 && D != 512)
-        return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: D not in {64, 128, 256, 512}");
-    if (T > 65536) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: T > 65536");
+        return fail(SCKV_EUNSUPPORTED, std::string(name) + ": D not in {64, 128, 256, 512}");
+    if (T > 65536) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": T > 65536");
     if (B == 0 || m == 0) return SCKV_OK;
-    if (T == 0) return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: T == 0");
+    if (T == 0) return fail(SCKV_EINVAL, std::string(name) + ": T == 0");
     if (!q || !idx || !sink || !out || (ra > 0 && !rows_a) || (rb > 0 && !rows_b))
-        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: null pointer");
+        return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
     if ((uintptr_t)q % 16 || (uintptr_t)rows_a % 16 || (uintptr_t)rows_b % 16 || (uintptr_t)out % 16 ||
         (uintptr_t)idx % 4 || (uintptr_t)sink % 4)
-        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: q / rows / out must be 16-byte aligned");
-    if (ra + rb > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: ra + rb >= 2^31");
-    if (!(scale > 0.0f) || !(scale < INFINITY)) return fail(SCKV_EINVAL, "sckv_sparse_attn_sink: bad scale");
+        return fail(SCKV_EINVAL, std::string(name) + ": q / rows / out must be 16-byte aligned");
+    if (ra + rb > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": ra + rb >= 2^31");
+    if (!(scale > 0.0f) || !(scale < INFINITY)) return fail(SCKV_EINVAL, std::string(name) + ": bad scale");
     const int64_t nq = (int64_t)B * m;
     int cps, nsplit;
     attn_split(nq, T, &cps, &nsplit);
-    if (nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: grid too large");
+    if (nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": grid too large");
     const size_t need = attn_workspace_bytes(B, m, H, D, T);
-    if (need && (!ws || ws_bytes < need)) return fail(SCKV_EWORKSPACE, "sckv_sparse_attn_sink: workspace too small");
+    if (need && (!ws || ws_bytes < need)) return fail(SCKV_EWORKSPACE, std::string(name) + ": workspace too small");
     float* part_o = nullptr;
     float* part_ml = nullptr;
     if (nsplit > 1) {
@@ -851,8 +858,71 @@ extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t 
     }
 #undef SCKV_ATTN
     if (rc || nsplit == 1) return rc;
-    if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink: too many queries");
+    if (nq > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": too many queries");
     combine_kernel<<<dim3((unsigned)nq, (unsigned)H), dim3(COMBINE_THREADS), 0, s>>>(part_o, part_ml, sink, nsplit, H,
                                                                                     D, oo);
-    return check_launch("sckv_sparse_attn_sink (combine)");
+    return check_launch(name);
+}
+
+// Scratch of the no-allocation entry point: the split partials live in this
+// file-scope device array (one copy per GPU, held until the process ends).
+// Host code never uses the array's name as an address: it asks the runtime
+// for the device address once per device (scratch_ptr) and passes that.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[64] = {nullptr};
+
+// Device address of this device's copy of `scratch` (looked up on the first
+// call on each device, with that device current).
+int scratch_ptr(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink_noalloc: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink_noalloc: device index >= 64");
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink_noalloc: hipGetSymbolAddress: ") +
+                                       hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SCKV_OK;
+}
+
+}  // namespace
+}  // namespace sckv
+
+extern "C" int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
+                                     const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m,
+                                     int H, int D, void* out, void* ws, size_t ws_bytes, void* stream) {
+    return sckv::attn_run("sckv_sparse_attn_sink", q, rows_a, ra, rows_b, rb, idx, T, sink, scale, B, m, H, D, out,
+                          ws, ws_bytes, stream);
+}
+
+extern "C" size_t sckv_sparse_attn_sink_noalloc_max_bytes(void) { return sckv::NOALLOC_SCRATCH_BYTES; }
+
+extern "C" int sckv_sparse_attn_sink_noalloc(const void* q, const void* rows_a, int64_t ra, const void* rows_b,
+                                             int64_t rb, const int32_t* idx, int T, const float* sink, float scale,
+                                             int B, int64_t m, int H, int D, void* out, void* stream) {
+    using namespace sckv;
+    if (B < 0 || m < 0 || H <= 0 || D <= 0 || T < 0)
+        return fail(SCKV_EINVAL, "sckv_sparse_attn_sink_noalloc: bad sizes");
+    const size_t need = attn_workspace_bytes(B, m, H, D, T);
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink_noalloc: this shape needs " + std::to_string(need) +
+                                           " bytes of split partials, more than the " +
+                                           std::to_string(NOALLOC_SCRATCH_BYTES) +
+                                           " bytes of static scratch; call sckv_sparse_attn_sink with a workspace");
+    void* ws = nullptr;
+    if (need) {
+        const int rc = scratch_ptr(&ws);
+        if (rc) return rc;
+    }
+    return attn_run("sckv_sparse_attn_sink_noalloc", q, rows_a, ra, rows_b, rb, idx, T, sink, scale, B, m, H, D, out,
+                    ws, NOALLOC_SCRATCH_BYTES, stream);
 }
