@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, datasheet
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, datasheet
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA, datasheet
 
 DEFAULT_B = {"tiny_decode": 1, "decode": 2048, "long_decode": 512, "causal_prefill": 1, "chunked_prefill": 1}
 
@@ -76,9 +77,13 @@ def counts(w, B, call, kcache="bf16"):
     if call == "visible_idx":
         return {"bytes": B * m * w.K * 4, "flops": 0, "bound": "hbm"}
     if call == "index_scores_topk":
+        # flops: only queries that see more than K rows need scores (a query
+        # seeing V <= K rows selects all of them); the all-visible-pairs count
+        # is reported beside it
         by = B * (max(V) * krow + m * w.Hi * w.Di * 2 + m * w.Hi * 4 + m * w.K * 4)
-        fl = B * sum(V) * w.Hi * w.Di * 2
-        return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm"}
+        fl = B * sum(v for v in V if v > w.K) * w.Hi * w.Di * 2
+        return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm",
+                "flops_all_visible": B * sum(V) * w.Hi * w.Di * 2}
     if call == "sparse_attn_sink":
         rows = (w.m if w.start_pos == 0 else (win + m if m > 1 else None))
         row_bytes = (rows + w.n_c) * D * 2 if rows is not None else pairs * D * 2
@@ -94,6 +99,8 @@ def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
+        if f == "peak.hip":  # measurement kernels, not the hot path
+            continue
         text = open(os.path.join(csrc, f), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
@@ -234,34 +241,245 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
     log(f"wrote {out} and {tj}")
 
 
-def cpu_baseline(w, seconds):
-    """The oracle as it stands, single-threaded, on a bounded sample of the same
-    workload (one sequence; decode: whole steps, prefill: sampled queries)."""
+def cpu_info():
+    """Host CPU model and the CPUs this process may run on."""
+    model = None
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_available": avail}
+
+
+def cpu_baseline(w, seconds, threads):
+    """The oracle as it stands on a bounded sample of the same workload, on one
+    thread and on `threads` threads (the oracle's C calls release the GIL;
+    work is split over independent sequences for decode, over the queries of
+    one step for prefill, which changes no result).  Decode: whole steps of one
+    sequence each; prefill: sampled query tokens of one step (index list +
+    attention per query)."""
     import numpy as np  # noqa: PLC0415
+    from concurrent.futures import ThreadPoolExecutor  # noqa: PLC0415
 
     import sckv_synth as synth  # noqa: PLC0415
     from tests.helpers import oracle_step, sample_queries  # noqa: PLC0415
 
     x = synth.make_inputs(w, 1)
-    tokens, t0 = 0, time.perf_counter()
-    if w.m == 1:
-        while True:
+    qs = None if w.m == 1 else np.concatenate([sample_queries(w, extra=64, seed=1),
+                                               np.random.default_rng(2).integers(0, w.m, size=4096)])
+
+    def unit(i):
+        if w.m == 1:
             oracle_step(w, x, 0)
-            tokens += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        sample = f"{tokens} whole decode step(s) of one sequence"
-    else:
-        qs = sample_queries(w, extra=64, seed=1)
-        for t in qs:
-            oracle_step(w, x, 0, np.array([t]))
-            tokens += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        sample = f"{tokens} query token(s) of one {w.m}-token step (index lists + attention per query)"
-    el = time.perf_counter() - t0
-    return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample,
-            "seconds": round(el, 2)}
+        else:
+            oracle_step(w, x, 0, np.array([qs[i % qs.size]]))
+        return 1
+
+    def timed(nthreads):
+        tokens, i, t0 = 0, 0, time.perf_counter()
+        with ThreadPoolExecutor(nthreads) as ex:
+            while time.perf_counter() - t0 < seconds:
+                tokens += sum(ex.map(unit, range(i, i + nthreads)))
+                i += nthreads
+        return tokens, time.perf_counter() - t0
+
+    t1, e1 = timed(1)
+    tn, en = timed(threads)
+    what = "whole decode step(s) of one sequence" if w.m == 1 else \
+        f"query token(s) of one {w.m}-token step (index list + attention per query)"
+    out = {"value": tn / en, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{tn} {what} on {threads} threads in {en:.1f} s",
+           "single_thread": {"value": t1 / e1, "cores": 1, "sample": f"{t1} {what} in {e1:.1f} s"}}
+    out.update(cpu_info())
+    return out
+
+
+def peak_lib():
+    import ctypes  # noqa: PLC0415
+
+    path = os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "libsckv_peak.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is missing: build first (python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(path)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.sckv_peak_copy.argtypes = [vp, vp, i64, i32, i32, vp]
+    L.sckv_peak_read.argtypes = [vp, i64, vp, i32, i32, vp]
+    L.sckv_peak_mfma.argtypes = [i32, i64, i32, vp, vp]
+    L.sckv_peak_mfma_flops.argtypes = [i32, i64, i32]
+    L.sckv_peak_mfma_flops.restype = ctypes.c_double
+    L.sckv_peak_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def measure_peaks():
+    """The roofline denominators re-measured on this GPU (libsckv_peak.so):
+    a 2 GiB copy and a 4 GiB read (past the 256 MB last-level cache), and
+    dense matrix-core loops for bf16 and for e2m1 x e2m1 with block scales.
+    Each figure is the best over a small sweep of launch shapes (workgroups,
+    loads in flight) of a few launches each, timed with HIP events."""
+    import torch  # noqa: PLC0415
+
+    L = peak_lib()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def best(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn()
+            b.record(stream)
+            if rc:
+                raise RuntimeError(L.sckv_peak_last_error().decode())
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return min(a.elapsed_time(b) for a, b in ts) / 1e3
+
+    n = 2 << 30
+    src = torch.empty(2 * n, dtype=torch.uint8, device="cuda").fill_(3)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    out = torch.empty(ncu * 32 * 256, dtype=torch.int32, device="cuda")
+    shapes = [(ncu * wpc, depth) for wpc in (4, 8, 16, 32) for depth in (4, 8, 16)]
+    t_copy = min(best(lambda: L.sckv_peak_copy(src.data_ptr(), dst.data_ptr(), n, g, d, sp), 3) for g, d in shapes)
+    t_read = min(best(lambda: L.sckv_peak_read(src.data_ptr(), 2 * n, out.data_ptr(), g, d, sp), 3) for g, d in shapes)
+    del src, dst
+    res = {"hbm_copy_GBs": round(2 * n / t_copy / 1e9, 1), "hbm_read_GBs": round(2 * n / t_read / 1e9, 1),
+           "copy_bytes": n, "read_bytes": 2 * n}
+    fo = torch.empty(ncu * 4 * 256, dtype=torch.float32, device="cuda")
+    iters = 512
+    for kind, name in ((0, "bf16_mfma_TFLOPs"), (1, "fp4_mfma_TFLOPs")):
+        res[name] = round(max(L.sckv_peak_mfma_flops(kind, iters, ncu * wpc)
+                              / best(lambda: L.sckv_peak_mfma(kind, iters, ncu * wpc, fo.data_ptr(), sp), reps=3)
+                              / 1e12 for wpc in (1, 2, 4)), 1)
+    torch.cuda.empty_cache()
+    return res
+
+
+def roofline_of(cnt, ms, peaks=None, dtype=None):
+    """Achieved rate of a call against the datasheet peak (and the measured
+    one when given) of its bound: HBM bytes, or matrix-core flops of its
+    contraction's dtype (bf16, or fp4 for the packed indexer)."""
+    if cnt["bound"] == "hbm":
+        achieved = cnt["bytes"] / (ms / 1e3) / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": round(achieved / HBM_PEAK_GBS, 4)}
+        if peaks:
+            r["measured_peak"] = peaks["hbm_read_GBs"]
+            r["frac_measured"] = round(achieved / peaks["hbm_read_GBs"], 4)
+        return r
+    achieved = cnt["flops"] / (ms / 1e3) / 1e12
+    pk = FP4_PEAK_TFLOPS if dtype == "fp4" else BF16_PEAK_TFLOPS
+    r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": pk, "unit": "TFLOP/s", "frac": round(achieved / pk, 4),
+         "contraction": dtype or "bf16"}
+    if dtype == "fp4":
+        r["frac_of_bf16_peak"] = round(achieved / BF16_PEAK_TFLOPS, 4)
+    if peaks:
+        mp = peaks["fp4_mfma_TFLOPs" if dtype == "fp4" else "bf16_mfma_TFLOPs"]
+        r["measured_peak"] = mp
+        r["frac_measured"] = round(achieved / mp, 4)
+    return r
+
+
+def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
+    """Time whole steps of workload w over B sequences (inputs drawn on the
+    device, resident before the timed region), then each library call with
+    events around it on the same stream; optionally the B = 1 latency."""
+    import torch  # noqa: PLC0415
+
+    import sckv_synth as synth  # noqa: PLC0415
+    from sparse_compressed_kv_e2m1_amd.step import PathState  # noqa: PLC0415
+
+    log(f"bench: workload {w.name} B={B}: generating inputs on the device")
+    x = synth.make_inputs(w, B, device="cuda")
+    st = PathState(w, x, B, kcache=kcache)
+    del x
+    st.setup()
+    calls = st.calls()
+    st._calls = calls
+    torch.cuda.synchronize()
+    log(f"bench: {w.name}: warmup {warmup}")
+    for _ in range(warmup):
+        st.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    run_step, launch = st.step, "eager"
+    if graph:
+        g = st.capture_graph()
+        run_step, launch = g.replay, "hip graph"
+        for _ in range(warmup):
+            run_step()
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        run_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / steps
+    log(f"bench: {w.name}: {steps} steps, {ms:.4f} ms/step (events), wall {wall * 1e3 / steps:.4f} ms/step")
+    per = {name: [] for name, _ in calls}
+    for _ in range(steps):
+        for name, f in calls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            per[name].append((a, b))
+    torch.cuda.synchronize()
+    per_ms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in per.items()}
+    log(f"bench: {w.name}: per call ms " + json.dumps({k: round(v, 5) for k, v in per_ms.items()}))
+    del st, calls
+    torch.cuda.empty_cache()
+
+    sing = None
+    if single and B > 1:
+        x1 = synth.make_inputs(w, 1, device="cuda")
+        s1 = PathState(w, x1, 1, kcache=kcache)
+        s1.setup()
+        for _ in range(warmup):
+            s1.step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            s1.step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms1 = a.elapsed_time(b) / steps
+        sing = {"instances": 1, "ms_per_step": round(ms1, 5), "tokens_per_s": round(w.m / (ms1 / 1e3), 1)}
+        del s1, x1
+        torch.cuda.empty_cache()
+
+    kc = kcache if w.Hi else "none"
+    dtypes = {"index_scores_topk": "fp4" if kcache == "fp4" else "bf16"}
+    call_info = {}
+    for name, t in per_ms.items():
+        cnt = counts(w, B, name, kcache)
+        r = roofline_of(cnt, t, peaks, dtypes.get(name))
+        r.update({"ms_per_launch": round(t, 5), "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
+                  "traffic": traffic_for(w.name, B, name, kc)})
+        if "flops_all_visible" in cnt:
+            r["flops_all_visible_pairs"] = cnt["flops_all_visible"]
+        call_info[name] = r
+    dom = max(per_ms, key=per_ms.get)
+    roof = dict(call_info[dom])
+    roof["kernel"] = dom
+    tokens = B * w.m
+    return {"workload": describe(w), "instances": B, "tokens_per_step": tokens, "value": round(tokens / (ms / 1e3), 1),
+            "ms_per_step": round(ms, 5), "indexer_k_cache": kcache if w.Hi else None, "step_launch": launch,
+            "roofline": roof, "calls": call_info, "single_instance": sing}
 
 
 def main():
@@ -273,8 +491,11 @@ def main():
     ap.add_argument("--instances", type=int, default=None, help="B independent sequences per step")
     ap.add_argument("--kcache", choices=["fp4", "bf16"], default="fp4",
                     help="indexer k cache storage: packed fp4 codes + E8M0 bytes (default) or bf16 rows")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--legs", default="long_decode,causal_prefill,chunked_prefill",
+                    help="other workloads timed in the same run and reported under 'legs' (comma list; '' = none)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per thread count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip re-measuring the HBM and matrix-core peaks")
     ap.add_argument("--no-single", action="store_true", help="skip the B = 1 latency run (for profiling)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph of one step (measured: within noise of the call-by-call "
@@ -311,120 +532,52 @@ def main():
     import torch  # noqa: PLC0415
 
     import sckv_synth as synth  # noqa: PLC0415
-    from sparse_compressed_kv_e2m1_amd.step import PathState  # noqa: PLC0415
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    peaks = None
+    if not args.no_peaks:
+        log("bench: re-measuring the HBM and matrix-core peaks")
+        peaks = measure_peaks()
+        log("bench: measured peaks " + json.dumps(peaks))
     w = synth.WORKLOADS[args.workload]
     B = args.instances or DEFAULT_B[args.workload]
-    log(f"bench: workload {w.name} B={B}: generating inputs on the device")
-    x = synth.make_inputs(w, B, device="cuda")
-    st = PathState(w, x, B, kcache=args.kcache)
-    del x
-    st.setup()
-    calls = st.calls()
-    st._calls = calls
-    torch.cuda.synchronize()
-
-    log(f"bench: warmup {args.warmup}")
-    for _ in range(args.warmup):
-        st.step()
-    torch.cuda.synchronize()
-
-    # whole steps, launched call by call, or (--graph) replayed from a HIP
-    # graph of one step (the same library calls, without per-launch host work)
-    stream = torch.cuda.current_stream()
-    run_step = st.step
-    launch = "eager"
-    if args.graph:
-        graph = st.capture_graph()
-        run_step = graph.replay
-        launch = "hip graph"
-        for _ in range(args.warmup):
-            run_step()
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        run_step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-    log(f"bench: {args.steps} steps, {ms:.4f} ms/step (events), wall {wall * 1e3 / args.steps:.4f} ms/step")
-
-    # per call, events on the same stream around each library call
-    per = {name: [] for name, _ in calls}
-    for _ in range(args.steps):
-        for name, f in calls:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            f()
-            b.record(stream)
-            per[name].append((a, b))
-    torch.cuda.synchronize()
-    per_ms = {n: sum(a.elapsed_time(b) for a, b in v) / len(v) for n, v in per.items()}
-    log("bench: per call ms " + json.dumps({k: round(v, 5) for k, v in per_ms.items()}))
-
-    # single sequence latency (B = 1) on the same workload
-    single = None
-    if B > 1 and not args.no_single:
-        x1 = synth.make_inputs(w, 1, device="cuda")
-        s1 = PathState(w, x1, 1, kcache=args.kcache)
-        s1.setup()
-        for _ in range(args.warmup):
-            s1.step()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            s1.step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms1 = a.elapsed_time(b) / args.steps
-        single = {"instances": 1, "ms_per_step": round(ms1, 5), "tokens_per_s": round(w.m / (ms1 / 1e3), 1)}
-        del s1, x1
-
-    tokens = B * w.m
-    value = tokens / (ms / 1e3)
-    dom = max(per_ms, key=per_ms.get)
-    cnt = counts(w, B, dom, args.kcache)
-    if cnt["bound"] == "hbm":
-        achieved = cnt["bytes"] / (per_ms[dom] / 1e3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = cnt["flops"] / (per_ms[dom] / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / BF16_PEAK_TFLOPS, 4)}
-    roof["kernel"] = dom
-    roof["ms_per_launch"] = round(per_ms[dom], 5)
-    roof["algorithmic_bytes"] = cnt["bytes"]
-    roof["algorithmic_flops"] = cnt["flops"]
-    roof["traffic"] = traffic_for(w.name, B, dom, args.kcache if w.Hi else "none")
+    head = run_leg(w, B, args.kcache, args.steps, args.warmup, single=not args.no_single, graph=args.graph,
+                   peaks=peaks)
+    legs = {}
+    for name in [n for n in args.legs.split(",") if n and n != w.name]:
+        lw = synth.WORKLOADS[name]
+        legs[name] = run_leg(lw, DEFAULT_B[name], args.kcache, args.steps, args.warmup, single=False,
+                             graph=args.graph, peaks=peaks)
 
     line = {
         "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",
-        "value": round(value, 1),
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
+        "dtype_note": ("attention: bf16 operands, f32 accumulation; indexer contraction: e2m1 x e2m1 with "
+                       "power-of-two block scales on the fp4 matrix cores (products and sums exact), bf16 scores"
+                       if args.kcache == "fp4" else "bf16 operands, f32 accumulation"),
         "data": "synthetic (seeded N(0,1), device generator)",
-        "config": {"workload": describe(w), "instances": B, "tokens_per_step": tokens,
-                   "indexer_k_cache": args.kcache if w.Hi else None, "step_launch": launch},
-        "roofline": roof,
-        "per_call_ms": {k: round(v, 5) for k, v in per_ms.items()},
-        "single_instance": single,
+        "config": {"workload": head["workload"], "instances": B, "tokens_per_step": head["tokens_per_step"],
+                   "indexer_k_cache": head["indexer_k_cache"], "step_launch": head["step_launch"]},
+        "roofline": head["roofline"],
+        "per_call_ms": {k: v["ms_per_launch"] for k, v in head["calls"].items()},
+        "calls": head["calls"],
+        "single_instance": head["single_instance"],
+        "legs": legs,
+        "measured_peaks": peaks,
     }
     if not args.no_cpu_baseline:
-        log(f"bench: timing the oracle on the host for ~{args.cpu_seconds:.0f} s")
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        threads = max(1, min(16, len(os.sched_getaffinity(0))))
+        log(f"bench: timing the oracle on the host (~{args.cpu_seconds:.0f} s on 1 and on {threads} threads)")
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, threads)
     print(json.dumps(line), flush=True)
 
 

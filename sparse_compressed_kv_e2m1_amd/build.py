@@ -15,6 +15,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsckv.so")
 SOURCES = ["abi.hip", "quant.hip", "window.hip", "decode.hip", "indexer.hip", "attn.hip"]
+# measurement kernels for the roofline denominators (not the hot path): a library of their own
+PEAK_LIB = os.path.join(HERE, "libsckv_peak.so")
+PEAK_SOURCES = ["peak.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -34,11 +37,12 @@ FLAGS = [
 
 
 def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source to an object in parallel, then link libsckv.so."""
+    """Compile every source to an object in parallel, then link libsckv.so
+    and libsckv_peak.so."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     procs, objs = [], []
-    for src in SOURCES:
+    for src in SOURCES + PEAK_SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
         objs.append(obj)
         cmd = [HIPCC, *[f for f in FLAGS if f != "-shared"], "-c", os.path.join(CSRC, src), "-o", obj]
@@ -56,12 +60,14 @@ def build(verbose: bool = False, jobs: int = 5) -> str:
             print("\n".join(lines))
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (PEAK_LIB, PEAK_SOURCES)):
+        tmp = lib + ".tmp"
+        mine = [o for o in objs if os.path.basename(o).replace(".o", ".hip") in srcs]
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *mine, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

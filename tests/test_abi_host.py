@@ -10,8 +10,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_calls():
-    src = open(os.path.join(ROOT, "include", "sckv.h")).read()
+def declared_calls(header="sckv.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(sckv_[a-z0-9_]+)\s*\(", src)))
 
@@ -32,6 +32,26 @@ def test_library_exports_every_declared_call():
     for n in declared_calls():
         assert hasattr(lib, n), n
     assert sk.sckv_abi_version() == 1
+    assert "sckv_sparse_attn_sink_noalloc" in declared_calls()
+    assert sk.sckv_sparse_attn_sink_noalloc_max_bytes() == 32 << 20
+
+
+def test_peak_library_exports_every_declared_call():
+    """The measurement kernels (roofline denominators) live in a library of
+    their own, declared in include/sckv_peak.h."""
+    peak = ctypes.CDLL(os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "libsckv_peak.so"))
+    names = declared_calls("sckv_peak.h")
+    assert {"sckv_peak_copy", "sckv_peak_read", "sckv_peak_mfma", "sckv_peak_mfma_flops"} <= set(names)
+    for n in names:
+        assert hasattr(peak, n), n
+    peak.sckv_peak_mfma_flops.restype = ctypes.c_double
+    peak.sckv_peak_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
+    assert peak.sckv_peak_mfma_flops(0, 10, 3) == 32 * 32 * 16 * 2 * 8 * 10 * 3 * 4
+    assert peak.sckv_peak_mfma_flops(1, 10, 3) == 32 * 32 * 64 * 2 * 8 * 10 * 3 * 4
+    peak.sckv_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_void_p]
+    assert peak.sckv_peak_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 63, 1, 4, None) == -1  # size
+    assert peak.sckv_peak_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 64, 1, 5, None) == -1  # depth
 
 
 def test_header_compiles_as_c():
@@ -41,7 +61,8 @@ def test_header_compiles_as_c():
 
     with tempfile.TemporaryDirectory() as d:
         c = os.path.join(d, "t.c")
-        open(c, "w").write('#include "sckv.h"\nint main(void){return sckv_abi_version() == 1 ? 0 : 1;}\n')
+        open(c, "w").write('#include "sckv.h"\n#include "sckv_peak.h"\n'
+                           'int main(void){return sckv_abi_version() == 1 ? 0 : 1;}\n')
         subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-I", os.path.join(ROOT, "include"),
                         c], check=True)
 
