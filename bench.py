@@ -164,9 +164,35 @@ def _csv_rows(folder, suffix):
     return list(csv.DictReader(open(paths[0])))
 
 
+# Matrix-core and LDS counters of one --pmc pass (6 SQ counters + 1 GRBM),
+# and the MI355X unit counts the ratios divide by.
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F6F4",
+               "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE"]
+CU_NUM, SIMD_NUM, XCD_NUM = 256, 1024, 8  # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
+
+
+def _sq_counters(folder):
+    """Per kernel (steady-state dispatches): the average per dispatch of each
+    counter of the SQ/ pass under folder, or {} without one."""
+    d = os.path.join(folder, "SQ")
+    if not os.path.isdir(d):
+        return {}
+    g = _steady_groups(_csv_rows(d, "counter_collection.csv"), lambda r: r["Grid_Size"])
+    out = {}
+    for k, rows in g.items():
+        nd = len({r["Dispatch_Id"] for r in rows})
+        acc, span = {}, {}
+        for r in rows:
+            acc[r["Counter_Name"]] = acc.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            span[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        out[k] = {c: v / nd for c, v in acc.items()}
+        out[k]["duration_ns"] = sum(span.values()) / len(span)
+    return out
+
+
 def summarize_profiles(w, B, folder, commands, kcache="bf16"):
     """Turn rocprofv3 output under `folder` (trace/, FETCH_SIZE/, WRITE_SIZE/,
-    copy_FETCH_SIZE/, copy_WRITE_SIZE/) into the text summary
+    SQ/, copy_FETCH_SIZE/, copy_WRITE_SIZE/) into the text summary
     profiles/hot_path_kernels_<workload>_B<B>.txt and the HBM-traffic entries
     of profiles/traffic.json (counter KiB per dispatch, scaled so that a plain
     1 GiB device copy reads and writes 1 GiB)."""
@@ -209,6 +235,29 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
         rd = "-" if rd is None else f"{rd * scale['FETCH_SIZE'] / 1e6:.2f}"
         wr = "-" if wr is None else f"{wr * scale['WRITE_SIZE'] / 1e6:.2f}"
         lines.append(f"{k[:44]:<44} {calls[k]:>5} {dur[k]:>9.2f} {rd:>9} {wr:>9}")
+    sq = _sq_counters(folder)
+    if sq:
+        lines += ["#", "# matrix-core and LDS counters (one rocprofv3 --pmc pass: " + " ".join(SQ_COUNTERS) + ")",
+                  f"#   gui        = GRBM_GUI_ACTIVE / {XCD_NUM} (the counter is summed over the XCDs): active cycles",
+                  f"#   mfma_busy  = SQ_VALU_MFMA_BUSY_CYCLES / (gui x {SIMD_NUM} SIMDs)",
+                  "#   mfma_GFLOP = (SQ_INSTS_VALU_MFMA_MOPS_BF16 + SQ_INSTS_VALU_MFMA_MOPS_F6F4) x 512",
+                  f"#   lds_active = SQ_LDS_IDX_ACTIVE / (gui x {CU_NUM} CUs); "
+                  "bank_conf = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+                  "#   gui_GHz    = gui / the dispatch's duration in this pass (the clock the kernel ran at)",
+                  f"{'kernel':<44} {'mfma_busy':>9} {'mfma_GFLOP':>10} {'lds_active':>10} {'bank_conf':>9} "
+                  f"{'lds_instr':>10} {'gui_GHz':>7}"]
+        for k in sorted(dur, key=lambda k: -dur[k]):
+            c = sq.get(k)
+            if not c or not c.get("GRBM_GUI_ACTIVE"):
+                continue
+            gui = c["GRBM_GUI_ACTIVE"] / XCD_NUM
+            busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (gui * SIMD_NUM)
+            fl = (c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F6F4", 0)) * 512 / 1e9
+            act = c.get("SQ_LDS_IDX_ACTIVE", 0) / (gui * CU_NUM)
+            bc = c.get("SQ_LDS_BANK_CONFLICT", 0) / max(1.0, c.get("SQ_LDS_IDX_ACTIVE", 0))
+            ghz = gui / c["duration_ns"] if c.get("duration_ns") else float("nan")
+            lines.append(f"{k[:44]:<44} {busy:>9.1%} {fl:>10.2f} {act:>10.1%} {bc:>9.1%} "
+                         f"{c.get('SQ_INSTS_LDS', 0):>10.3g} {ghz:>7.2f}")
     lines += ["#", f"{'library call':<20} {'avg_us':>9} {'alg_MB':>9} {'hbm_MB':>9}"]
     entries = {}
     for call in dict.fromkeys(names):
