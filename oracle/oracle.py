@@ -76,6 +76,13 @@ def lib():
     L.sckvo_sparse_attn.argtypes = [_u16p, _u16p, _i64, _u16p, _i64, _i32p, _int, _f32p, ctypes.c_float, _int, _int,
                                     _i64p, _i64, _f64p]
     L.sckvo_sparse_attn.restype = _int
+    L.sckvo_yarn_freqs_cis.argtypes = [_int, _i64, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_float, _f32p]
+    L.sckvo_yarn_freqs_cis.restype = None
+    L.sckvo_latent_position.argtypes = [_i64, _int]
+    L.sckvo_latent_position.restype = _i64
+    L.sckvo_rope_rows.argtypes = [_u16p, _i64, _int, _int, _f32p, _i64, _i64p, _int, _u16p]
+    L.sckvo_rope_rows.restype = _int
     _lib = L
     return L
 
@@ -252,3 +259,39 @@ def compressed_idx(q_raw_bits, k_hat_bits, w, start_pos: int, ratio: int, K: int
         v = visible(start_pos + int(t), ratio, n_c)
         out[i] = topk(scores[i], v, K, offset)
     return out, bad
+
+
+# --- YaRN RoPE of the compressed latent (compress.rs yarn_freqs_cis; the rope
+# of a new latent group before its fp4 round trip and cache copy) -----------
+
+def yarn_freqs_cis(dim: int, seqlen: int, original_seq_len: int, base: float, factor: float, beta_fast: float,
+                   beta_slow: float):
+    """float32 [seqlen, dim/2, 2] table of (cos, sin) per position and pair."""
+    out = np.zeros((seqlen, dim // 2, 2), dtype=np.float32)
+    lib().sckvo_yarn_freqs_cis(dim, seqlen, original_seq_len, base, factor, beta_fast, beta_slow, out)
+    return out
+
+
+def latent_position(j: int, ratio: int) -> int:
+    """Position of compressed row j: the first position of its group."""
+    return lib().sckvo_latent_position(j, ratio)
+
+
+def rope_rows(x_bits, rope_dim: int, table, pos, inverse: bool = False):
+    """bf16 bits of the rows x [rows, cols] with their last rope_dim values
+    rotated at the positions pos [rows] (interleaved pairs)."""
+    x = _u16(x_bits)
+    rows, cols = x.shape
+    t = np.ascontiguousarray(table, dtype=np.float32)
+    pos = np.ascontiguousarray(pos, dtype=np.int64).reshape(-1)
+    y = np.empty_like(x)
+    if lib().sckvo_rope_rows(x, rows, cols, rope_dim, t.reshape(-1), t.shape[0], pos, int(inverse), y) != 0:
+        raise ValueError("oracle: position outside the rotation table")
+    return y
+
+
+def latent_rope_quant(x_bits, rope_dim: int, table, pos):
+    """The latent path of a new compressed row: rotate (bf16 result), then the
+    e4m3-scale fp4 round trip."""
+    r = rope_rows(x_bits, rope_dim, table, pos)
+    return quant(r.reshape(-1), E4M3_B16).reshape(r.shape)

@@ -548,3 +548,103 @@ int sckvo_sparse_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, con
     free(rp);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* YaRN RoPE of the compressed latent  [compress.rs: yarn_freqs_cis, and     */
+/* attention_any: a new latent group is rotated at its position, then fp4    */
+/* round-tripped with e4m3 scales, then copied into the cache; forward.rs:   */
+/* the rope call on the latent before fp4_quant and the cache copy]          */
+/* ------------------------------------------------------------------------ */
+
+/* The rotation table of the compressed layers for positions 0 .. seqlen-1
+ * (compress.rs yarn_freqs_cis), steps in the page's order:
+ *   1. pair i (0 <= i < dim/2) has the base frequency 1 / base^(2i/dim), in
+ *      binary32 (the exponent 2i/dim is itself a binary32 quotient);
+ *   2. in binary64, the correction dimension of a rotation count r is
+ *      dim * ln(L / (r * 2 * pi)) / (2 ln base) with L = original_seq_len;
+ *      low = max(floor(that of beta_fast), 0), high = min(ceil(that of
+ *      beta_slow), dim - 1), both then binary32;
+ *   3. ramp_i = clamp((i - low) / max(high - low, 0.001), 0, 1) and the
+ *      frequency becomes f/factor * ramp_i + f * (1 - ramp_i), in binary32 in
+ *      the page's operation order (f / factor * (1 - smooth) + f * smooth with
+ *      smooth = 1 - ramp);
+ *   4. entry (p, i) is (cos a, sin a) of the binary32 angle a = p * f_i.
+ * out is [seqlen][dim/2][2] binary32.  dim must be even and positive. */
+void sckvo_yarn_freqs_cis(int dim, int64_t seqlen, int64_t original_seq_len, float base, float factor,
+                          float beta_fast, float beta_slow, float* out) {
+    const int half = dim / 2;
+    float* f = (float*)malloc(sizeof(float) * (size_t)(half > 0 ? half : 1));
+    for (int i = 0; i < half; ++i) f[i] = 1.0f / powf(base, (float)(2 * i) / (float)dim);
+    const double two_ln_base = 2.0 * log((double)base);
+    const double c_fast = (double)dim * log((double)original_seq_len / ((double)beta_fast * 2.0 * M_PI)) / two_ln_base;
+    const double c_slow = (double)dim * log((double)original_seq_len / ((double)beta_slow * 2.0 * M_PI)) / two_ln_base;
+    double lo = floor(c_fast);
+    if (lo < 0.0) lo = 0.0;
+    double hi = ceil(c_slow);
+    if (hi > (double)(dim - 1)) hi = (double)(dim - 1);
+    const float low = (float)lo, high = (float)hi;
+    float span = high - low;
+    if (span < 1e-3f) span = 1e-3f;
+    for (int i = 0; i < half; ++i) {
+        float ramp = ((float)i - low) / span;
+        if (ramp < 0.0f) ramp = 0.0f;
+        if (ramp > 1.0f) ramp = 1.0f;
+        const float smooth = 1.0f - ramp;
+        f[i] = f[i] / factor * (1.0f - smooth) + f[i] * smooth;
+    }
+    for (int64_t p = 0; p < seqlen; ++p)
+        for (int i = 0; i < half; ++i) {
+            const float a = (float)p * f[i];
+            out[(p * half + i) * 2 + 0] = cosf(a);
+            out[(p * half + i) * 2 + 1] = sinf(a);
+        }
+    free(f);
+}
+
+/* Position of compressed row j of a layer with `ratio` positions a row: the
+ * first position of its group, j * ratio.  This is the page's g * ratio for
+ * the groups of a prefill from position 0 and its start_pos + 1 - ratio for
+ * the one group a decode step completes (j = (start_pos + 1) / ratio - 1);
+ * for a chunk at start_pos > 0 (an extension) the same rule names each new
+ * row's group. */
+int64_t sckvo_latent_position(int64_t j, int ratio) { return j * (int64_t)ratio; }
+
+/* Rotary embedding of bf16 rows (compress.rs and forward.rs name apply_rotary
+ * / rope without printing them; the reading used here): the last rope_dim
+ * values of each row of `cols` are rope_dim/2 pairs (2i, 2i+1) of the rope
+ * slice, pair i a complex number x0 + i x1 turned by the table angle (p, i)
+ * of the row's position p:
+ *   forward  y0 = x0 c - x1 s,  y1 = x0 s + x1 c
+ *   inverse  y0 = x0 c + x1 s,  y1 = x1 c - x0 s
+ * every product and sum one binary32 operation (no fused multiply-add), the
+ * result rounded to bf16 (the latent buffer the rotation writes holds bf16);
+ * the other values are copied.  table is [n_pos][rope_dim/2][2] (cos, sin);
+ * pos[r] is row r's position.  Returns -1 when a position is outside the
+ * table, else 0. */
+int sckvo_rope_rows(const uint16_t* x, int64_t rows, int cols, int rope_dim, const float* table, int64_t n_pos,
+                    const int64_t* pos, int inverse, uint16_t* y) {
+    const int half = rope_dim / 2;
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t p = pos[r];
+        if (p < 0 || p >= n_pos) return -1;
+        const uint16_t* xr = x + r * cols;
+        uint16_t* yr = y + r * cols;
+        for (int c = 0; c < cols; ++c) yr[c] = xr[c];
+        for (int i = 0; i < half; ++i) {
+            const int j = cols - rope_dim + 2 * i;
+            const float x0 = sckvo_bf16_to_f32(xr[j]), x1 = sckvo_bf16_to_f32(xr[j + 1]);
+            const float c = table[(p * half + i) * 2 + 0], s = table[(p * half + i) * 2 + 1];
+            float y0, y1;
+            if (!inverse) {
+                y0 = x0 * c - x1 * s;
+                y1 = x0 * s + x1 * c;
+            } else {
+                y0 = x0 * c + x1 * s;
+                y1 = x1 * c - x0 * s;
+            }
+            yr[j] = sckvo_f32_to_bf16(y0);
+            yr[j + 1] = sckvo_f32_to_bf16(y1);
+        }
+    }
+    return 0;
+}
