@@ -100,6 +100,50 @@ int sckv_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* 
                     int64_t cols, int mode, void* stream);
 
 /*
+ * sckv_yarn_freqs_cis -- HOST function: the rotation table of the compressed
+ * layers' latent rotary embedding (compress.rs yarn_freqs_cis), computed once
+ * per model on the host in binary32, in the page's order:
+ *   f_i   = 1 / base^(2i/dim) for pair i < dim/2;
+ *   low   = max(floor(d(beta_fast)), 0), high = min(ceil(d(beta_slow)), dim-1)
+ *           with d(r) = dim ln(original_seq_len / (2 pi r)) / (2 ln base)
+ *           (binary64, then binary32);
+ *   ramp  = clamp((i - low) / max(high - low, 0.001), 0, 1), smooth = 1 - ramp,
+ *   f_i   = f_i / factor * (1 - smooth) + f_i * smooth;
+ *   table[p][i] = (cos(p f_i), sin(p f_i)) with the binary32 angle p * f_i.
+ *   table  [seqlen, dim/2, 2] f32, HOST memory the caller owns (copy it to
+ *          the device for sckv_rope_quant_rows / sckv_decode_prepare).
+ * dim even and positive, base > 1, factor, beta_fast, beta_slow > 0, else
+ * SCKV_EINVAL.  No device work.
+ */
+int sckv_yarn_freqs_cis(float* table, int dim, int64_t seqlen, int64_t original_seq_len, float base, float factor,
+                        float beta_fast, float beta_slow);
+
+/*
+ * sckv_rope_quant_rows -- the latent path of new compressed rows (compress.rs
+ * attention_any, forward.rs AttnV41::forward: the new latent groups are
+ * rotated at their positions, then fp4 round-tripped with e4m3 scales in
+ * blocks of 16, then written to the cache): row r of x is turned at position
+ * pos0 + r * pos_step, then goes through sckv_quant_rows(SCKV_FP4_E4M3_B16).
+ * The rotation (apply_rotary, not printed; the reading implemented): the last
+ * rope_dim values of a row are rope_dim/2 pairs (2i, 2i+1) of that slice,
+ * pair i of the row at position p becomes
+ *   (x0 c - x1 s, x0 s + x1 c),  (c, s) = table[p][i],
+ * with binary32 products and sums (no fused multiply-add), each result
+ * rounded to bf16 (the latent buffer holds bf16) before the round trip; the
+ * other values pass unchanged.  Compressed row j's position is j * ratio
+ * (the page's g * ratio from position 0, start_pos + 1 - ratio in decode).
+ *   x, y   [rows, cols] bf16, row strides ldx / ldy; in place allowed (x == y,
+ *          ldx == ldy), other overlap not
+ *   table  [n_pos, rope_dim/2, 2] f32 device array (sckv_yarn_freqs_cis),
+ *          8-byte aligned
+ * cols % 16 == 0, rope_dim even with 0 < rope_dim <= cols, pos0 >= 0,
+ * pos_step >= 0 and every row's position below n_pos, else SCKV_EINVAL.
+ */
+int sckv_rope_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                         const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
+                         void* stream);
+
+/*
  * sckv_ring_write -- write this step's m kv rows into the window ring: the row
  * of position p goes to slot p mod win; only the last min(m, win) positions
  * are written (forward.rs: the ring's one or two stream-ordered copies at
@@ -143,6 +187,7 @@ int sckv_window_idx(int B, int64_t m, int64_t start_pos, int win, int32_t* idx, 
  * fp4_quant_e4m3_inplace, fp4_quant_e8m0_inplace).  The result is exactly
  * that of, in any order (the four write disjoint memory):
  *   sckv_quant_rows(lat_new, ld_lat_new, lat_dst, ld_lat_dst, B, D, SCKV_FP4_E4M3_B16)
+ *     (sckv_rope_quant_rows with the same rows when rope_table is given)
  *   sckv_quant_pack(k_new, ld_k_new, k_codes, ld_codes, k_scales, ld_scales, B, Di, SCKV_FP4_E8M0_B32)
  *   sckv_ring_write(kv_new, ld_kv_new, ring, ld_ring, B, 1, start_pos, win, D)
  *   sckv_window_idx(B, 1, start_pos, win, idx, ld_idx)
@@ -156,6 +201,11 @@ int sckv_window_idx(int B, int64_t m, int64_t start_pos, int win, int32_t* idx, 
  *   kv_new     [B] new kv rows of D bf16, stride ld_kv_new
  *   ring       [B, win, D] bf16, stride ld_ring per sequence (>= win*D)
  *   idx        [B, 1, ld_idx] int32; columns 0 .. win-1 written
+ *   rope_table the rotation table ([n_pos, rope_dim/2, 2] f32 on the device,
+ *              sckv_yarn_freqs_cis), or NULL: with a table the latent rows
+ *              are turned at position lat_pos before their round trip, exactly
+ *              as sckv_rope_quant_rows(lat_new, ld_lat_new, lat_dst,
+ *              ld_lat_dst, B, D, rope_table, n_pos, rope_dim, lat_pos, 0)
  * D % 16 == 0, Di % 32 == 0; every row pointer 16-byte aligned and every
  * stride a multiple of 16 bytes (ld_scales excepted), else SCKV_EINVAL.
  */
@@ -163,7 +213,7 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
                         const void* k_new, int64_t ld_k_new, void* k_codes, int64_t ld_codes, void* k_scales,
                         int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new, void* ring,
                         int64_t ld_ring, int B, int D, int win, int64_t start_pos, int32_t* idx, int64_t ld_idx,
-                        void* stream);
+                        const float* rope_table, int64_t n_pos, int rope_dim, int64_t lat_pos, void* stream);
 
 /*
  * sckv_visible_idx -- the compressed part of every query's index list when
@@ -288,7 +338,7 @@ size_t sckv_workspace_bytes(int op, int B, int64_t m, int H, int D, int64_t n);
 /* Thread-local description of the last failed call on this thread ("" if none). */
 const char* sckv_last_error(void);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int sckv_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,6 +35,15 @@ class Workload:
     Di: int           # indexer head dim
     K: int            # compressed columns of the index list (top-k, or all visible)
     seed: int = 0
+    # rotary embedding of the latent rows (the last rope_dim values of a row;
+    # YaRN table parameters -- the pages print none, these are the model
+    # family's published settings)
+    rope_dim: int = 64
+    rope_base: float = 10000.0
+    rope_factor: float = 40.0
+    rope_orig_len: int = 4096
+    rope_beta_fast: float = 32.0
+    rope_beta_slow: float = 1.0
 
     @property
     def T(self) -> int:
@@ -45,6 +54,12 @@ class Workload:
     def scale(self) -> float:
         """Softmax scale 1/sqrt(D), as binary32."""
         return float(torch.tensor(float(self.D), dtype=torch.float32).pow(-0.5).item())
+
+    @property
+    def rope_positions(self) -> int:
+        """Rows of the rotation table a step needs: compressed row j sits at
+        position j * ratio."""
+        return max(1, (self.n_c - 1) * self.ratio + 1)
 
     @property
     def first_new_row(self) -> int:
@@ -58,7 +73,7 @@ class Workload:
 # The five workloads of the hot path (shapes, derived values checked in tests).
 WORKLOADS = {
     "tiny_decode": Workload("tiny_decode", m=1, start_pos=255, H=8, D=64, win=16, ratio=4, n_c=64,
-                            Hi=4, Di=32, K=16),
+                            Hi=4, Di=32, K=16, rope_dim=8),
     "decode": Workload("decode", m=1, start_pos=32767, H=64, D=512, win=128, ratio=4, n_c=8192,
                        Hi=64, Di=128, K=512),
     "long_decode": Workload("long_decode", m=1, start_pos=131071, H=64, D=512, win=128, ratio=4, n_c=32768,

@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     sckv_quant_pack,
     sckv_quant_rows,
     sckv_ring_write,
+    sckv_rope_quant_rows,
     sckv_rows_a_len,
     sckv_sparse_attn_sink,
     sckv_sparse_attn_sink_noalloc,
@@ -36,5 +37,6 @@ from ._binding import (  # noqa: F401
     sckv_visible_idx,
     sckv_window_idx,
     sckv_workspace_bytes,
+    sckv_yarn_freqs_cis,
     workspace,
 )

@@ -45,7 +45,10 @@ def _load():
     L.sckv_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, vp]
     L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
     L.sckv_decode_prepare.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i32,
-                                      i32, i64, vp, i64, vp]
+                                      i32, i64, vp, i64, vp, i64, i32, i64, vp]
+    L.sckv_yarn_freqs_cis.argtypes = [vp, i32, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float]
+    L.sckv_rope_quant_rows.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, i32, i64, i64, vp]
     L.sckv_rows_a_len.argtypes = [i32, i64, i64]
     L.sckv_rows_a_len.restype = i64
     L.sckv_window_idx.argtypes = [i32, i64, i64, i32, vp, i64, vp]
@@ -161,9 +164,11 @@ def sckv_ring_write(rows: torch.Tensor, rows_bstride: int, ring: torch.Tensor, r
 def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_new, ld_k_new: int, k_codes,
                         ld_codes: int, k_scales, ld_scales: int, Di: int, kv_new: torch.Tensor, ld_kv_new: int,
                         ring: torch.Tensor, ld_ring: int, B: int, D: int, win: int, start_pos: int,
-                        idx: torch.Tensor, ld_idx: int, stream=None):
+                        idx: torch.Tensor, ld_idx: int, rope_table: torch.Tensor | None = None, rope_dim: int = 0,
+                        lat_pos: int = 0, stream=None):
     """Row arguments: device tensors whose data pointers start the first row
-    (lat_new / lat_dst / k_new / k_codes / k_scales may be None)."""
+    (lat_new / lat_dst / k_new / k_codes / k_scales / rope_table may be None;
+    rope_table is the [n_pos, rope_dim/2, 2] f32 device table)."""
     def p(t, dtype, name):
         if t is None:
             return None
@@ -175,7 +180,30 @@ def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_ne
         p(k_new, torch.bfloat16, "k_new"), ld_k_new, p(k_codes, torch.uint8, "k_codes"), ld_codes,
         p(k_scales, torch.uint8, "k_scales"), ld_scales, Di, p(kv_new, torch.bfloat16, "kv_new"), ld_kv_new,
         p(ring, torch.bfloat16, "ring"), ld_ring, B, D, win, start_pos, p(idx, torch.int32, "idx"), ld_idx,
-        _stream(stream)))
+        p(rope_table, torch.float32, "rope_table"), 0 if rope_table is None else rope_table.shape[0], rope_dim,
+        lat_pos, _stream(stream)))
+
+
+def sckv_yarn_freqs_cis(dim: int, seqlen: int, original_seq_len: int, base: float, factor: float, beta_fast: float,
+                        beta_slow: float) -> torch.Tensor:
+    """The rotation table, built on the host by the library: a CPU f32 tensor
+    [seqlen, dim/2, 2] (copy it to the device for the rotating calls)."""
+    t = torch.empty((seqlen, dim // 2, 2), dtype=torch.float32)
+    _check("sckv_yarn_freqs_cis", lib.sckv_yarn_freqs_cis(t.data_ptr(), dim, seqlen, original_seq_len, base, factor,
+                                                          beta_fast, beta_slow))
+    return t
+
+
+def sckv_rope_quant_rows(x: torch.Tensor, ldx: int, y: torch.Tensor, ldy: int, rows: int, cols: int,
+                         table: torch.Tensor, rope_dim: int, pos0: int, pos_step: int, stream=None):
+    """x / y: bf16 device tensors whose data pointers start the first row;
+    table: the [n_pos, rope_dim/2, 2] f32 device table."""
+    for t, n in ((x, "x"), (y, "y")):
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{n}: expected a bf16 device tensor")
+    _check("sckv_rope_quant_rows", lib.sckv_rope_quant_rows(
+        x.data_ptr(), ldx, y.data_ptr(), ldy, rows, cols, _ptr(table, torch.float32, "table"), table.shape[0],
+        rope_dim, pos0, pos_step, _stream(stream)))
 
 
 def sckv_rows_a_len(win: int, m: int, start_pos: int) -> int:

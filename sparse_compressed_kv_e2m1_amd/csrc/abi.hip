@@ -38,4 +38,4 @@ extern "C" size_t sckv_workspace_bytes(int op, int B, int64_t m, int H, int D, i
 
 extern "C" const char* sckv_last_error(void) { return sckv::g_last_error.c_str(); }
 
-extern "C" int sckv_abi_version(void) { return 1; }
+extern "C" int sckv_abi_version(void) { return 2; }

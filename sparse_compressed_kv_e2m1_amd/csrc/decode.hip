@@ -7,8 +7,10 @@
 // round trip of a completed latent group before its cache copy, the ring copy
 // at slot start_pos mod window before attention, window_topk_idxs) and page
 // "metrale_model_arch/deepseek_v41_ref/compress.rs" (fp4_quant_e4m3_inplace,
-// fp4_quant_e8m0_inplace).  Each part computes exactly what the separate calls
-// sckv_quant_rows, sckv_quant_pack, sckv_ring_write and sckv_window_idx compute
+// fp4_quant_e8m0_inplace, yarn_freqs_cis and the rotation of a new latent
+// group before its round trip).  Each part computes exactly what the separate
+// calls sckv_rope_quant_rows (or sckv_quant_rows without a rotation table),
+// sckv_quant_pack, sckv_ring_write and sckv_window_idx compute
 // (the same device code); they write disjoint memory, so one launch with a
 // workgroup per sequence replaces four launches whose cost at decode size is
 // almost all launch and drain time.
@@ -39,6 +41,9 @@ struct PrepArgs {
     int64_t start_pos;
     int32_t* idx;
     int64_t ld_idx;
+    const float* rope_table;  // NULL: the latent row is not rotated
+    int rope_dim;
+    int64_t lat_pos;
 };
 
 // Max over aligned groups of 8 or 16 lanes by DPP (every lane of the group
@@ -64,8 +69,16 @@ __global__ __launch_bounds__(PREP_THREADS) void decode_prepare_kernel(PrepArgs a
     if (a.lat_new) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.lat_new + b * a.ld_lat_new);
         uint32_t* dst = reinterpret_cast<uint32_t*>(a.lat_dst + b * a.ld_lat_dst);
+        const int rope_first = (a.D - a.rope_dim) / 2;  // first pair of the rope slice
+        const float2* rt = a.rope_table ? reinterpret_cast<const float2*>(a.rope_table) + a.lat_pos * (a.rope_dim / 2)
+                                        : nullptr;
         for (int p = t; p < a.D / 2; p += PREP_THREADS) {
-            const uint32_t w = src[p];
+            uint32_t w = src[p];
+            if (rt && p >= rope_first) {
+                // the rotary turn of pair p before the round trip (sckv_rope_quant_rows)
+                const float2 cs = rt[p - rope_first];
+                w = rope_pair_bits(w, cs.x, cs.y);
+            }
             const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
             const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 8);
             const float s = block_scale<SCKV_FP4_E4M3_B16>(amax);
@@ -116,7 +129,8 @@ extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void
                                    const void* k_new, int64_t ld_k_new, void* k_codes, int64_t ld_codes,
                                    void* k_scales, int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new,
                                    void* ring, int64_t ld_ring, int B, int D, int win, int64_t start_pos,
-                                   int32_t* idx, int64_t ld_idx, void* stream) {
+                                   int32_t* idx, int64_t ld_idx, const float* rope_table, int64_t n_pos,
+                                   int rope_dim, int64_t lat_pos, void* stream) {
     using namespace sckv;
     const char* name = "sckv_decode_prepare";
     if (B < 0 || D <= 0 || win <= 0 || start_pos < 0) return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
@@ -126,6 +140,11 @@ extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void
     if (k_new && (!k_codes || !k_scales || Di <= 0 || Di % 32 != 0 || ld_k_new < Di || ld_codes < Di / 2 ||
                   ld_scales < Di / 32))
         return fail(SCKV_EINVAL, std::string(name) + ": k rows: null destination, Di not a multiple of 32 or short stride");
+    if (lat_new && rope_table &&
+        (rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > D || lat_pos < 0 || lat_pos >= n_pos ||
+         (uintptr_t)rope_table % 8))
+        return fail(SCKV_EINVAL, std::string(name) + ": rotation: rope_dim must be even, positive and at most D, "
+                                                     "lat_pos inside the table, the table 8-byte aligned");
     if (!kv_new || !ring || !idx) return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
     if (ld_kv_new < D || ld_ring < (int64_t)win * D || ld_idx < win)
         return fail(SCKV_EINVAL, std::string(name) + ": a stride is shorter than its row");
@@ -140,7 +159,8 @@ extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void
     if (!ok) return fail(SCKV_EINVAL, std::string(name) + ": rows must be 16-byte aligned with 16-byte strides");
     PrepArgs a{(const uint16_t*)lat_new, ld_lat_new, (uint16_t*)lat_dst, ld_lat_dst, (const uint16_t*)k_new, ld_k_new,
                (uint8_t*)k_codes, ld_codes, (uint8_t*)k_scales, ld_scales, Di, (const uint16_t*)kv_new, ld_kv_new,
-               (uint16_t*)ring, ld_ring, D, win, start_pos, idx, ld_idx};
+               (uint16_t*)ring, ld_ring, D, win, start_pos, idx, ld_idx, lat_new ? rope_table : nullptr,
+               rope_dim, lat_pos};
     decode_prepare_kernel<<<dim3((unsigned)B), dim3(PREP_THREADS), 0, (hipStream_t)stream>>>(a);
     return check_launch(name);
 }

@@ -15,10 +15,21 @@ constexpr int QUANT_THREADS = 256;
 
 // rows x cols values, row strides ldx / ldy (elements); cols % BLOCK == 0.
 // VEC: every block is 16-byte aligned in x and y (checked on the host).
-template <int MODE, bool VEC>
+// Rotation before the round trip (ROPE): the last rope_dim values of row r
+// turn by the table row of position pos0 + r * pos_step (table [n_pos]
+// [rope_dim / 2] pairs of binary32 cos, sin; pair i = values cols - rope_dim
+// + 2i, + 2i + 1), each turned pair rounded to bf16 first.
+struct RopeArgs {
+    const float* table;
+    int rope_dim;
+    int64_t pos0, pos_step;
+};
+
+template <int MODE, bool VEC, bool ROPE = false>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     uint16_t* __restrict__ y, int64_t ldy,
-                                                                    int64_t blocks_per_row, int64_t nblocks) {
+                                                                    int64_t blocks_per_row, int64_t nblocks,
+                                                                    RopeArgs rope = RopeArgs{}) {
     constexpr int BLOCK = QuantMode<MODE>::BLOCK;
     const int64_t gid = (int64_t)blockIdx.x * QUANT_THREADS + threadIdx.x;
     if (gid >= nblocks) return;
@@ -40,6 +51,22 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_
     } else {
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
+    }
+    if (ROPE) {
+        const int64_t cols = blocks_per_row * BLOCK;
+        const int64_t first = cols - rope.rope_dim;  // first value of the rope slice (even)
+        if (col + BLOCK > first) {
+            const int half = rope.rope_dim / 2;
+            const float2* t = reinterpret_cast<const float2*>(rope.table) + (rope.pos0 + row * rope.pos_step) * half;
+#pragma unroll
+            for (int k = 0; k < BLOCK / 2; ++k) {
+                const int64_t c = col + 2 * k;
+                if (c >= first) {
+                    const float2 cs = t[(c - first) / 2];
+                    w[k] = rope_pair_bits(w[k], cs.x, cs.y);
+                }
+            }
+        }
     }
     quant_block<MODE>(w);
     if (VEC) {
@@ -97,6 +124,49 @@ int quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t ro
     if (mode == SCKV_FP4_E4M3_B16)
         return launch_quant<SCKV_FP4_E4M3_B16>((const uint16_t*)x, ldx, (uint16_t*)y, ldy, rows, cols, s);
     return launch_quant<SCKV_FP4_E8M0_B32>((const uint16_t*)x, ldx, (uint16_t*)y, ldy, rows, cols, s);
+}
+
+// The latent path of new compressed rows: rotation of the rope slice, then
+// the E4M3_B16 round trip, one lane per block of 16.
+int rope_quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                         const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
+                         void* stream) {
+    const char* name = "sckv_rope_quant_rows";
+    if (rows < 0 || cols < 0 || n_pos < 0 || pos0 < 0 || pos_step < 0)
+        return fail(SCKV_EINVAL, std::string(name) + ": negative size or position");
+    if (cols % 16 != 0) return fail(SCKV_EINVAL, std::string(name) + ": row length is not a multiple of 16");
+    if (rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > cols)
+        return fail(SCKV_EINVAL, std::string(name) + ": rope_dim must be even, positive and at most the row length");
+    if (rows == 0 || cols == 0) return SCKV_OK;
+    if (!x || !y || !table) return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
+    if (ldx < cols || ldy < cols) return fail(SCKV_EINVAL, std::string(name) + ": row stride shorter than the row");
+    if ((uintptr_t)x % 2 || (uintptr_t)y % 2 || (uintptr_t)table % 8)
+        return fail(SCKV_EINVAL, std::string(name) + ": misaligned pointer (bf16 rows 2 bytes, table 8 bytes)");
+    if (pos0 + (rows - 1) * pos_step >= n_pos)
+        return fail(SCKV_EINVAL, std::string(name) + ": a row's position is outside the rotation table");
+    if (x != y) {
+        const uintptr_t xs = (uintptr_t)x, ys = (uintptr_t)y;
+        const uintptr_t xe = xs + (uintptr_t)(((rows - 1) * ldx + cols) * 2);
+        const uintptr_t ye = ys + (uintptr_t)(((rows - 1) * ldy + cols) * 2);
+        if (xs < ye && ys < xe) return fail(SCKV_EINVAL, std::string(name) + ": x and y overlap without being equal");
+    } else if (ldx != ldy) {
+        return fail(SCKV_EINVAL, std::string(name) + ": in place needs ldx == ldy");
+    }
+    const int64_t bpr = cols / 16, nblocks = rows * bpr;
+    const int64_t grid = (nblocks + QUANT_THREADS - 1) / QUANT_THREADS;
+    if (grid > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": too many blocks for one launch");
+    const RopeArgs r{table, rope_dim, pos0, pos_step};
+    const uint16_t* xx = (const uint16_t*)x;
+    uint16_t* yy = (uint16_t*)y;
+    hipStream_t s = (hipStream_t)stream;
+    const bool vec = ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0) && (ldx % 8 == 0) && (ldy % 8 == 0);
+    if (vec)
+        quant_rows_kernel<SCKV_FP4_E4M3_B16, true, true><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+            xx, ldx, yy, ldy, bpr, nblocks, r);
+    else
+        quant_rows_kernel<SCKV_FP4_E4M3_B16, false, true><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+            xx, ldx, yy, ldy, bpr, nblocks, r);
+    return check_launch(name);
 }
 
 // ---- packed storage: 4-bit codes (two a byte, the even element low) and one
@@ -198,4 +268,10 @@ extern "C" int sckv_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy,
 extern "C" int sckv_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds,
                                int64_t rows, int64_t cols, int mode, void* stream) {
     return sckv::quant_pack_launch(x, ldx, codes, ldc, scales, lds, rows, cols, mode, stream);
+}
+
+extern "C" int sckv_rope_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64_t rows, int64_t cols,
+                                    const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
+                                    void* stream) {
+    return sckv::rope_quant_rows_impl(x, ldx, y, ldy, rows, cols, table, n_pos, rope_dim, pos0, pos_step, stream);
 }

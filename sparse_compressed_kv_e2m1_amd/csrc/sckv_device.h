@@ -202,6 +202,21 @@ __device__ __forceinline__ uint32_t pack_block(const uint32_t (&w)[QuantMode<MOD
     return scale_byte<MODE>(s);
 }
 
+// ---------------------------------------------------------------- rotary turn
+
+// Rotary turn of one pair (x0, x1) of a row's rope slice by the table entry
+// (c, s) (pages: compress.rs attention_any and forward.rs AttnV41::forward
+// rotate a new latent group before its fp4 round trip; the rotation itself is
+// not printed -- the reading is x0 + i x1 times c + i s): binary32 products and
+// sums, no fused multiply-add (the library is built with -ffp-contract=off),
+// each result rounded to bf16.  w holds x0 in the low half, x1 in the high.
+__device__ __forceinline__ uint32_t rope_pair_bits(uint32_t w, float c, float s) {
+    const float x0 = bf16_bits_to_f32(w & 0xffffu), x1 = bf16_bits_to_f32(w >> 16);
+    const float y0 = x0 * c - x1 * s;
+    const float y1 = x0 * s + x1 * c;
+    return f32_to_bf16_bits(y0) | (f32_to_bf16_bits(y1) << 16);
+}
+
 // Row of position q inside rows_a (the layout sckv_rows_a_len describes).
 __device__ __forceinline__ int64_t window_row(int win, int64_t m, int64_t start_pos, int64_t q) {
     if (start_pos == 0) return q;

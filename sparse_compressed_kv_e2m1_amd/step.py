@@ -5,9 +5,10 @@ trip, no CPU compute).
 Order of a step (page "metrale_model_arch/attn_v41/forward.rs",
 AttnV41::forward; page "metrale_model_arch/deepseek_v41_ref/compress.rs",
 attention_any):
-  1. fp4 round trip of the step's new compressed latent rows into the latent
-     cache (e4m3 scales, block 16) and of the new indexer k rows into the k
-     cache (power-of-two scales, block 32);
+  1. rotary turn (YaRN table, position j * ratio for compressed row j) and fp4
+     round trip of the step's new compressed latent rows into the latent
+     cache (e4m3 scales, block 16); fp4 round trip of the new indexer k rows
+     into the k cache (power-of-two scales, block 32);
   2. decode (m == 1, start_pos > 0): the new kv row goes into its ring slot
      before attention;
   3. window columns of every query's index list;
@@ -89,6 +90,9 @@ class PathState:
         self.n_new = w.n_c - self.first_new
         lat = inputs["latent_raw"]
         self.latent = dev(lat)
+        # the latent rows' rotation table, built once (on the host, by the library)
+        self.rope_table = sk.sckv_yarn_freqs_cis(w.rope_dim, w.rope_positions, w.rope_orig_len, w.rope_base,
+                                                 w.rope_factor, w.rope_beta_fast, w.rope_beta_slow).to(device)
         self.latent_new = lat[:, self.first_new:].to(device).clone()  # a buffer of its own, never a view
         if w.Hi:
             self.iq = dev(inputs["iq"])
@@ -111,8 +115,9 @@ class PathState:
         as earlier steps left them)."""
         w, B = self.w, self.B
         if self.first_new > 0:
-            sk.sckv_quant_rows(self.latent, w.n_c * w.D, self.latent, w.n_c * w.D, B, self.first_new * w.D,
-                               sk.SCKV_FP4_E4M3_B16)
+            for b in range(B):  # row j of each sequence turned at j * ratio, then round-tripped
+                sk.sckv_rope_quant_rows(self.latent[b], w.D, self.latent[b], w.D, self.first_new, w.D,
+                                        self.rope_table, w.rope_dim, 0, w.ratio)
             if w.Hi and self.kcache == "fp4":
                 # every row packed (the step's own new rows are packed again by its first calls)
                 sk.sckv_quant_pack(self.ik, w.Di, self.ik_codes, w.Di // 2, self.ik_scales, w.Di // 32, B * w.n_c,
@@ -124,6 +129,17 @@ class PathState:
     def _quant_new(self, src, dst, width, mode):
         w, B = self.w, self.B
         if self.n_new == 0:
+            return
+        if mode == sk.SCKV_FP4_E4M3_B16:
+            # the latent: rotary turn at j * ratio, then the round trip
+            pos0 = self.first_new * w.ratio
+            if self.n_new == 1:  # one row per sequence, all at one position
+                sk.sckv_rope_quant_rows(src, width, dst[:, self.first_new:], w.n_c * width, B, width, self.rope_table,
+                                        w.rope_dim, pos0, 0)
+            else:
+                for b in range(B):
+                    sk.sckv_rope_quant_rows(src[b], width, dst[b, self.first_new:], width, self.n_new, width,
+                                            self.rope_table, w.rope_dim, pos0, w.ratio)
             return
         if self.n_new == 1 or B == 1:
             # B x n_new rows: either one row per sequence, or one sequence
@@ -163,7 +179,7 @@ class PathState:
                 self.latent_new if new else None, D, self.latent[:, f] if new else None, w.n_c * D,
                 self.ik_new if new else None, w.Di, self.ik_codes[:, f] if new else None, w.n_c * w.Di // 2,
                 self.ik_scales[:, f] if new else None, w.n_c * w.Di // 32, w.Di, self.kv_new, D, self.ring, win * D,
-                B, D, win, w.start_pos, self.idx, self.T))]
+                B, D, win, w.start_pos, self.idx, self.T, self.rope_table, w.rope_dim, f * w.ratio))]
             return out + self._score_and_attend_calls()
         out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
         if w.Hi and self.kcache == "fp4":

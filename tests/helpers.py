@@ -38,6 +38,20 @@ def oracle_rows_a(w, x, b: int) -> np.ndarray:
     return np.concatenate([ring, kv], axis=0)
 
 
+def oracle_rope_table(w):
+    return oracle.yarn_freqs_cis(w.rope_dim, w.rope_positions, w.rope_orig_len, w.rope_base, w.rope_factor,
+                                 w.rope_beta_fast, w.rope_beta_slow)
+
+
+def oracle_latent(w, x, b: int) -> np.ndarray:
+    """The latent cache after the step: every compressed row j turned at its
+    position j * ratio, then round-tripped (the rows before this step as
+    earlier steps left them, the new ones as this step writes them)."""
+    pos = np.array([oracle.latent_position(j, w.ratio) for j in range(w.n_c)], dtype=np.int64)
+    return oracle.latent_rope_quant(bits(x["latent_raw"][b]).reshape(w.n_c, w.D), w.rope_dim, oracle_rope_table(w),
+                                    pos)
+
+
 def oracle_threads() -> int:
     """Worker threads for oracle calls over many queries (the oracle releases
     the GIL inside its C calls; each query's result is independent of the
@@ -61,7 +75,7 @@ def oracle_step(w, x, b: int = 0, qsel=None, attn_qsel=None, threads: int = 1):
     step of workload w; threads > 1 splits the queries over worker threads."""
     qsel = np.arange(w.m, dtype=np.int64) if qsel is None else np.asarray(qsel, dtype=np.int64)
     attn_qsel = qsel if attn_qsel is None else np.asarray(attn_qsel, dtype=np.int64)
-    latent = oracle.quant(bits(x["latent_raw"][b]).reshape(-1), oracle.E4M3_B16).reshape(w.n_c, w.D)
+    latent = oracle_latent(w, x, b)
     rows_a = oracle_rows_a(w, x, b)
     widx, ra = oracle.window_idx(w.win, w.m, w.start_pos)
     assert ra == rows_a.shape[0]

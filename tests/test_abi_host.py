@@ -21,7 +21,7 @@ def test_header_declares_the_calls():
     for n in ["sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_rows_a_len", "sckv_window_idx",
               "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
               "sckv_last_error", "sckv_abi_version", "sckv_quant_pack", "sckv_index_scores_topk_fp4",
-              "sckv_decode_prepare"]:
+              "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows"]:
         assert n in names
 
 
@@ -31,7 +31,7 @@ def test_library_exports_every_declared_call():
     lib = ctypes.CDLL(sk.LIB_PATH)
     for n in declared_calls():
         assert hasattr(lib, n), n
-    assert sk.sckv_abi_version() == 1
+    assert sk.sckv_abi_version() == 2
     assert "sckv_sparse_attn_sink_noalloc" in declared_calls()
     assert sk.sckv_sparse_attn_sink_noalloc_max_bytes() == 32 << 20
 
@@ -143,13 +143,15 @@ def test_error_paths(L):
     # decode set-up: sizes, strides, alignment, missing destinations
     def dp(**kw):
         a = dict(ld_lat_new=512, ld_lat_dst=512, ld_k_new=128, ld_codes=64, ld_scales=4, Di=128, ld_kv_new=512,
-                 ld_ring=128 * 512, B=2, D=512, win=128, start_pos=1000, ld_idx=640)
+                 ld_ring=128 * 512, B=2, D=512, win=128, start_pos=1000, ld_idx=640, n_pos=4000, rope_dim=64,
+                 lat_pos=996)
         a.update({k: v for k, v in kw.items() if k in a})
         return L.sckv_decode_prepare(kw.get("lat_new", fake), a["ld_lat_new"], kw.get("lat_dst", fake),
                                      a["ld_lat_dst"], kw.get("k_new", fake), a["ld_k_new"], kw.get("k_codes", fake),
                                      a["ld_codes"], kw.get("k_scales", fake), a["ld_scales"], a["Di"],
                                      kw.get("kv_new", fake), a["ld_kv_new"], kw.get("ring", fake), a["ld_ring"],
-                                     a["B"], a["D"], a["win"], a["start_pos"], kw.get("idx", fake), a["ld_idx"], None)
+                                     a["B"], a["D"], a["win"], a["start_pos"], kw.get("idx", fake), a["ld_idx"],
+                                     kw.get("rope_table", None), a["n_pos"], a["rope_dim"], a["lat_pos"], None)
 
     assert dp(D=520) == sk.SCKV_EINVAL                 # not a multiple of 16
     assert dp(Di=100) == sk.SCKV_EINVAL                # not a multiple of 32
@@ -158,6 +160,25 @@ def test_error_paths(L):
     assert dp(kv_new=None) == sk.SCKV_EINVAL
     assert dp(idx=None) == sk.SCKV_EINVAL
     assert dp(ld_ring=1000) == sk.SCKV_EINVAL          # shorter than win * D
+    assert dp(rope_table=fake, rope_dim=63) == sk.SCKV_EINVAL   # odd rotation width
+    assert dp(rope_table=fake, rope_dim=520) == sk.SCKV_EINVAL  # wider than the row
+    assert dp(rope_table=fake, lat_pos=4000) == sk.SCKV_EINVAL  # position outside the table
+    assert dp(rope_table=ctypes.c_void_p(0x1004)) == sk.SCKV_EINVAL  # table not 8-byte aligned
+
+    def rq(**kw):
+        a = dict(ldx=512, ldy=512, rows=4, cols=512, n_pos=100, rope_dim=64, pos0=0, pos_step=4)
+        a.update({k: v for k, v in kw.items() if k in a})
+        return L.sckv_rope_quant_rows(kw.get("x", fake), a["ldx"], kw.get("y", ctypes.c_void_p(0x100000)), a["ldy"],
+                                      a["rows"], a["cols"], kw.get("table", fake), a["n_pos"], a["rope_dim"],
+                                      a["pos0"], a["pos_step"], None)
+
+    assert rq(cols=520) == sk.SCKV_EINVAL               # not a multiple of 16
+    assert rq(rope_dim=0) == sk.SCKV_EINVAL
+    assert rq(rope_dim=7) == sk.SCKV_EINVAL
+    assert rq(pos0=97, pos_step=1) == sk.SCKV_EINVAL    # last row at position 100: outside
+    assert rq(pos_step=-1) == sk.SCKV_EINVAL
+    assert rq(table=None) == sk.SCKV_EINVAL
+    assert rq(rows=0) == sk.SCKV_OK
     assert dp(ld_idx=100) == sk.SCKV_EINVAL            # shorter than win
     assert dp(ring=ctypes.c_void_p(0x1004)) == sk.SCKV_EINVAL  # not 16-byte aligned
     assert dp(ld_codes=72) == sk.SCKV_EINVAL           # code rows not 16-byte strided
@@ -187,3 +208,28 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 for bad in ("import oracle", "from oracle", "libsckv_oracle", "sckvo_", "oracle.py"):
                     assert bad not in text, (f, bad)
+
+
+def test_rotation_table_matches_oracle():
+    """The library's host-built rotation table (sckv_yarn_freqs_cis) is the
+    oracle's, bit for bit, at the workloads' parameters and at plain RoPE; bad
+    parameters are refused."""
+    import numpy as np
+
+    import sckv_synth as synth
+    import sparse_compressed_kv_e2m1_amd as sk
+    from oracle import oracle
+
+    for w in synth.WORKLOADS.values():
+        args = (w.rope_dim, w.rope_positions, w.rope_orig_len, w.rope_base, w.rope_factor, w.rope_beta_fast,
+                w.rope_beta_slow)
+        got = sk.sckv_yarn_freqs_cis(*args).numpy()
+        want = oracle.yarn_freqs_cis(*args)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), w.name
+    got = sk.sckv_yarn_freqs_cis(128, 300, 8192, 500000.0, 1.0, 32.0, 1.0).numpy()
+    assert np.array_equal(got.view(np.uint32), oracle.yarn_freqs_cis(128, 300, 8192, 500000.0, 1.0, 32.0, 1.0)
+                          .view(np.uint32))
+    for bad in ((63, 4, 4096, 1e4, 40.0, 32.0, 1.0), (64, 4, 4096, 1.0, 40.0, 32.0, 1.0),
+                (64, 4, 4096, 1e4, 0.0, 32.0, 1.0)):
+        with pytest.raises(sk.SckvError):
+            sk.sckv_yarn_freqs_cis(*bad)

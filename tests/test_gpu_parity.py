@@ -224,12 +224,50 @@ def test_ring_write_bit_exact(sk, win, m, start_pos, D):
         assert np.array_equal(got[b, win:], rows[b])
 
 
-@pytest.mark.parametrize("B,D,Di,win,start_pos,new", [(3, 512, 128, 128, 32767, True), (2, 64, 32, 16, 5, True),
-                                                       (4, 512, 128, 128, 1000, False), (2, 256, 64, 8, 7, True)])
-def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new):
+ROPE_CASES = [
+    # rows, cols, rope_dim, n_pos, pos0, pos_step, ldx_pad, in_place, unaligned
+    (1, 512, 64, 32765, 32764, 0, 0, False, False),      # one decode row
+    (2048, 512, 64, 32765, 32764, 0, 0, False, False),   # a decode batch: every row at one position
+    (1024, 512, 64, 4093, 0, 4, 0, False, False),        # causal prefill's 1024 groups at g * 4
+    (16, 512, 64, 65409, 63488, 128, 0, False, False),   # chunked prefill's new rows at j * 128
+    (37, 64, 8, 200, 3, 5, 24, True, False),             # rotation inside a block, strided, in place
+    (5, 128, 128, 60, 7, 9, 0, False, True),             # the whole row rotated, 2-byte aligned rows
+    (9, 256, 32, 131069, 131068, 0, 8, False, False),    # far positions
+]
+
+
+@pytest.mark.parametrize("case", ROPE_CASES, ids=lambda c: "r{}c{}rd{}p{}s{}".format(c[0], c[1], c[2], c[4], c[5]))
+def test_rope_quant_rows_bit_exact(sk, case):
+    """The latent path of new rows (rotary turn at pos0 + r * pos_step, then
+    the E4M3_B16 round trip) against the oracle, bit for bit; rows outside
+    the call unchanged."""
+    rows, cols, rd, n_pos, pos0, pos_step, pad, in_place, unaligned = case
+    rng = np.random.default_rng(rows * 7 + cols + rd)
+    ld = cols + pad
+    x = bits(bf16_of(rng.standard_normal((rows, ld)) * np.exp2(rng.integers(-6, 6, size=(rows, 1)))))
+    table = oracle.yarn_freqs_cis(rd, n_pos, 4096, 10000.0, 40.0, 32.0, 1.0)
+    pos = pos0 + np.arange(rows, dtype=np.int64) * pos_step
+    want = oracle.latent_rope_quant(np.ascontiguousarray(x[:, :cols]), rd, table, pos)
+    off = 1 if unaligned else 0
+    xd = torch.zeros(rows * ld + off, dtype=torch.bfloat16, device="cuda")
+    xd[off:] = from_bits(x.reshape(-1), "cuda")
+    yd = xd if in_place else torch.full((rows * ld + off,), 7.0, dtype=torch.bfloat16, device="cuda")
+    say(f"rope quant rows {case}")
+    sk.sckv_rope_quant_rows(xd[off:], ld, yd[off:], ld, rows, cols, torch.from_numpy(table).cuda(), rd, pos0, pos_step)
+    got = bits(yd)[off:].reshape(rows, ld)
+    assert np.array_equal(got[:, :cols], want), np.argwhere(got[:, :cols] != want)[:5]
+    if pad:
+        assert np.array_equal(got[:, cols:], x[:, cols:] if in_place else bits(bf16_of(np.full((rows, pad), 7.0))))
+
+
+@pytest.mark.parametrize("B,D,Di,win,start_pos,new,rope_dim", [
+    (3, 512, 128, 128, 32767, True, 64), (2, 64, 32, 16, 5, True, 8), (4, 512, 128, 128, 1000, False, 64),
+    (2, 256, 64, 8, 7, True, 0), (2, 512, 128, 128, 131071, True, 512)])
+def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new, rope_dim):
     """The one-launch decode set-up against the oracle: the latent row's
-    E4M3_B16 round trip into the cache, the packed E8M0_B32 k row, the ring
-    slot and the window columns; nothing else in the buffers changes."""
+    rotary turn (when a table is given) and E4M3_B16 round trip into the
+    cache, the packed E8M0_B32 k row, the ring slot and the window columns;
+    nothing else in the buffers changes."""
     n_c = 6
     f = 4  # cache row of the completed group
     rng = np.random.default_rng(B * 1000 + start_pos)
@@ -244,15 +282,19 @@ def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new):
     lat_d, ring_d = from_bits(latent, "cuda"), from_bits(ring, "cuda")
     codes_d, scales_d = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
     idx = torch.full((B, 1, ld_idx), 77, dtype=torch.int32, device="cuda")
-    say(f"decode prepare B={B} D={D} Di={Di} win={win} start_pos={start_pos} new={new}")
+    lat_pos = max(0, start_pos - 3)  # the completed group's position
+    table = oracle.yarn_freqs_cis(rope_dim, lat_pos + 1, 4096, 10000.0, 40.0, 32.0, 1.0) if rope_dim else None
+    say(f"decode prepare B={B} D={D} Di={Di} win={win} start_pos={start_pos} new={new} rope_dim={rope_dim}")
     sk.sckv_decode_prepare(from_bits(lat_new, "cuda") if new else None, D, lat_d[:, f] if new else None, n_c * D,
                            from_bits(k_new, "cuda") if new else None, Di, codes_d[:, f] if new else None,
                            n_c * Di // 2, scales_d[:, f] if new else None, n_c * Di // 32, Di,
-                           from_bits(kv_new, "cuda"), D, ring_d, win * D, B, D, win, start_pos, idx, ld_idx)
+                           from_bits(kv_new, "cuda"), D, ring_d, win * D, B, D, win, start_pos, idx, ld_idx,
+                           torch.from_numpy(table).cuda() if rope_dim else None, rope_dim, lat_pos)
     want_lat, want_codes, want_scales = latent.copy(), codes.copy(), scales.copy()
     if new:
         for b in range(B):
-            want_lat[b, f] = oracle.quant(lat_new[b], oracle.E4M3_B16)
+            want_lat[b, f] = (oracle.latent_rope_quant(lat_new[b][None], rope_dim, table, [lat_pos])[0] if rope_dim
+                              else oracle.quant(lat_new[b], oracle.E4M3_B16))
             c, sc = oracle.pack(k_new[b], oracle.E8M0_B32)
             want_codes[b, f], want_scales[b, f] = c, sc
     assert np.array_equal(bits(lat_d), want_lat)
