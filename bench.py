@@ -49,11 +49,14 @@ def describe(w):
     return s
 
 
-def counts(w, B, call, kcache="bf16"):
+def counts(w, B, call, kcache="bf16", latent="bf16"):
     """Algorithmic bytes and flops of one library call for one step of B
-    sequences: what the method must read and write (bf16 storage, each needed
-    row once, valid (query, row) pairs only).  The implementation's workspace
-    traffic is not counted.  bound: the roofline the call is judged against."""
+    sequences: what the method must read and write (each needed row once,
+    valid (query, row) pairs only) in the storage the step uses: bf16 rows as
+    on the pages, or, for the packed caches, codes + scale bytes (an indexer k
+    row 68 B at Di = 128, a latent row 288 B at D = 512).  The
+    implementation's workspace traffic is not counted.  bound: the roofline
+    the call is judged against."""
     m, win, D = w.m, w.win, w.D
     V = [min(w.n_c, (w.start_pos + t + 1) // w.ratio) for t in range(m)]
     Wv = [min(win, w.start_pos + t + 1) for t in range(m)]
@@ -61,8 +64,9 @@ def counts(w, B, call, kcache="bf16"):
     pairs = sum(Wv) + sum(C)
     n_new = w.n_c - w.first_new_row
     dense = m > 1
+    lrow = D // 2 + D // 16 if latent == "fp4" else D * 2  # stored bytes of a latent row
     if call == "quant_latent":
-        return {"bytes": B * n_new * D * 4, "flops": 0, "bound": "hbm"}
+        return {"bytes": B * n_new * (D * 2 + lrow), "flops": 0, "bound": "hbm"}
     krow = w.Di // 2 + w.Di // 32 if kcache == "fp4" else w.Di * 2  # stored bytes of an indexer k row
     if call == "quant_index_k":
         return {"bytes": B * n_new * (w.Di * 2 + krow), "flops": 0, "bound": "hbm"}
@@ -71,7 +75,7 @@ def counts(w, B, call, kcache="bf16"):
     if call == "window_idx":
         return {"bytes": B * m * win * 4, "flops": 0, "bound": "hbm"}
     if call == "decode_prepare":  # the four set-up calls of a decode step in one launch
-        return {"bytes": sum(counts(w, B, c, kcache)["bytes"]
+        return {"bytes": sum(counts(w, B, c, kcache, latent)["bytes"]
                              for c in ("quant_latent", "quant_index_k", "ring_write", "window_idx")),
                 "flops": 0, "bound": "hbm"}
     if call == "visible_idx":
@@ -86,7 +90,7 @@ def counts(w, B, call, kcache="bf16"):
                 "flops_all_visible": B * sum(V) * w.Hi * w.Di * 2}
     if call == "sparse_attn_sink":
         rows = (w.m if w.start_pos == 0 else (win + m if m > 1 else None))
-        row_bytes = (rows + w.n_c) * D * 2 if rows is not None else pairs * D * 2
+        row_bytes = (rows * D * 2 + w.n_c * lrow) if rows is not None else (sum(Wv) * D * 2 + sum(C) * lrow)
         by = B * (row_bytes + 2 * m * w.H * D * 2 + m * w.T * 4 + w.H * 4)
         fl = B * pairs * w.H * D * 4
         return {"bytes": by, "flops": fl, "bound": "mfma" if dense else "hbm"}
@@ -108,7 +112,7 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def traffic_for(workload, B, call, kcache):
+def traffic_for(workload, B, call, kcache, latent="bf16"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -120,13 +124,14 @@ def traffic_for(workload, B, call, kcache):
         return None
     if rec.get("kernel_source_hash") != kernel_source_hash():
         return None
-    entry = rec.get("entries", {}).get(f"{workload}/B{B}/{kcache}/{call}")
+    lat = "" if latent == "bf16" else f"/latent_{latent}"
+    entry = rec.get("entries", {}).get(f"{workload}/B{B}/{kcache}{lat}/{call}")
     return None if entry is None else entry.get("hbm_bytes_per_launch")
 
 
 # Library call -> the kernels it launches (demangled-name prefixes).
 CALL_KERNELS = {
-    "quant_latent": ["quant_rows_kernel<0,"],
+    "quant_latent": ["quant_rows_kernel<0,", "quant_pack_kernel<0,"],
     "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1>"],
     "ring_write": ["ring_write_kernel"],
     "decode_prepare": ["decode_prepare_kernel"],
@@ -190,7 +195,7 @@ def _sq_counters(folder):
     return out
 
 
-def summarize_profiles(w, B, folder, commands, kcache="bf16"):
+def summarize_profiles(w, B, folder, commands, kcache="bf16", latent="bf16"):
     """Turn rocprofv3 output under `folder` (trace/, FETCH_SIZE/, WRITE_SIZE/,
     SQ/, copy_FETCH_SIZE/, copy_WRITE_SIZE/) into the text summary
     profiles/hot_path_kernels_<workload>_B<B>.txt and the HBM-traffic entries
@@ -218,7 +223,7 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
                          or "copy" in r["Kernel_Name"].lower())
         scale[c] = (1 << 30) / copy_bytes
     lines = [f"# rocprofv3 summary: compressed sparse attention hot path, {describe(w)}, B={B}"
-             + (f", indexer k cache {kcache}" if w.Hi else ""), "#"]
+             + (f", indexer k cache {kcache}" if w.Hi else "") + f", latent cache {latent}", "#"]
     lines += ["# commands (repo root as working directory):"] + [f"#   {c}" for c in commands]
     lines += [f"# counter scale (1 GiB device copy): FETCH_SIZE x{scale.get('FETCH_SIZE', float('nan')):.3f}, "
               f"WRITE_SIZE x{scale.get('WRITE_SIZE', float('nan')):.3f}",
@@ -270,12 +275,13 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16"):
         if res["FETCH_SIZE"] and res["WRITE_SIZE"] and all(k in res[c] for c in res for k in ks):
             hbm = sum(res["FETCH_SIZE"].get(k, 0) * scale["FETCH_SIZE"] + res["WRITE_SIZE"].get(k, 0)
                       * scale["WRITE_SIZE"] for k in ks)
-        alg = counts(w, B, call, kcache)["bytes"]
+        alg = counts(w, B, call, kcache, latent)["bytes"]
         lines.append(f"{call:<20} {us:>9.2f} {alg / 1e6:>9.2f} {'-' if hbm is None else f'{hbm / 1e6:.2f}':>9}")
-        entries[f"{w.name}/B{B}/{kcache if w.Hi else 'none'}/{call}"] = {"kernels": ks, "avg_us": round(us, 3),
+        lat = "" if latent == "bf16" else f"/latent_{latent}"
+        entries[f"{w.name}/B{B}/{kcache if w.Hi else 'none'}{lat}/{call}"] = {"kernels": ks, "avg_us": round(us, 3),
                                             "hbm_bytes_per_launch": None if hbm is None else int(hbm)}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    kc = f"_kcache_{kcache}" if w.Hi else ""
+    kc = (f"_kcache_{kcache}" if w.Hi else "") + ("" if latent == "bf16" else f"_latent_{latent}")
     out = os.path.join(ROOT, "profiles", f"hot_path_kernels_{w.name}_B{B}{kc}.txt")
     open(out, "w").write("\n".join(lines) + "\n")
     tj = os.path.join(ROOT, "profiles", "traffic.json")
@@ -439,7 +445,7 @@ def roofline_of(cnt, ms, peaks=None, dtype=None):
     return r
 
 
-def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
+def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, latent="bf16"):
     """Time whole steps of workload w over B sequences (inputs drawn on the
     device, resident before the timed region), then each library call with
     events around it on the same stream; optionally the B = 1 latency."""
@@ -450,7 +456,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
 
     log(f"bench: workload {w.name} B={B}: generating inputs on the device")
     x = synth.make_inputs(w, B, device="cuda")
-    st = PathState(w, x, B, kcache=kcache)
+    st = PathState(w, x, B, kcache=kcache, latent=latent)
     del x
     st.setup()
     calls = st.calls()
@@ -495,7 +501,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
     sing = None
     if single and B > 1:
         x1 = synth.make_inputs(w, 1, device="cuda")
-        s1 = PathState(w, x1, 1, kcache=kcache)
+        s1 = PathState(w, x1, 1, kcache=kcache, latent=latent)
         s1.setup()
         for _ in range(warmup):
             s1.step()
@@ -515,10 +521,10 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
     dtypes = {"index_scores_topk": "fp4" if kcache == "fp4" else "bf16"}
     call_info = {}
     for name, t in per_ms.items():
-        cnt = counts(w, B, name, kcache)
+        cnt = counts(w, B, name, kcache, latent)
         r = roofline_of(cnt, t, peaks, dtypes.get(name))
         r.update({"ms_per_launch": round(t, 5), "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
-                  "traffic": traffic_for(w.name, B, name, kc)})
+                  "traffic": traffic_for(w.name, B, name, kc, latent)})
         if "flops_all_visible" in cnt:
             r["flops_all_visible_pairs"] = cnt["flops_all_visible"]
         call_info[name] = r
@@ -527,7 +533,8 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None):
     roof["kernel"] = dom
     tokens = B * w.m
     return {"workload": describe(w), "instances": B, "tokens_per_step": tokens, "value": round(tokens / (ms / 1e3), 1),
-            "ms_per_step": round(ms, 5), "indexer_k_cache": kcache if w.Hi else None, "step_launch": launch,
+            "ms_per_step": round(ms, 5), "indexer_k_cache": kcache if w.Hi else None, "latent_cache": latent,
+            "step_launch": launch,
             "roofline": roof, "calls": call_info, "single_instance": sing}
 
 
@@ -540,6 +547,8 @@ def main():
     ap.add_argument("--instances", type=int, default=None, help="B independent sequences per step")
     ap.add_argument("--kcache", choices=["fp4", "bf16"], default="fp4",
                     help="indexer k cache storage: packed fp4 codes + E8M0 bytes (default) or bf16 rows")
+    ap.add_argument("--latent", choices=["fp4", "bf16"], default="bf16",
+                    help="latent cache storage: packed fp4 codes + e4m3 bytes, or bf16 rows (the pages' layout)")
     ap.add_argument("--legs", default="long_decode,causal_prefill,chunked_prefill",
                     help="other workloads timed in the same run and reported under 'legs' (comma list; '' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per thread count")
@@ -559,7 +568,8 @@ def main():
         import sckv_synth as synth  # noqa: PLC0415
 
         w = synth.WORKLOADS[args.workload]
-        summarize_profiles(w, args.instances or DEFAULT_B[args.workload], args.summarize, args.command, args.kcache)
+        summarize_profiles(w, args.instances or DEFAULT_B[args.workload], args.summarize, args.command, args.kcache,
+                           args.latent)
         return
     if args.copy_calibration:
         import torch  # noqa: PLC0415
@@ -591,12 +601,12 @@ def main():
     w = synth.WORKLOADS[args.workload]
     B = args.instances or DEFAULT_B[args.workload]
     head = run_leg(w, B, args.kcache, args.steps, args.warmup, single=not args.no_single, graph=args.graph,
-                   peaks=peaks)
+                   peaks=peaks, latent=args.latent)
     legs = {}
     for name in [n for n in args.legs.split(",") if n and n != w.name]:
         lw = synth.WORKLOADS[name]
         legs[name] = run_leg(lw, DEFAULT_B[name], args.kcache, args.steps, args.warmup, single=False,
-                             graph=args.graph, peaks=peaks)
+                             graph=args.graph, peaks=peaks, latent=args.latent)
 
     line = {
         "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",
@@ -615,7 +625,8 @@ def main():
                        if args.kcache == "fp4" else "bf16 operands, f32 accumulation"),
         "data": "synthetic (seeded N(0,1), device generator)",
         "config": {"workload": head["workload"], "instances": B, "tokens_per_step": head["tokens_per_step"],
-                   "indexer_k_cache": head["indexer_k_cache"], "step_launch": head["step_launch"]},
+                   "indexer_k_cache": head["indexer_k_cache"], "latent_cache": head["latent_cache"],
+                   "step_launch": head["step_launch"]},
         "roofline": head["roofline"],
         "per_call_ms": {k: v["ms_per_launch"] for k, v in head["calls"].items()},
         "calls": head["calls"],

@@ -144,6 +144,22 @@ int sckv_rope_quant_rows(const void* x, int64_t ldx, void* y, int64_t ldy, int64
                          void* stream);
 
 /*
+ * sckv_rope_quant_pack -- sckv_rope_quant_rows stored packed: the rotated,
+ * round-tripped latent rows as sckv_quant_pack(SCKV_FP4_E4M3_B16) stores them
+ * (4-bit e2m1 codes, two a byte, the even element low; one E4M3FN scale byte
+ * per 16 values).  288 bytes instead of 1024 for a 512-wide latent row; code
+ * value * scale is exactly the bf16 value sckv_rope_quant_rows produces.
+ *   x       [rows, cols] bf16, row stride ldx (elements)
+ *   codes   [rows, cols/2] bytes, row stride ldc (bytes)
+ *   scales  [rows, cols/16] bytes, row stride lds (bytes)
+ *   table, n_pos, rope_dim, pos0, pos_step as in sckv_rope_quant_rows
+ * x, codes and scales must not overlap.
+ */
+int sckv_rope_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
+                         int64_t cols, const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
+                         void* stream);
+
+/*
  * sckv_ring_write -- write this step's m kv rows into the window ring: the row
  * of position p goes to slot p mod win; only the last min(m, win) positions
  * are written (forward.rs: the ring's one or two stream-ordered copies at
@@ -206,6 +222,11 @@ int sckv_window_idx(int B, int64_t m, int64_t start_pos, int win, int32_t* idx, 
  *              are turned at position lat_pos before their round trip, exactly
  *              as sckv_rope_quant_rows(lat_new, ld_lat_new, lat_dst,
  *              ld_lat_dst, B, D, rope_table, n_pos, rope_dim, lat_pos, 0)
+ *   lat_codes  with lat_dst NULL: the latent rows are stored packed instead,
+ *              as sckv_rope_quant_pack (or sckv_quant_pack in SCKV_FP4_E4M3_B16
+ *              without a table) would: codes rows of D/2 bytes, stride
+ *              ld_lat_codes, and lat_scales rows of D/16 e4m3 scale bytes,
+ *              stride ld_lat_scales (bytes)
  * D % 16 == 0, Di % 32 == 0; every row pointer 16-byte aligned and every
  * stride a multiple of 16 bytes (ld_scales excepted), else SCKV_EINVAL.
  */
@@ -213,7 +234,8 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
                         const void* k_new, int64_t ld_k_new, void* k_codes, int64_t ld_codes, void* k_scales,
                         int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new, void* ring,
                         int64_t ld_ring, int B, int D, int win, int64_t start_pos, int32_t* idx, int64_t ld_idx,
-                        const float* rope_table, int64_t n_pos, int rope_dim, int64_t lat_pos, void* stream);
+                        const float* rope_table, int64_t n_pos, int rope_dim, int64_t lat_pos, void* lat_codes,
+                        int64_t ld_lat_codes, void* lat_scales, int64_t ld_lat_scales, void* stream);
 
 /*
  * sckv_visible_idx -- the compressed part of every query's index list when
@@ -303,6 +325,24 @@ int sckv_index_scores_topk_fp4(const void* q, const void* k_codes, const void* k
 int sckv_sparse_attn_sink(const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
                           const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m, int H, int D,
                           void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sckv_sparse_attn_sink_fp4 -- sckv_sparse_attn_sink with the compressed rows
+ * (rows_b, the latent cache) stored packed as sckv_rope_quant_pack /
+ * sckv_quant_pack(SCKV_FP4_E4M3_B16) store them: the same results, bit for
+ * bit, as sckv_sparse_attn_sink over the bf16 values they stand for (code
+ * value * scale, which is exactly the latent round trip).  Each packed row is
+ * read once (288 bytes instead of 1024 at D = 512) and expanded to bf16 on
+ * chip.  rows_a stays bf16 (the window rows are not round-tripped).
+ *   rows_b_codes   [B, rb, D/2] bytes, 16-byte aligned
+ *   rows_b_scales  [B, rb, D/16] bytes (e4m3 codes), 16-byte aligned
+ * Supported: D = 512 (else SCKV_EUNSUPPORTED); the rest as
+ * sckv_sparse_attn_sink, with the same workspace size.
+ */
+int sckv_sparse_attn_sink_fp4(const void* q, const void* rows_a, int64_t ra, const void* rows_b_codes,
+                              const void* rows_b_scales, int64_t rb, const int32_t* idx, int T, const float* sink,
+                              float scale, int B, int64_t m, int H, int D, void* out, void* ws, size_t ws_bytes,
+                              void* stream);
 
 /*
  * sckv_sparse_attn_sink_noalloc -- sckv_sparse_attn_sink for callers that

@@ -29,9 +29,11 @@ from ._binding import (  # noqa: F401
     sckv_quant_pack,
     sckv_quant_rows,
     sckv_ring_write,
+    sckv_rope_quant_pack,
     sckv_rope_quant_rows,
     sckv_rows_a_len,
     sckv_sparse_attn_sink,
+    sckv_sparse_attn_sink_fp4,
     sckv_sparse_attn_sink_noalloc,
     sckv_sparse_attn_sink_noalloc_max_bytes,
     sckv_visible_idx,

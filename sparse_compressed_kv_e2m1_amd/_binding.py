@@ -45,7 +45,8 @@ def _load():
     L.sckv_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, i32, vp]
     L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
     L.sckv_decode_prepare.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i32,
-                                      i32, i64, vp, i64, vp, i64, i32, i64, vp]
+                                      i32, i64, vp, i64, vp, i64, i32, i64, vp, i64, vp, i64, vp]
+    L.sckv_rope_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp, i64, i32, i64, i64, vp]
     L.sckv_yarn_freqs_cis.argtypes = [vp, i32, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                       ctypes.c_float]
     L.sckv_rope_quant_rows.argtypes = [vp, i64, vp, i64, i64, i64, vp, i64, i32, i64, i64, vp]
@@ -59,6 +60,8 @@ def _load():
                                              vp, i64, i64, vp, vp, sz, vp]
     L.sckv_sparse_attn_sink.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32, vp,
                                         vp, sz, vp]
+    L.sckv_sparse_attn_sink_fp4.argtypes = [vp, vp, i64, vp, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32,
+                                            vp, vp, sz, vp]
     L.sckv_sparse_attn_sink_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32,
                                                 i32, vp, vp]
     L.sckv_sparse_attn_sink_noalloc_max_bytes.argtypes = []
@@ -165,7 +168,8 @@ def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_ne
                         ld_codes: int, k_scales, ld_scales: int, Di: int, kv_new: torch.Tensor, ld_kv_new: int,
                         ring: torch.Tensor, ld_ring: int, B: int, D: int, win: int, start_pos: int,
                         idx: torch.Tensor, ld_idx: int, rope_table: torch.Tensor | None = None, rope_dim: int = 0,
-                        lat_pos: int = 0, stream=None):
+                        lat_pos: int = 0, lat_codes=None, ld_lat_codes: int = 0, lat_scales=None,
+                        ld_lat_scales: int = 0, stream=None):
     """Row arguments: device tensors whose data pointers start the first row
     (lat_new / lat_dst / k_new / k_codes / k_scales / rope_table may be None;
     rope_table is the [n_pos, rope_dim/2, 2] f32 device table)."""
@@ -181,7 +185,8 @@ def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_ne
         p(k_scales, torch.uint8, "k_scales"), ld_scales, Di, p(kv_new, torch.bfloat16, "kv_new"), ld_kv_new,
         p(ring, torch.bfloat16, "ring"), ld_ring, B, D, win, start_pos, p(idx, torch.int32, "idx"), ld_idx,
         p(rope_table, torch.float32, "rope_table"), 0 if rope_table is None else rope_table.shape[0], rope_dim,
-        lat_pos, _stream(stream)))
+        lat_pos, p(lat_codes, torch.uint8, "lat_codes"), ld_lat_codes, p(lat_scales, torch.uint8, "lat_scales"),
+        ld_lat_scales, _stream(stream)))
 
 
 def sckv_yarn_freqs_cis(dim: int, seqlen: int, original_seq_len: int, base: float, factor: float, beta_fast: float,
@@ -204,6 +209,21 @@ def sckv_rope_quant_rows(x: torch.Tensor, ldx: int, y: torch.Tensor, ldy: int, r
     _check("sckv_rope_quant_rows", lib.sckv_rope_quant_rows(
         x.data_ptr(), ldx, y.data_ptr(), ldy, rows, cols, _ptr(table, torch.float32, "table"), table.shape[0],
         rope_dim, pos0, pos_step, _stream(stream)))
+
+
+def sckv_rope_quant_pack(x: torch.Tensor, ldx: int, codes: torch.Tensor, ldc: int, scales: torch.Tensor, lds: int,
+                         rows: int, cols: int, table: torch.Tensor, rope_dim: int, pos0: int, pos_step: int,
+                         stream=None):
+    """x: bf16 device tensor; codes / scales: uint8 device tensors, each
+    tensor's data pointer at its first row; table: [n_pos, rope_dim/2, 2] f32."""
+    if not x.is_cuda or x.dtype != torch.bfloat16:
+        raise ValueError("x: expected a bf16 device tensor")
+    for t, n in ((codes, "codes"), (scales, "scales")):
+        if not t.is_cuda or t.dtype != torch.uint8:
+            raise ValueError(f"{n}: expected a uint8 device tensor")
+    _check("sckv_rope_quant_pack", lib.sckv_rope_quant_pack(
+        x.data_ptr(), ldx, codes.data_ptr(), ldc, scales.data_ptr(), lds, rows, cols,
+        _ptr(table, torch.float32, "table"), table.shape[0], rope_dim, pos0, pos_step, _stream(stream)))
 
 
 def sckv_rows_a_len(win: int, m: int, start_pos: int) -> int:
@@ -270,3 +290,16 @@ def sckv_sparse_attn_sink_noalloc(q: torch.Tensor, rows_a: torch.Tensor, ra: int
 
 def sckv_sparse_attn_sink_noalloc_max_bytes() -> int:
     return int(lib.sckv_sparse_attn_sink_noalloc_max_bytes())
+
+
+def sckv_sparse_attn_sink_fp4(q: torch.Tensor, rows_a: torch.Tensor, ra: int, rows_b_codes: torch.Tensor | None,
+                              rows_b_scales: torch.Tensor | None, rb: int, idx: torch.Tensor, T: int,
+                              sink: torch.Tensor, scale: float, B: int, m: int, H: int, D: int, out: torch.Tensor,
+                              ws: torch.Tensor | None = None, stream=None):
+    if ws is None:
+        ws = workspace(SCKV_OP_SPARSE_ATTN_SINK, B, m, H, D, T, device=out.device)
+    _check("sckv_sparse_attn_sink_fp4", lib.sckv_sparse_attn_sink_fp4(
+        _ptr(q, torch.bfloat16, "q"), _ptr(rows_a, torch.bfloat16, "rows_a"), ra,
+        _ptr(rows_b_codes, torch.uint8, "rows_b_codes"), _ptr(rows_b_scales, torch.uint8, "rows_b_scales"), rb,
+        _ptr(idx, torch.int32, "idx"), T, _ptr(sink, torch.float32, "sink"), float(scale), B, m, H, D,
+        _ptr(out, torch.bfloat16, "out"), _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))

@@ -131,13 +131,29 @@ __device__ __forceinline__ float lane_xor1(float v) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
 }
 
-template <int D, int NHW, int CPS, int NS, bool CS>
+// e4m3 scale byte (E4M3FN code of a positive finite scale) as binary32.
+__device__ __forceinline__ float e4m3_code_to_f32(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15u, mt = c & 7u;
+    return e ? __uint_as_float(((e + 120u) << 23) | (mt << 20)) : (float)mt * 0x1p-9f;
+}
+
+// PK: rows_b is the packed latent cache (sckv_rope_quant_pack / sckv_quant_pack
+// in SCKV_FP4_E4M3_B16: codes [rb][D/2] bytes at rows_b, e4m3 scale bytes
+// [rb][D/16] at rb_scales); D = 512 only.  A packed row's 256 code bytes and
+// 32 scale bytes are copied into the last 288 bytes of its 2 D + 32-byte stage
+// slot, and the wave that copied it expands it in place to the bf16 row
+// (codes x scale, exact) before the chunk's barrier.
+template <int D, int NHW, int CPS, int NS, bool CS, bool PK = false>
 __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
-    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const uint8_t* __restrict__ rb_scales) {
     using S = AttnShape<D, NHW, CPS, NS, CS>;
+    static_assert(!PK || D == 512, "packed rows_b at D = 512 only");
+    constexpr int PKB = D / 2 + D / 16;  // packed bytes of a row (codes, then scale bytes)
+    constexpr int PKO = S::RS - PKB;     // where they land in the row's stage slot
     constexpr int NTH = S::WAVES * 64;
     extern __shared__ __align__(16) unsigned char lds[];
     int32_t* idx_l = reinterpret_cast<int32_t*>(lds + S::OFF_IDX);
@@ -153,7 +169,9 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
     const int split = (int)(blockIdx.x - qi * nsplit);
     const int64_t b = (uint32_t)qi / (uint32_t)m;  // query counts are below 2^31 (checked at launch)
     const uint16_t* rows_a_b = rows_a + b * ra * D;
-    const uint16_t* rows_b_b = rows_b ? rows_b + b * rb * D : nullptr;
+    const uint16_t* rows_b_b = (rows_b && !PK) ? rows_b + b * rb * D : nullptr;
+    const uint8_t* codes_b = PK ? reinterpret_cast<const uint8_t*>(rows_b) + b * rb * (D / 2) : nullptr;
+    const uint8_t* scl_b = PK ? rb_scales + b * rb * (D / 16) : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
     const uint16_t* qrow = q + qi * (int64_t)H * D;
 
@@ -291,12 +309,35 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
             // writing a scalar register and a memory instruction reading it)
             const uint32_t iv = (uint32_t)ic[lane & (S::RPW - 1)];
             const uint16_t* base = (iv < (uint32_t)ra) ? rows_a_b : rows_b_sh;
-            const uint64_t addr = (uint64_t)((iv < rab) ? base + (size_t)iv * D : qrow);
+            // PK: a packed row's codes and scale bytes (rows_b rows only)
+            const bool pk = PK && iv >= (uint32_t)ra && iv < rab;
+            const uint64_t addr = pk ? (uint64_t)(codes_b + (size_t)(iv - (uint32_t)ra) * (D / 2))
+                                     : (uint64_t)((iv < rab) ? base + (size_t)iv * D : qrow);
+            const uint64_t saddr = pk ? (uint64_t)(scl_b + (size_t)(iv - (uint32_t)ra) * (D / 16)) : 0ull;
 #pragma unroll
             for (int rr = 0; rr < S::RPW; ++rr) {
                 const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)addr, rr);
                 const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), rr);
                 const uint32_t lb = st + (uint32_t)((hw * S::RPW + rr) * S::RS);
+                if (PK && __builtin_amdgcn_readlane((int)pk, rr)) {
+                    // 16 lanes copy the 256 code bytes, 2 lanes the 32 scale
+                    // bytes, into the slot's last 288 bytes
+                    const uint32_t slo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)saddr, rr);
+                    const uint32_t shi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(saddr >> 32), rr);
+                    if (lane < D / 32)
+                        asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                                     :
+                                     : "v"((uint32_t)lane * 16u), "s"((const void*)(((uint64_t)hi << 32) | lo)),
+                                       "s"(lb + (uint32_t)PKO)
+                                     : "memory", "m0");
+                    if (lane < D / 256)
+                        asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+                                     :
+                                     : "v"((uint32_t)lane * 16u), "s"((const void*)(((uint64_t)shi << 32) | slo)),
+                                       "s"(lb + (uint32_t)(PKO + D / 2))
+                                     : "memory", "m0");
+                    continue;
+                }
                 asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
                              :
                              : "v"((uint32_t)lane * 16u), "s"((const void*)(((uint64_t)hi << 32) | lo)), "s"(lb)
@@ -322,6 +363,51 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
         }
     };
 
+    // PK: expand this wave's packed rows of chunk j (stage at stp) in place:
+    // lane (row 4 rho + lane / 16, piece k = lane % 16) turns the 16 code
+    // bytes of values 32 k .. 32 k + 31 (blocks 2k, 2k + 1) into 64 bf16
+    // bytes at the start of the row; every lane reads before any lane writes
+    // (the writes need the read values), so the overlap of the last pieces'
+    // outputs with the packed bytes is harmless.
+    auto expand = [&](const unsigned char* stp, int j) {
+        if constexpr (PK) {
+            unsigned char* stw = const_cast<unsigned char*>(stp);
+#pragma unroll
+            for (int rho = 0; rho < S::RPW / 4; ++rho) {
+                const int rr = 4 * rho + (lane >> 4);
+                const int k = lane & 15;
+                const uint32_t iv = (uint32_t)idx_l[j * CHUNK + hw * S::RPW + rr];
+                if (iv >= (uint32_t)ra && iv < rab) {
+                    unsigned char* row = stw + (hw * S::RPW + rr) * S::RS;
+                    const u32x4 c = *reinterpret_cast<const u32x4*>(row + PKO + 16 * k);
+                    const uint32_t sb = *reinterpret_cast<const uint16_t*>(row + PKO + D / 2 + 2 * k);
+                    asm volatile("" ::: "memory");
+                    const float s0 = e4m3_code_to_f32(sb & 0xffu), s1 = e4m3_code_to_f32(sb >> 8);
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const float sc = d < 2 ? s0 : s1;
+                        // byte by of code word d: values 32 k + 8 d + 2 by (low nibble) and + 1;
+                        // the products have at most 6 significant bits, so they and the
+                        // bf16 packing are exact
+                        const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], 1.0f, 0);
+                        const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], 1.0f, 1);
+                        const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], 1.0f, 2);
+                        const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c[d], 1.0f, 3);
+                        u32x4 ov;
+                        ov[0] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0[0] * sc, v0[1] * sc}, bf16x2));
+                        ov[1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v1[0] * sc, v1[1] * sc}, bf16x2));
+                        ov[2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v2[0] * sc, v2[1] * sc}, bf16x2));
+                        ov[3] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v3[0] * sc, v3[1] * sc}, bf16x2));
+                        *reinterpret_cast<u32x4*>(row + 64 * k + 16 * d) = ov;
+                    }
+                }
+            }
+        } else {
+            (void)stp;
+            (void)j;
+        }
+    };
+
     f32x4 o[S::NT];
 #pragma unroll
     for (int nt = 0; nt < S::NT; ++nt) o[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -341,10 +427,11 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
             const unsigned char* stp = lds + (set * S::NST + (it & 1)) * S::STAGE;
             if (!resume) {
                 wait_vmcnt<0>();  // this wave's copies of its current chunk landed
+                const int j = (it < n_own) ? next_own(cb) : 0;
+                if (PK && it < n_own) expand(stp, j);
                 __syncthreads();  // everyone's did; last iteration's stages are free
                 if (it + 1 < n_own) issue((it + 1) & 1, next_own(ib));
                 if (it < n_own) {
-                    const int j = next_own(cb);
                     const uint32_t mask =
                         (uint32_t)(__ballot((uint32_t)idx_l[j * CHUNK + (lane & 31)] < rab) & 0xffffffffull);
                     // S^T for rows 0-15 and 16-31: lane holds head l16, rows mt*16 + g*4 + 0..3
@@ -732,25 +819,28 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     *nsplit = (nchunks + cps - 1) / cps;
 }
 
-template <int D, int NHW, int CPS, int NS = 2, bool CS = false>
+template <int D, int NHW, int CPS, int NS = 2, bool CS = false, bool PK = false>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
-                int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
+                int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
+                const uint8_t* rb_scales) {
     using Sh = AttnShape<D, NHW, CPS, NS, CS>;
     if (Sh::LDS_BYTES > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS, CS>,
+        hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS, CS, PK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<D, NHW, CPS, NS, CS><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES, s>>>(
-        q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps, nsplit, out, part_o, part_ml);
+    sparse_attn_kernel<D, NHW, CPS, NS, CS, PK><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES,
+                                                 s>>>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps,
+                                                      nsplit, out, part_o, part_ml, rb_scales);
     return check_launch("sckv_sparse_attn_sink");
 }
 
-template <int D, int NHW>
+template <int D, int NHW, bool PK = false>
 int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
-                  int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
+                  int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
+                  const uint8_t* rb_scales) {
     if constexpr (D == 512 && NHW == 4) {
         // unsplit lists of up to 64 chunks and at least two queries per
         // compute unit: one set of 4 waves (76 KB of LDS), so that two
@@ -760,33 +850,34 @@ int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
         const int ncu = compute_units();
         const bool one_set = nsplit == 1 && ncu > 0 && nq >= 2 * (int64_t)ncu;
         if (cps <= 64 && one_set)
-            return launch_attn<D, NHW, 64, 1, true>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
-                                              nsplit, out, part_o, part_ml, s);
+            return launch_attn<D, NHW, 64, 1, true, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
+                                                        cps, nsplit, out, part_o, part_ml, s, rb_scales);
         // (up to 72 chunks, e.g. a 128-row window plus a top-2048 list: the
         // index buffer still leaves room for two workgroups)
         if (cps <= 72 && one_set)
-            return launch_attn<D, NHW, 72, 1, true>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps,
-                                              nsplit, out, part_o, part_ml, s);
+            return launch_attn<D, NHW, 72, 1, true, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
+                                                        cps, nsplit, out, part_o, part_ml, s, rb_scales);
     }
     if (cps <= 64)
-        return launch_attn<D, NHW, 64>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
-                                       out, part_o, part_ml, s);
-    return launch_attn<D, NHW, MAX_CPS>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
-                                        out, part_o, part_ml, s);
+        return launch_attn<D, NHW, 64, 2, false, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
+                                                     cps, nsplit, out, part_o, part_ml, s, rb_scales);
+    return launch_attn<D, NHW, MAX_CPS, 2, false, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
+                                                      cps, nsplit, out, part_o, part_ml, s, rb_scales);
 }
 
-template <int D>
+template <int D, bool PK = false>
 int launch_attn_d(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
-                  int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s) {
+                  int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
+                  const uint8_t* rb_scales) {
     if (H <= 16)
-        return launch_attn_c<D, 1>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
-                                   part_o, part_ml, s);
+        return launch_attn_c<D, 1, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
+                                       out, part_o, part_ml, s, rb_scales);
     if (H <= 32)
-        return launch_attn_c<D, 2>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
-                                   part_o, part_ml, s);
-    return launch_attn_c<D, 4>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
-                               part_o, part_ml, s);
+        return launch_attn_c<D, 2, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
+                                       out, part_o, part_ml, s, rb_scales);
+    return launch_attn_c<D, 4, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, out,
+                                   part_o, part_ml, s, rb_scales);
 }
 
 }  // namespace
@@ -809,9 +900,11 @@ namespace {
 
 // The whole call (checks, attention launch, combine of split partials) with
 // the partials in ws; `name` prefixes error messages.
+// rb_scales non-NULL: rows_b is the packed latent cache (codes; see the
+// kernel's PK variant), D = 512 only.
 int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, const void* rows_b, int64_t rb,
              const int32_t* idx, int T, const float* sink, float scale, int B, int64_t m, int H, int D, void* out,
-             void* ws, size_t ws_bytes, void* stream) {
+             void* ws, size_t ws_bytes, void* stream, const void* rb_scales = nullptr) {
     if (B < 0 || m < 0 || ra < 0 || rb < 0 || H <= 0 || D <= 0 || T < 0)
         return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
     if (H > 64) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": H > 64");
@@ -827,6 +920,11 @@ int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, co
         return fail(SCKV_EINVAL, std::string(name) + ": q / rows / out must be 16-byte aligned");
     if (ra + rb > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": ra + rb >= 2^31");
     if (!(scale > 0.0f) || !(scale < INFINITY)) return fail(SCKV_EINVAL, std::string(name) + ": bad scale");
+    if (rb_scales) {
+        if (D != 512) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": packed rows_b at D = 512 only");
+        if ((uintptr_t)rb_scales % 16)
+            return fail(SCKV_EINVAL, std::string(name) + ": packed rows_b scale bytes must be 16-byte aligned");
+    }
     const int64_t nq = (int64_t)B * m;
     int cps, nsplit;
     attn_split(nq, T, &cps, &nsplit);
@@ -848,13 +946,19 @@ int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, co
     const uint16_t* bb = (const uint16_t*)rows_b;
     uint16_t* oo = (uint16_t*)out;
     int rc;
+    const uint8_t* sc = (const uint8_t*)rb_scales;
 #define SCKV_ATTN(D) \
-    launch_attn_d<D>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s)
-    switch (D) {
-        case 64: rc = SCKV_ATTN(64); break;
-        case 128: rc = SCKV_ATTN(128); break;
-        case 256: rc = SCKV_ATTN(256); break;
-        default: rc = SCKV_ATTN(512); break;
+    launch_attn_d<D>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s, sc)
+    if (rb_scales) {
+        rc = launch_attn_d<512, true>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o,
+                                      part_ml, s, sc);
+    } else {
+        switch (D) {
+            case 64: rc = SCKV_ATTN(64); break;
+            case 128: rc = SCKV_ATTN(128); break;
+            case 256: rc = SCKV_ATTN(256); break;
+            default: rc = SCKV_ATTN(512); break;
+        }
     }
 #undef SCKV_ATTN
     if (rc || nsplit == 1) return rc;
@@ -925,4 +1029,16 @@ extern "C" int sckv_sparse_attn_sink_noalloc(const void* q, const void* rows_a, 
     }
     return attn_run("sckv_sparse_attn_sink_noalloc", q, rows_a, ra, rows_b, rb, idx, T, sink, scale, B, m, H, D, out,
                     ws, NOALLOC_SCRATCH_BYTES, stream);
+}
+
+extern "C" int sckv_sparse_attn_sink_fp4(const void* q, const void* rows_a, int64_t ra, const void* rows_b_codes,
+                                         const void* rows_b_scales, int64_t rb, const int32_t* idx, int T,
+                                         const float* sink, float scale, int B, int64_t m, int H, int D, void* out,
+                                         void* ws, size_t ws_bytes, void* stream) {
+    using namespace sckv;
+    if (rb > 0 && !rows_b_scales) return fail(SCKV_EINVAL, "sckv_sparse_attn_sink_fp4: null rows_b scale bytes");
+    if (D != 512) return fail(SCKV_EUNSUPPORTED, "sckv_sparse_attn_sink_fp4: D must be 512");
+    // (no rows_b: the bf16 kernel is the same computation)
+    return attn_run("sckv_sparse_attn_sink_fp4", q, rows_a, ra, rows_b_codes, rb, idx, T, sink, scale, B, m, H, D,
+                    out, ws, ws_bytes, stream, rb > 0 ? rows_b_scales : nullptr);
 }

@@ -44,6 +44,10 @@ struct PrepArgs {
     const float* rope_table;  // NULL: the latent row is not rotated
     int rope_dim;
     int64_t lat_pos;
+    uint8_t* lat_codes;  // non-NULL: the latent row is stored packed (codes + e4m3 scale bytes)
+    int64_t ld_lat_codes;
+    uint8_t* lat_scales;
+    int64_t ld_lat_scales;
 };
 
 // Max over aligned groups of 8 or 16 lanes by DPP (every lane of the group
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(PREP_THREADS) void decode_prepare_kernel(PrepArgs a
     // latent row: values 2p, 2p + 1 in lane p (E4M3_B16 round trip, bf16 out)
     if (a.lat_new) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.lat_new + b * a.ld_lat_new);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(a.lat_dst + b * a.ld_lat_dst);
+        uint32_t* dst = a.lat_dst ? reinterpret_cast<uint32_t*>(a.lat_dst + b * a.ld_lat_dst) : nullptr;
         const int rope_first = (a.D - a.rope_dim) / 2;  // first pair of the rope slice
         const float2* rt = a.rope_table ? reinterpret_cast<const float2*>(a.rope_table) + a.lat_pos * (a.rope_dim / 2)
                                         : nullptr;
@@ -82,7 +86,16 @@ __global__ __launch_bounds__(PREP_THREADS) void decode_prepare_kernel(PrepArgs a
             const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
             const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 8);
             const float s = block_scale<SCKV_FP4_E4M3_B16>(amax);
-            dst[p] = fp4_value<SCKV_FP4_E4M3_B16>(lo, s, 0.0f) | (fp4_value<SCKV_FP4_E4M3_B16>(hi, s, 0.0f) << 16);
+            if (a.lat_codes) {
+                // packed (sckv_rope_quant_pack): one code byte a lane, the
+                // e4m3 scale byte from the block's first lane
+                const uint32_t clo = e2m1_code(e2m1_round_mag(fminf(__fdiv_rn(fabsf(lo), s), 6.0f)), lo);
+                const uint32_t chi = e2m1_code(e2m1_round_mag(fminf(__fdiv_rn(fabsf(hi), s), 6.0f)), hi);
+                a.lat_codes[b * a.ld_lat_codes + p] = (uint8_t)(clo | (chi << 4));
+                if ((p & 7) == 0) a.lat_scales[b * a.ld_lat_scales + p / 8] = (uint8_t)scale_byte<SCKV_FP4_E4M3_B16>(s);
+            } else {
+                dst[p] = fp4_value<SCKV_FP4_E4M3_B16>(lo, s, 0.0f) | (fp4_value<SCKV_FP4_E4M3_B16>(hi, s, 0.0f) << 16);
+            }
         }
     }
     // indexer k row: values 2p, 2p + 1 in lane p (E8M0_B32, packed: one code
@@ -130,13 +143,18 @@ extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void
                                    void* k_scales, int64_t ld_scales, int Di, const void* kv_new, int64_t ld_kv_new,
                                    void* ring, int64_t ld_ring, int B, int D, int win, int64_t start_pos,
                                    int32_t* idx, int64_t ld_idx, const float* rope_table, int64_t n_pos,
-                                   int rope_dim, int64_t lat_pos, void* stream) {
+                                   int rope_dim, int64_t lat_pos, void* lat_codes, int64_t ld_lat_codes,
+                                   void* lat_scales, int64_t ld_lat_scales, void* stream) {
     using namespace sckv;
     const char* name = "sckv_decode_prepare";
     if (B < 0 || D <= 0 || win <= 0 || start_pos < 0) return fail(SCKV_EINVAL, std::string(name) + ": bad sizes");
     if (D % 16 != 0) return fail(SCKV_EINVAL, std::string(name) + ": D is not a multiple of 16");
-    if (lat_new && (!lat_dst || ld_lat_new < D || ld_lat_dst < D))
+    if (lat_new && !lat_codes && (!lat_dst || ld_lat_new < D || ld_lat_dst < D))
         return fail(SCKV_EINVAL, std::string(name) + ": latent rows: null destination or stride below D");
+    if (lat_new && lat_codes &&
+        (lat_dst || !lat_scales || ld_lat_new < D || ld_lat_codes < D / 2 || ld_lat_scales < D / 16))
+        return fail(SCKV_EINVAL, std::string(name) + ": packed latent rows: give codes and scales (and no bf16 "
+                                                     "destination) with strides of at least D/2 and D/16 bytes");
     if (k_new && (!k_codes || !k_scales || Di <= 0 || Di % 32 != 0 || ld_k_new < Di || ld_codes < Di / 2 ||
                   ld_scales < Di / 32))
         return fail(SCKV_EINVAL, std::string(name) + ": k rows: null destination, Di not a multiple of 32 or short stride");
@@ -153,14 +171,15 @@ extern "C" int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void
     if (start_pos + win > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": positions past 2^31");
     // 16-byte vectors throughout
     const bool ok = aligned16(kv_new) && aligned16(ring) && (ld_kv_new % 8 == 0) && (ld_ring % 8 == 0) &&
-                    (!lat_new || (aligned16(lat_new) && aligned16(lat_dst) && ld_lat_new % 8 == 0 &&
-                                  ld_lat_dst % 8 == 0)) &&
+                    (!lat_new || (aligned16(lat_new) && ld_lat_new % 8 == 0 &&
+                                  (lat_codes || (aligned16(lat_dst) && ld_lat_dst % 8 == 0)))) &&
                     (!k_new || (aligned16(k_new) && aligned16(k_codes) && ld_k_new % 8 == 0 && ld_codes % 16 == 0));
     if (!ok) return fail(SCKV_EINVAL, std::string(name) + ": rows must be 16-byte aligned with 16-byte strides");
     PrepArgs a{(const uint16_t*)lat_new, ld_lat_new, (uint16_t*)lat_dst, ld_lat_dst, (const uint16_t*)k_new, ld_k_new,
                (uint8_t*)k_codes, ld_codes, (uint8_t*)k_scales, ld_scales, Di, (const uint16_t*)kv_new, ld_kv_new,
                (uint16_t*)ring, ld_ring, D, win, start_pos, idx, ld_idx, lat_new ? rope_table : nullptr,
-               rope_dim, lat_pos};
+               rope_dim, lat_pos, lat_new ? (uint8_t*)lat_codes : nullptr, ld_lat_codes, (uint8_t*)lat_scales,
+               ld_lat_scales};
     decode_prepare_kernel<<<dim3((unsigned)B), dim3(PREP_THREADS), 0, (hipStream_t)stream>>>(a);
     return check_launch(name);
 }

@@ -25,6 +25,39 @@ struct RopeArgs {
     int64_t pos0, pos_step;
 };
 
+// Checks of a rotation table and the rows' positions (every row's position
+// pos0 + r * pos_step inside the table).
+int rope_checks(const char* name, int64_t rows, int64_t cols, const float* table, int64_t n_pos, int rope_dim,
+                int64_t pos0, int64_t pos_step) {
+    if (n_pos < 0 || pos0 < 0 || pos_step < 0) return fail(SCKV_EINVAL, std::string(name) + ": negative position");
+    if (rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > cols)
+        return fail(SCKV_EINVAL, std::string(name) + ": rope_dim must be even, positive and at most the row length");
+    if (!table || (uintptr_t)table % 8)
+        return fail(SCKV_EINVAL, std::string(name) + ": null or misaligned (8 bytes) rotation table");
+    if (rows > 0 && pos0 + (rows - 1) * pos_step >= n_pos)
+        return fail(SCKV_EINVAL, std::string(name) + ": a row's position is outside the rotation table");
+    return SCKV_OK;
+}
+
+// The rotary turn of the pairs of one block (values col .. col + BLOCK - 1 of
+// row `row`, held as bf16 pairs) that fall in the rope slice.
+template <int BLOCK>
+__device__ __forceinline__ void rope_block(uint32_t (&w)[BLOCK / 2], int64_t row, int64_t col, int64_t cols,
+                                           const RopeArgs& rope) {
+    const int64_t first = cols - rope.rope_dim;  // first value of the rope slice (even)
+    if (col + BLOCK <= first) return;
+    const int half = rope.rope_dim / 2;
+    const float2* t = reinterpret_cast<const float2*>(rope.table) + (rope.pos0 + row * rope.pos_step) * half;
+#pragma unroll
+    for (int k = 0; k < BLOCK / 2; ++k) {
+        const int64_t c = col + 2 * k;
+        if (c >= first) {
+            const float2 cs = t[(c - first) / 2];
+            w[k] = rope_pair_bits(w[k], cs.x, cs.y);
+        }
+    }
+}
+
 template <int MODE, bool VEC, bool ROPE = false>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     uint16_t* __restrict__ y, int64_t ldy,
@@ -52,22 +85,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_rows_kernel(const uint16_
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
     }
-    if (ROPE) {
-        const int64_t cols = blocks_per_row * BLOCK;
-        const int64_t first = cols - rope.rope_dim;  // first value of the rope slice (even)
-        if (col + BLOCK > first) {
-            const int half = rope.rope_dim / 2;
-            const float2* t = reinterpret_cast<const float2*>(rope.table) + (rope.pos0 + row * rope.pos_step) * half;
-#pragma unroll
-            for (int k = 0; k < BLOCK / 2; ++k) {
-                const int64_t c = col + 2 * k;
-                if (c >= first) {
-                    const float2 cs = t[(c - first) / 2];
-                    w[k] = rope_pair_bits(w[k], cs.x, cs.y);
-                }
-            }
-        }
-    }
+    if (ROPE) rope_block<BLOCK>(w, row, col, blocks_per_row * BLOCK, rope);
     quant_block<MODE>(w);
     if (VEC) {
 #pragma unroll
@@ -132,18 +150,14 @@ int rope_quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64
                          const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
                          void* stream) {
     const char* name = "sckv_rope_quant_rows";
-    if (rows < 0 || cols < 0 || n_pos < 0 || pos0 < 0 || pos_step < 0)
-        return fail(SCKV_EINVAL, std::string(name) + ": negative size or position");
+    if (rows < 0 || cols < 0) return fail(SCKV_EINVAL, std::string(name) + ": negative size");
     if (cols % 16 != 0) return fail(SCKV_EINVAL, std::string(name) + ": row length is not a multiple of 16");
-    if (rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > cols)
-        return fail(SCKV_EINVAL, std::string(name) + ": rope_dim must be even, positive and at most the row length");
+    if (const int rc = rope_checks(name, rows, cols, table, n_pos, rope_dim, pos0, pos_step)) return rc;
     if (rows == 0 || cols == 0) return SCKV_OK;
-    if (!x || !y || !table) return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
+    if (!x || !y) return fail(SCKV_EINVAL, std::string(name) + ": null pointer");
     if (ldx < cols || ldy < cols) return fail(SCKV_EINVAL, std::string(name) + ": row stride shorter than the row");
-    if ((uintptr_t)x % 2 || (uintptr_t)y % 2 || (uintptr_t)table % 8)
-        return fail(SCKV_EINVAL, std::string(name) + ": misaligned pointer (bf16 rows 2 bytes, table 8 bytes)");
-    if (pos0 + (rows - 1) * pos_step >= n_pos)
-        return fail(SCKV_EINVAL, std::string(name) + ": a row's position is outside the rotation table");
+    if ((uintptr_t)x % 2 || (uintptr_t)y % 2)
+        return fail(SCKV_EINVAL, std::string(name) + ": misaligned pointer (bf16 rows 2 bytes)");
     if (x != y) {
         const uintptr_t xs = (uintptr_t)x, ys = (uintptr_t)y;
         const uintptr_t xe = xs + (uintptr_t)(((rows - 1) * ldx + cols) * 2);
@@ -171,12 +185,12 @@ int rope_quant_rows_impl(const void* x, int64_t ldx, void* y, int64_t ldy, int64
 
 // ---- packed storage: 4-bit codes (two a byte, the even element low) and one
 // scale byte per block; one lane per block, as above.
-template <int MODE>
+template <int MODE, bool ROPE = false>
 __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_t* __restrict__ x, int64_t ldx,
                                                                     uint8_t* __restrict__ codes, int64_t ldc,
                                                                     uint8_t* __restrict__ scales, int64_t lds,
                                                                     int64_t blocks_per_row, int64_t nblocks,
-                                                                    bool vec) {
+                                                                    bool vec, RopeArgs rope = RopeArgs{}) {
     constexpr int BLOCK = QuantMode<MODE>::BLOCK;
     const int64_t gid = (int64_t)blockIdx.x * QUANT_THREADS + threadIdx.x;
     if (gid >= nblocks) return;
@@ -197,6 +211,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_
 #pragma unroll
         for (int i = 0; i < BLOCK / 2; ++i) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
     }
+    if (ROPE) rope_block<BLOCK>(w, row, blk * BLOCK, blocks_per_row * BLOCK, rope);
     // BLOCK/2 bytes of codes: byte i holds elements 2i (low) and 2i+1 (high)
     uint32_t cw[BLOCK / 8];
     const uint32_t sbyte = pack_block<MODE>(w, cw);
@@ -217,7 +232,7 @@ __global__ __launch_bounds__(QUANT_THREADS) void quant_pack_kernel(const uint16_
 }  // namespace
 
 int quant_pack_launch(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds, int64_t rows,
-                      int64_t cols, int mode, void* stream) {
+                      int64_t cols, int mode, void* stream, const RopeArgs* rope = nullptr) {
     if (mode != SCKV_FP4_E4M3_B16 && mode != SCKV_FP4_E8M0_B32) return fail(SCKV_EINVAL, "sckv_quant_pack: bad mode");
     const int block = (mode == SCKV_FP4_E4M3_B16) ? 16 : 32;
     if (rows < 0 || cols < 0) return fail(SCKV_EINVAL, "sckv_quant_pack: negative size");
@@ -238,7 +253,10 @@ int quant_pack_launch(const void* x, int64_t ldx, void* codes, int64_t ldc, void
     if (grid > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, "sckv_quant_pack: too many blocks for one launch");
     const bool vec = (xs % 16 == 0) && (ldx % 8 == 0) && (cs % (block / 2) == 0) && (ldc % (block / 2) == 0);
     hipStream_t s = (hipStream_t)stream;
-    if (mode == SCKV_FP4_E4M3_B16)
+    if (rope)  // the latent: rotation, then the e4m3-scale round trip
+        quant_pack_kernel<SCKV_FP4_E4M3_B16, true><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
+            (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec, *rope);
+    else if (mode == SCKV_FP4_E4M3_B16)
         quant_pack_kernel<SCKV_FP4_E4M3_B16><<<dim3((unsigned)grid), dim3(QUANT_THREADS), 0, s>>>(
             (const uint16_t*)x, ldx, (uint8_t*)codes, ldc, (uint8_t*)scales, lds, bpr, nblocks, vec);
     else
@@ -274,4 +292,16 @@ extern "C" int sckv_rope_quant_rows(const void* x, int64_t ldx, void* y, int64_t
                                     const float* table, int64_t n_pos, int rope_dim, int64_t pos0, int64_t pos_step,
                                     void* stream) {
     return sckv::rope_quant_rows_impl(x, ldx, y, ldy, rows, cols, table, n_pos, rope_dim, pos0, pos_step, stream);
+}
+
+extern "C" int sckv_rope_quant_pack(const void* x, int64_t ldx, void* codes, int64_t ldc, void* scales, int64_t lds,
+                                    int64_t rows, int64_t cols, const float* table, int64_t n_pos, int rope_dim,
+                                    int64_t pos0, int64_t pos_step, void* stream) {
+    using namespace sckv;
+    const char* name = "sckv_rope_quant_pack";
+    if (rows < 0 || cols < 0) return fail(SCKV_EINVAL, std::string(name) + ": negative size");
+    if (cols % 16 != 0) return fail(SCKV_EINVAL, std::string(name) + ": row length is not a multiple of 16");
+    if (const int rc = rope_checks(name, rows, cols, table, n_pos, rope_dim, pos0, pos_step)) return rc;
+    const RopeArgs r{table, rope_dim, pos0, pos_step};
+    return quant_pack_launch(x, ldx, codes, ldc, scales, lds, rows, cols, SCKV_FP4_E4M3_B16, stream, &r);
 }

@@ -58,13 +58,19 @@ class PathState:
     raw CPU inputs (see sckv_synth.make_inputs).  setup() round-trips the cache
     rows that existed before this step; step() runs the hot path."""
 
-    def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16"):
+    def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16", latent: str = "bf16"):
         """kcache: "bf16" keeps the indexer k cache as round-tripped bf16 rows
         (the pages' layout); "fp4" keeps it packed (4-bit codes + one E8M0 byte
-        per 32 values) and scores it on the scaled fp4 matrix cores."""
+        per 32 values) and scores it on the scaled fp4 matrix cores.
+        latent: "bf16" keeps the latent cache as round-tripped bf16 rows (the
+        pages' layout); "fp4" keeps it packed (4-bit codes + one e4m3 byte per
+        16 values, 288 bytes a 512-wide row) and the attention expands the
+        rows it gathers on chip (D = 512)."""
         if kcache not in ("bf16", "fp4"):
             raise ValueError(kcache)
-        self.w, self.B, self.device, self.kcache = w, B, device, kcache
+        if latent not in ("bf16", "fp4") or (latent == "fp4" and w.D != 512):
+            raise ValueError(f"latent={latent} (packed latent rows need D = 512)")
+        self.w, self.B, self.device, self.kcache, self.latent_fmt = w, B, device, kcache, latent
         dev = lambda t: t.to(device).contiguous()  # noqa: E731
         self.q = dev(inputs["q"])
         self.sink = dev(inputs["sink"])
@@ -94,6 +100,9 @@ class PathState:
         self.rope_table = sk.sckv_yarn_freqs_cis(w.rope_dim, w.rope_positions, w.rope_orig_len, w.rope_base,
                                                  w.rope_factor, w.rope_beta_fast, w.rope_beta_slow).to(device)
         self.latent_new = lat[:, self.first_new:].to(device).clone()  # a buffer of its own, never a view
+        if latent == "fp4":
+            self.lat_codes = torch.zeros((B, w.n_c, D // 2), dtype=torch.uint8, device=device)
+            self.lat_scales = torch.zeros((B, w.n_c, D // 16), dtype=torch.uint8, device=device)
         if w.Hi:
             self.iq = dev(inputs["iq"])
             self.iw = dev(inputs["iw"])
@@ -116,8 +125,12 @@ class PathState:
         w, B = self.w, self.B
         if self.first_new > 0:
             for b in range(B):  # row j of each sequence turned at j * ratio, then round-tripped
-                sk.sckv_rope_quant_rows(self.latent[b], w.D, self.latent[b], w.D, self.first_new, w.D,
-                                        self.rope_table, w.rope_dim, 0, w.ratio)
+                if self.latent_fmt == "fp4":
+                    sk.sckv_rope_quant_pack(self.latent[b], w.D, self.lat_codes[b], w.D // 2, self.lat_scales[b],
+                                            w.D // 16, self.first_new, w.D, self.rope_table, w.rope_dim, 0, w.ratio)
+                else:
+                    sk.sckv_rope_quant_rows(self.latent[b], w.D, self.latent[b], w.D, self.first_new, w.D,
+                                            self.rope_table, w.rope_dim, 0, w.ratio)
             if w.Hi and self.kcache == "fp4":
                 # every row packed (the step's own new rows are packed again by its first calls)
                 sk.sckv_quant_pack(self.ik, w.Di, self.ik_codes, w.Di // 2, self.ik_scales, w.Di // 32, B * w.n_c,
@@ -129,6 +142,17 @@ class PathState:
     def _quant_new(self, src, dst, width, mode):
         w, B = self.w, self.B
         if self.n_new == 0:
+            return
+        if mode == sk.SCKV_FP4_E4M3_B16 and self.latent_fmt == "fp4":
+            # the latent, packed: rotary turn at j * ratio, round trip, codes + scale bytes
+            pos0, f, D = self.first_new * w.ratio, self.first_new, w.D
+            if self.n_new == 1:
+                sk.sckv_rope_quant_pack(src, width, self.lat_codes[:, f], w.n_c * D // 2, self.lat_scales[:, f],
+                                        w.n_c * D // 16, B, width, self.rope_table, w.rope_dim, pos0, 0)
+            else:
+                for b in range(B):
+                    sk.sckv_rope_quant_pack(src[b], width, self.lat_codes[b, f], D // 2, self.lat_scales[b, f],
+                                            D // 16, self.n_new, width, self.rope_table, w.rope_dim, pos0, w.ratio)
             return
         if mode == sk.SCKV_FP4_E4M3_B16:
             # the latent: rotary turn at j * ratio, then the round trip
@@ -175,11 +199,14 @@ class PathState:
             # columns in one launch (the same results as the four calls below)
             f = self.first_new
             new = self.n_new == 1
+            pk = self.latent_fmt == "fp4"
             out = [("decode_prepare", lambda: sk.sckv_decode_prepare(
-                self.latent_new if new else None, D, self.latent[:, f] if new else None, w.n_c * D,
+                self.latent_new if new else None, D, self.latent[:, f] if (new and not pk) else None, w.n_c * D,
                 self.ik_new if new else None, w.Di, self.ik_codes[:, f] if new else None, w.n_c * w.Di // 2,
                 self.ik_scales[:, f] if new else None, w.n_c * w.Di // 32, w.Di, self.kv_new, D, self.ring, win * D,
-                B, D, win, w.start_pos, self.idx, self.T, self.rope_table, w.rope_dim, f * w.ratio))]
+                B, D, win, w.start_pos, self.idx, self.T, self.rope_table, w.rope_dim, f * w.ratio,
+                self.lat_codes[:, f] if (new and pk) else None, w.n_c * D // 2,
+                self.lat_scales[:, f] if (new and pk) else None, w.n_c * D // 16))]
             return out + self._score_and_attend_calls()
         out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
         if w.Hi and self.kcache == "fp4":
@@ -208,9 +235,14 @@ class PathState:
         else:
             out.append(("visible_idx", lambda: sk.sckv_visible_idx(B, m, w.start_pos, w.ratio, w.n_c, w.K, self.ra,
                                                                    self.idx, self.T, win)))
-        out.append(("sparse_attn_sink", lambda: sk.sckv_sparse_attn_sink(
-            self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink, w.scale, B, m, w.H, D,
-            self.out, ws=self.ws_attn)))
+        if self.latent_fmt == "fp4":
+            out.append(("sparse_attn_sink", lambda: sk.sckv_sparse_attn_sink_fp4(
+                self.q, self.rows_a, self.ra, self.lat_codes, self.lat_scales, w.n_c, self.idx, self.T, self.sink,
+                w.scale, B, m, w.H, D, self.out, ws=self.ws_attn)))
+        else:
+            out.append(("sparse_attn_sink", lambda: sk.sckv_sparse_attn_sink(
+                self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink, w.scale, B, m, w.H, D,
+                self.out, ws=self.ws_attn)))
         if self.mode == "fresh":
             out.append(("ring_write", lambda: sk.sckv_ring_write(self.rows_a, m * D, self.ring, win * D, B, m,
                                                                  w.start_pos, win, D)))

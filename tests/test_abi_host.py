@@ -21,7 +21,7 @@ def test_header_declares_the_calls():
     for n in ["sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_rows_a_len", "sckv_window_idx",
               "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
               "sckv_last_error", "sckv_abi_version", "sckv_quant_pack", "sckv_index_scores_topk_fp4",
-              "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows"]:
+              "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows", "sckv_rope_quant_pack"]:
         assert n in names
 
 
@@ -144,14 +144,16 @@ def test_error_paths(L):
     def dp(**kw):
         a = dict(ld_lat_new=512, ld_lat_dst=512, ld_k_new=128, ld_codes=64, ld_scales=4, Di=128, ld_kv_new=512,
                  ld_ring=128 * 512, B=2, D=512, win=128, start_pos=1000, ld_idx=640, n_pos=4000, rope_dim=64,
-                 lat_pos=996)
+                 lat_pos=996, ld_lat_codes=256, ld_lat_scales=32)
         a.update({k: v for k, v in kw.items() if k in a})
         return L.sckv_decode_prepare(kw.get("lat_new", fake), a["ld_lat_new"], kw.get("lat_dst", fake),
                                      a["ld_lat_dst"], kw.get("k_new", fake), a["ld_k_new"], kw.get("k_codes", fake),
                                      a["ld_codes"], kw.get("k_scales", fake), a["ld_scales"], a["Di"],
                                      kw.get("kv_new", fake), a["ld_kv_new"], kw.get("ring", fake), a["ld_ring"],
                                      a["B"], a["D"], a["win"], a["start_pos"], kw.get("idx", fake), a["ld_idx"],
-                                     kw.get("rope_table", None), a["n_pos"], a["rope_dim"], a["lat_pos"], None)
+                                     kw.get("rope_table", None), a["n_pos"], a["rope_dim"], a["lat_pos"],
+                                     kw.get("lat_codes", None), a["ld_lat_codes"], kw.get("lat_scales", None),
+                                     a["ld_lat_scales"], None)
 
     assert dp(D=520) == sk.SCKV_EINVAL                 # not a multiple of 16
     assert dp(Di=100) == sk.SCKV_EINVAL                # not a multiple of 32
@@ -164,6 +166,9 @@ def test_error_paths(L):
     assert dp(rope_table=fake, rope_dim=520) == sk.SCKV_EINVAL  # wider than the row
     assert dp(rope_table=fake, lat_pos=4000) == sk.SCKV_EINVAL  # position outside the table
     assert dp(rope_table=ctypes.c_void_p(0x1004)) == sk.SCKV_EINVAL  # table not 8-byte aligned
+    assert dp(lat_codes=fake, lat_scales=fake) == sk.SCKV_EINVAL      # packed and bf16 destinations at once
+    assert dp(lat_dst=None, lat_codes=fake) == sk.SCKV_EINVAL         # packed codes without scale bytes
+    assert dp(lat_dst=None, lat_codes=fake, lat_scales=fake, ld_lat_codes=200) == sk.SCKV_EINVAL  # short stride
 
     def rq(**kw):
         a = dict(ldx=512, ldy=512, rows=4, cols=512, n_pos=100, rope_dim=64, pos0=0, pos_step=4)

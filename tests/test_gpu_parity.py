@@ -260,10 +260,39 @@ def test_rope_quant_rows_bit_exact(sk, case):
         assert np.array_equal(got[:, cols:], x[:, cols:] if in_place else bits(bf16_of(np.full((rows, pad), 7.0))))
 
 
-@pytest.mark.parametrize("B,D,Di,win,start_pos,new,rope_dim", [
-    (3, 512, 128, 128, 32767, True, 64), (2, 64, 32, 16, 5, True, 8), (4, 512, 128, 128, 1000, False, 64),
-    (2, 256, 64, 8, 7, True, 0), (2, 512, 128, 128, 131071, True, 512)])
-def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new, rope_dim):
+@pytest.mark.parametrize("case", ROPE_CASES[:4] + ROPE_CASES[6:], ids=lambda c: "r{}c{}rd{}p{}s{}".format(
+    c[0], c[1], c[2], c[4], c[5]))
+def test_rope_quant_pack_bit_exact(sk, case):
+    """The packed latent writer: rotation, e4m3-scale round trip, 4-bit codes
+    and scale bytes, bit for bit the oracle's packing of its rotated round
+    trip."""
+    rows, cols, rd, n_pos, pos0, pos_step, pad, _, _ = case
+    rng = np.random.default_rng(rows * 11 + cols + rd)
+    ld = cols + pad
+    x = bits(bf16_of(rng.standard_normal((rows, ld)) * np.exp2(rng.integers(-6, 6, size=(rows, 1)))))
+    table = oracle.yarn_freqs_cis(rd, n_pos, 4096, 10000.0, 40.0, 32.0, 1.0)
+    pos = pos0 + np.arange(rows, dtype=np.int64) * pos_step
+    rt = oracle.latent_rope_quant(np.ascontiguousarray(x[:, :cols]), rd, table, pos)
+    wc, ws_ = oracle.pack(oracle.rope_rows(np.ascontiguousarray(x[:, :cols]), rd, table, pos).reshape(-1),
+                          oracle.E4M3_B16)
+    assert np.array_equal(oracle.unpack(wc, ws_, rows * cols, oracle.E4M3_B16), rt.reshape(-1))
+    codes = torch.full((rows, cols // 2 + 16), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows, cols // 16 + 16), 0xCD, dtype=torch.uint8, device="cuda")
+    say(f"rope quant pack {case}")
+    sk.sckv_rope_quant_pack(from_bits(x, "cuda"), ld, codes, cols // 2 + 16, scales, cols // 16 + 16, rows, cols,
+                            torch.from_numpy(table).cuda(), rd, pos0, pos_step)
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    assert np.array_equal(gc[:, :cols // 2], wc.reshape(rows, cols // 2))
+    assert np.array_equal(gs[:, :cols // 16], ws_.reshape(rows, cols // 16))
+    assert np.all(gc[:, cols // 2:] == 0xAB) and np.all(gs[:, cols // 16:] == 0xCD)
+
+
+@pytest.mark.parametrize("B,D,Di,win,start_pos,new,rope_dim,packed", [
+    (3, 512, 128, 128, 32767, True, 64, False), (2, 64, 32, 16, 5, True, 8, False),
+    (4, 512, 128, 128, 1000, False, 64, False), (2, 256, 64, 8, 7, True, 0, False),
+    (2, 512, 128, 128, 131071, True, 512, False), (3, 512, 128, 128, 32767, True, 64, True),
+    (2, 256, 64, 8, 7, True, 0, True)])
+def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new, rope_dim, packed):
     """The one-launch decode set-up against the oracle: the latent row's
     rotary turn (when a table is given) and E4M3_B16 round trip into the
     cache, the packed E8M0_B32 k row, the ring slot and the window columns;
@@ -285,16 +314,32 @@ def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new, rope_dim):
     lat_pos = max(0, start_pos - 3)  # the completed group's position
     table = oracle.yarn_freqs_cis(rope_dim, lat_pos + 1, 4096, 10000.0, 40.0, 32.0, 1.0) if rope_dim else None
     say(f"decode prepare B={B} D={D} Di={Di} win={win} start_pos={start_pos} new={new} rope_dim={rope_dim}")
-    sk.sckv_decode_prepare(from_bits(lat_new, "cuda") if new else None, D, lat_d[:, f] if new else None, n_c * D,
+    lc = rng.integers(0, 255, size=(B, n_c, D // 2)).astype(np.uint8)
+    ls = rng.integers(0, 255, size=(B, n_c, D // 16)).astype(np.uint8)
+    lc_d, ls_d = torch.from_numpy(lc).cuda(), torch.from_numpy(ls).cuda()
+    sk.sckv_decode_prepare(from_bits(lat_new, "cuda") if new else None, D,
+                           lat_d[:, f] if (new and not packed) else None, n_c * D,
                            from_bits(k_new, "cuda") if new else None, Di, codes_d[:, f] if new else None,
                            n_c * Di // 2, scales_d[:, f] if new else None, n_c * Di // 32, Di,
                            from_bits(kv_new, "cuda"), D, ring_d, win * D, B, D, win, start_pos, idx, ld_idx,
-                           torch.from_numpy(table).cuda() if rope_dim else None, rope_dim, lat_pos)
+                           torch.from_numpy(table).cuda() if rope_dim else None, rope_dim, lat_pos,
+                           lc_d[:, f] if (new and packed) else None, n_c * D // 2,
+                           ls_d[:, f] if (new and packed) else None, n_c * D // 16)
+    if packed:
+        want_lc, want_ls = lc.copy(), ls.copy()
+        if new:
+            for b in range(B):
+                r = (oracle.rope_rows(lat_new[b][None], rope_dim, table, [lat_pos])[0] if rope_dim else lat_new[b])
+                c, sc = oracle.pack(r, oracle.E4M3_B16)
+                want_lc[b, f], want_ls[b, f] = c, sc
+        assert np.array_equal(lc_d.cpu().numpy(), want_lc)
+        assert np.array_equal(ls_d.cpu().numpy(), want_ls)
     want_lat, want_codes, want_scales = latent.copy(), codes.copy(), scales.copy()
     if new:
         for b in range(B):
-            want_lat[b, f] = (oracle.latent_rope_quant(lat_new[b][None], rope_dim, table, [lat_pos])[0] if rope_dim
-                              else oracle.quant(lat_new[b], oracle.E4M3_B16))
+            if not packed:  # (with a packed destination the bf16 latent is untouched)
+                want_lat[b, f] = (oracle.latent_rope_quant(lat_new[b][None], rope_dim, table, [lat_pos])[0]
+                                  if rope_dim else oracle.quant(lat_new[b], oracle.E4M3_B16))
             c, sc = oracle.pack(k_new[b], oracle.E8M0_B32)
             want_codes[b, f], want_scales[b, f] = c, sc
     assert np.array_equal(bits(lat_d), want_lat)
@@ -751,6 +796,61 @@ def test_sparse_attn_long_list_one_workgroup(sk):
         assert ok, (b, worst)
 
 
+FP4_ATTN_CASES = [
+    # B, m, H, T, ra, rb, frac_invalid
+    (1, 1, 64, 640, 128, 8192, 0.05),     # split over workgroups (two-set kernel) + combine
+    (600, 1, 64, 640, 128, 600, 0.05),    # one-set column-split kernel
+    (520, 1, 64, 2176, 128, 4000, 0.1),   # one-set kernel, 68-chunk lists
+    (2, 3, 40, 100, 50, 300, 0.3),        # ragged T, padded head group
+    (300, 1, 16, 130, 20, 200, 0.1),      # 16 heads
+    (1, 2, 32, 2176, 128, 3000, 0.5),     # 32 heads, long split lists
+    (3, 2, 64, 64, 0, 500, 0.0),          # rows_b only
+]
+
+
+@pytest.mark.parametrize("case", FP4_ATTN_CASES, ids=lambda c: "B{}m{}H{}T{}".format(*c[:4]))
+def test_sparse_attn_packed_latent(sk, case):
+    """Attention over the packed latent rows (codes + e4m3 bytes, expanded on
+    chip) against the same call over the bf16 rows they stand for: bit for
+    bit; and against the oracle within the tolerance.  Index lists mix window
+    and latent rows inside chunks, with -1, out-of-range and duplicate
+    entries."""
+    B, m, H, T, ra, rb, frac = case
+    D = 512
+    rng = np.random.default_rng(B * 31 + T + rb)
+    q = bits(bf16_of(rng.standard_normal((B, m, H, D))))
+    A = bits(bf16_of(rng.standard_normal((B, max(ra, 1), D))))[:, :ra]
+    raw = bits(bf16_of(rng.standard_normal((B, rb, D)) * np.exp2(rng.integers(-4, 4, size=(B, rb, 1)))))
+    lat = oracle.quant(raw.reshape(-1), oracle.E4M3_B16).reshape(B, rb, D)
+    lc, ls = oracle.pack(raw.reshape(-1), oracle.E4M3_B16)
+    idx = rng.integers(0, ra + rb, size=(B, m, T)).astype(np.int32)
+    idx[rng.random((B, m, T)) < frac] = -1
+    idx[:, :, 1] = idx[:, :, 0]
+    if T > 40:
+        idx[:, :, 5] = ra + rb + 7  # out of range: skipped
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(D ** -0.5))
+    qd, Ad = from_bits(q, "cuda"), from_bits(A, "cuda") if ra else torch.zeros((B, 1, D), dtype=torch.bfloat16,
+                                                                                 device="cuda")
+    idd, skd = torch.from_numpy(idx).cuda(), torch.from_numpy(sink).cuda()
+    out_b = torch.empty((B, m, H, D), dtype=torch.bfloat16, device="cuda")
+    out_p = torch.full((B, m, H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    say(f"packed latent attention {case}")
+    sk.sckv_sparse_attn_sink(qd, Ad, ra, from_bits(lat, "cuda"), rb, idd, T, skd, scale, B, m, H, D, out_b)
+    sk.sckv_sparse_attn_sink_fp4(qd, Ad, ra, torch.from_numpy(lc.reshape(B, rb, D // 2)).cuda(),
+                                 torch.from_numpy(ls.reshape(B, rb, D // 16)).cuda(), rb, idd, T, skd, scale, B, m, H,
+                                 D, out_p)
+    torch.cuda.synchronize()
+    assert torch.equal(out_b.view(torch.int16), out_p.view(torch.int16)), case
+    got = vals(bits(out_p))
+    idx_ref = idx.copy()
+    idx_ref[idx_ref >= ra + rb] = -1
+    for b in sorted({0, B - 1}):
+        ref = oracle.sparse_attn(q[b], A[b] if ra else np.zeros((0, D), np.uint16), lat[b], idx_ref[b], sink, scale)
+        ok, worst = attn_tolerance_ok(got[b], ref)
+        assert ok, (b, worst)
+
+
 def test_sparse_attn_edge_rows(sk):
     """All -1 gives 0; out-of-range indices are skipped like -1."""
     B, m, H, D, ra, T = 1, 3, 64, 512, 40, 64
@@ -776,12 +876,14 @@ def test_sparse_attn_edge_rows(sk):
 
 # --------------------------------------------------------------------- the whole step per workload
 
-STEP_CASES = [(n, "bf16") for n in synth.WORKLOADS] + [
-    (n, "fp4") for n, w in synth.WORKLOADS.items() if w.Hi and w.Di in (128, 256)]
+STEP_CASES = [(n, "bf16", "bf16") for n in synth.WORKLOADS] + [
+    (n, "fp4", "bf16") for n, w in synth.WORKLOADS.items() if w.Hi and w.Di in (128, 256)] + [
+    (n, "fp4" if w.Hi else "bf16", "fp4") for n, w in synth.WORKLOADS.items() if w.D == 512]
 
 
-@pytest.mark.parametrize("name,B", [("decode", 2048), ("long_decode", 512)])
-def test_step_bench_launch_config_matches_oracle(sk, name, B):
+@pytest.mark.parametrize("name,B,latent", [("decode", 2048, "bf16"), ("long_decode", 512, "bf16"),
+                                           ("decode", 2048, "fp4"), ("long_decode", 512, "fp4")])
+def test_step_bench_launch_config_matches_oracle(sk, name, B, latent):
     """A whole decode step at the batch the bench times (packed k cache: the
     one-launch set-up, one score + top-K workgroup per query, one attention
     workgroup per query), inputs drawn on the device, checked against the
@@ -795,9 +897,9 @@ def test_step_bench_launch_config_matches_oracle(sk, name, B):
     # place on the caches and the ring)
     sampled = (0, 131, B - 1)
     xs = {b: {k: (v.cpu() if k == "sink" else v[b:b + 1].cpu()) for k, v in x.items()} for b in sampled}
-    st = PathState(w, x, B, kcache="fp4")
+    st = PathState(w, x, B, kcache="fp4", latent=latent)
     st.setup()
-    say(f"step {name} B={B}: running the HIP path")
+    say(f"step {name} B={B} ({latent} latent cache): running the HIP path")
     st.step()
     torch.cuda.synchronize()
     idx = st.idx.cpu().numpy()
@@ -858,8 +960,8 @@ def _oracle_step_cached(w, x, b):
     return _ORACLE_STEPS[key]
 
 
-@pytest.mark.parametrize("name,kcache", STEP_CASES, ids=lambda c: c if isinstance(c, str) else None)
-def test_step_matches_oracle(sk, name, kcache):
+@pytest.mark.parametrize("name,kcache,latent", STEP_CASES, ids=lambda c: c if isinstance(c, str) else None)
+def test_step_matches_oracle(sk, name, kcache, latent):
     """A whole step against the oracle: every query's index list bit for bit
     (prefill: all 4096 / 2048 of them), the attention outputs of every query
     for decode and of about 256 queries spread over the step for prefill."""
@@ -867,9 +969,9 @@ def test_step_matches_oracle(sk, name, kcache):
 
     w = synth.WORKLOADS[name]
     B = 2 if w.m == 1 else 1
-    say(f"step {name} ({kcache} k cache) B={B}: generating inputs")
+    say(f"step {name} ({kcache} k cache, {latent} latent cache) B={B}: generating inputs")
     x = synth.make_inputs(w, B)
-    st = PathState(w, x, B, kcache=kcache)
+    st = PathState(w, x, B, kcache=kcache, latent=latent)
     st.setup()
     say(f"step {name}: running the HIP path")
     st.step()
