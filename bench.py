@@ -74,6 +74,9 @@ def counts(w, B, call, kcache="bf16", latent="bf16"):
         return {"bytes": B * min(m, win) * D * 4, "flops": 0, "bound": "hbm"}
     if call == "window_idx":
         return {"bytes": B * m * win * 4, "flops": 0, "bound": "hbm"}
+    if call == "decode_step":  # a whole small-batch decode step in one launch
+        parts = [counts(w, B, c, kcache, latent) for c in ("decode_prepare", "index_scores_topk", "sparse_attn_sink")]
+        return {"bytes": sum(c["bytes"] for c in parts), "flops": sum(c["flops"] for c in parts), "bound": "hbm"}
     if call == "decode_prepare":  # the four set-up calls of a decode step in one launch
         return {"bytes": sum(counts(w, B, c, kcache, latent)["bytes"]
                              for c in ("quant_latent", "quant_index_k", "ring_write", "window_idx")),
@@ -135,6 +138,7 @@ CALL_KERNELS = {
     "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1>"],
     "ring_write": ["ring_write_kernel"],
     "decode_prepare": ["decode_prepare_kernel"],
+    "decode_step": ["decode_step_kernel"],
     "window_idx": ["window_idx_kernel"],
     "visible_idx": ["visible_idx_kernel"],
     "index_scores_topk": ["index_score_kernel", "topk_kernel"],
@@ -231,7 +235,7 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16", latent="bf16"):
               f"{'kernel':<44} {'calls':>5} {'avg_us':>9} {'read_MB':>9} {'write_MB':>9}"]
     # only the kernels of the step's own calls (set-up launches are left out)
     from sparse_compressed_kv_e2m1_amd.step import step_call_names  # noqa: PLC0415
-    names = step_call_names(w, kcache)
+    names = step_call_names(w, kcache, latent, B)
     mine = lambda k: any(k.startswith(p.replace(" ", "")) for c in names for p in CALL_KERNELS[c])  # noqa: E731
     dur = {k: v for k, v in dur.items() if mine(k)}
     for k in sorted(dur, key=lambda k: -dur[k]):
@@ -445,7 +449,8 @@ def roofline_of(cnt, ms, peaks=None, dtype=None):
     return r
 
 
-def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, latent="bf16"):
+def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, latent="bf16",
+            decode_launch="separate"):
     """Time whole steps of workload w over B sequences (inputs drawn on the
     device, resident before the timed region), then each library call with
     events around it on the same stream; optionally the B = 1 latency."""
@@ -456,7 +461,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
 
     log(f"bench: workload {w.name} B={B}: generating inputs on the device")
     x = synth.make_inputs(w, B, device="cuda")
-    st = PathState(w, x, B, kcache=kcache, latent=latent)
+    st = PathState(w, x, B, kcache=kcache, latent=latent, decode_launch=decode_launch)
     del x
     st.setup()
     calls = st.calls()
@@ -501,7 +506,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
     sing = None
     if single and B > 1:
         x1 = synth.make_inputs(w, 1, device="cuda")
-        s1 = PathState(w, x1, 1, kcache=kcache, latent=latent)
+        s1 = PathState(w, x1, 1, kcache=kcache, latent=latent, decode_launch=decode_launch)
         s1.setup()
         for _ in range(warmup):
             s1.step()
@@ -549,6 +554,9 @@ def main():
                     help="indexer k cache storage: packed fp4 codes + E8M0 bytes (default) or bf16 rows")
     ap.add_argument("--latent", choices=["fp4", "bf16"], default="bf16",
                     help="latent cache storage: packed fp4 codes + e4m3 bytes, or bf16 rows (the pages' layout)")
+    ap.add_argument("--decode-launch", choices=["separate", "one"], default="separate",
+                    help="decode steps: the separate calls (default), or the one cooperative launch "
+                         "sckv_decode_step for small batches")
     ap.add_argument("--legs", default="long_decode,causal_prefill,chunked_prefill",
                     help="other workloads timed in the same run and reported under 'legs' (comma list; '' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per thread count")
@@ -601,12 +609,12 @@ def main():
     w = synth.WORKLOADS[args.workload]
     B = args.instances or DEFAULT_B[args.workload]
     head = run_leg(w, B, args.kcache, args.steps, args.warmup, single=not args.no_single, graph=args.graph,
-                   peaks=peaks, latent=args.latent)
+                   peaks=peaks, latent=args.latent, decode_launch=args.decode_launch)
     legs = {}
     for name in [n for n in args.legs.split(",") if n and n != w.name]:
         lw = synth.WORKLOADS[name]
         legs[name] = run_leg(lw, DEFAULT_B[name], args.kcache, args.steps, args.warmup, single=False,
-                             graph=args.graph, peaks=peaks, latent=args.latent)
+                             graph=args.graph, peaks=peaks, latent=args.latent, decode_launch=args.decode_launch)
 
     line = {
         "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",

@@ -238,6 +238,54 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
                         int64_t ld_lat_codes, void* lat_scales, int64_t ld_lat_scales, void* stream);
 
 /*
+ * sckv_decode_step -- a whole decode step (m = 1 at start_pos > 0) of B <= 64
+ * sequences in ONE launch (forward.rs AttnV41::forward: ring copy, window
+ * list, indexer, merge, attend_and_project; compress.rs: the round trips, the
+ * rotation, attention_any).  The results are bit for bit those of
+ *   sckv_decode_prepare(lat_new, D, latent row n_c-1, n_c*D, k_new, Di, k_codes
+ *       row n_c-1, n_c*Di/2, k_scales row n_c-1, n_c*Di/32, Di, kv_new, D, ring,
+ *       win*D, B, D, win, start_pos, idx, win+K, rope_table, n_pos, rope_dim,
+ *       (n_c-1)*ratio, NULL, 0, NULL, 0)
+ *   sckv_index_scores_topk_fp4(iq, k_codes, k_scales, w, B, 1, Hi, Di, n_c,
+ *       ratio, start_pos, K, win, idx, win+K, win, NULL, ...)
+ *   sckv_sparse_attn_sink(q, ring, win, latent, n_c, idx, win+K, sink, scale,
+ *       B, 1, H, D, out, ...)
+ * run as phases of one cooperative launch with grid-wide barriers between
+ * them (the keys, index lists and split partials pass through ws).  For
+ * callers that need a step as a single launch: on MI355X each grid barrier
+ * (device-scope atomics across the eight XCDs' L2s) costs a few microseconds,
+ * more than the launch gaps of the separate calls, so those are faster at
+ * every batch size measured (B = 1: 73 against 40 us at n_c = 8192).
+ *   lat_new, k_new  [B] new raw latent rows (D bf16) and raw indexer k rows (Di
+ *                   bf16), contiguous, or both NULL when no compressed row
+ *                   completes at this step (else (start_pos+1) % ratio == 0 and
+ *                   n_c == (start_pos+1)/ratio: they become row n_c - 1)
+ *   kv_new          [B, D] the new kv rows (ring slot start_pos mod win)
+ *   rope_table      [n_pos, rope_dim/2, 2] f32 rotation table or NULL
+ *   latent          [B, n_c, D] bf16 latent cache; k_codes [B, n_c, Di/2],
+ *                   k_scales [B, n_c, Di/32] the packed indexer k cache;
+ *                   ring [B, win, D]
+ *   iq [B, Hi, Di] raw indexer q; w [B, Hi] f32; q [B, H, D]; sink [H] f32
+ *   idx [B, win+K] int32 (written); out [B, H, D] bf16 (written)
+ *   ws   at least sckv_decode_step_workspace_bytes(B, H, D, n_c, win+K); its
+ *        first 256 bytes hold the launch's barrier counters: they must be
+ *        zero before the first call that uses the workspace (allocate it
+ *        zeroed), and every completed call leaves them zero.  Calls that
+ *        share a workspace must not overlap (one stream).
+ * Supported: Hi = 64, Di = 128, D = 512, 33 <= H <= 64, B <= 64, n_c <= 32768
+ * with every compressed row visible at start_pos, win + K <= 4096, a device
+ * with cooperative launch (else SCKV_EUNSUPPORTED); 16-byte aligned rows.
+ */
+int sckv_decode_step(const void* lat_new, const void* k_new, const void* kv_new, const float* rope_table,
+                     int64_t n_pos, int rope_dim, void* latent, void* k_codes, void* k_scales, void* ring,
+                     const void* iq, const float* w, int Hi, int Di, int ratio, int K, const void* q,
+                     const float* sink, float scale, int H, int B, int64_t n_c, int D, int win, int64_t start_pos,
+                     int32_t* idx, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of sckv_decode_step ((size_t)-1 for invalid arguments). */
+size_t sckv_decode_step_workspace_bytes(int B, int H, int D, int64_t n_c, int T);
+
+/*
  * sckv_visible_idx -- the compressed part of every query's index list when
  * every causally visible compressed row is attended (a layer without an
  * indexer): offset + j for j < V_p, then -1 up to K, where compressed row j is

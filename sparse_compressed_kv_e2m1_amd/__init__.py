@@ -22,6 +22,8 @@ from ._binding import (  # noqa: F401
     lib,
     sckv_abi_version,
     sckv_decode_prepare,
+    sckv_decode_step,
+    sckv_decode_step_workspace_bytes,
     sckv_index_scores_topk,
     sckv_index_scores_topk_fp4,
     sckv_last_error,

@@ -60,6 +60,10 @@ def _load():
                                              vp, i64, i64, vp, vp, sz, vp]
     L.sckv_sparse_attn_sink.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32, vp,
                                         vp, sz, vp]
+    L.sckv_decode_step.argtypes = [vp, vp, vp, vp, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, vp,
+                                   ctypes.c_float, i32, i32, i64, i32, i32, i64, vp, vp, vp, sz, vp]
+    L.sckv_decode_step_workspace_bytes.argtypes = [i32, i32, i32, i64, i32]
+    L.sckv_decode_step_workspace_bytes.restype = sz
     L.sckv_sparse_attn_sink_fp4.argtypes = [vp, vp, i64, vp, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32, i32,
                                             vp, vp, sz, vp]
     L.sckv_sparse_attn_sink_noalloc.argtypes = [vp, vp, i64, vp, i64, vp, i32, vp, ctypes.c_float, i32, i64, i32,
@@ -303,3 +307,27 @@ def sckv_sparse_attn_sink_fp4(q: torch.Tensor, rows_a: torch.Tensor, ra: int, ro
         _ptr(rows_b_codes, torch.uint8, "rows_b_codes"), _ptr(rows_b_scales, torch.uint8, "rows_b_scales"), rb,
         _ptr(idx, torch.int32, "idx"), T, _ptr(sink, torch.float32, "sink"), float(scale), B, m, H, D,
         _ptr(out, torch.bfloat16, "out"), _ptr(ws, None, "ws"), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def sckv_decode_step_workspace_bytes(B: int, H: int, D: int, n_c: int, T: int) -> int:
+    return int(lib.sckv_decode_step_workspace_bytes(B, H, D, n_c, T))
+
+
+def sckv_decode_step(lat_new, k_new, kv_new: torch.Tensor, rope_table: torch.Tensor | None, rope_dim: int,
+                     latent: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, ring: torch.Tensor,
+                     iq: torch.Tensor, w: torch.Tensor, Hi: int, Di: int, ratio: int, K: int, q: torch.Tensor,
+                     sink: torch.Tensor, scale: float, H: int, B: int, n_c: int, D: int, win: int, start_pos: int,
+                     idx: torch.Tensor, out: torch.Tensor, ws: torch.Tensor | None = None, stream=None):
+    """All tensors contiguous device tensors (lat_new / k_new / rope_table may be None)."""
+    if ws is None:
+        nb = sckv_decode_step_workspace_bytes(B, H, D, n_c, win + K)
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=out.device)  # barrier words start at zero
+    _check("sckv_decode_step", lib.sckv_decode_step(
+        _ptr(lat_new, torch.bfloat16, "lat_new"), _ptr(k_new, torch.bfloat16, "k_new"),
+        _ptr(kv_new, torch.bfloat16, "kv_new"), _ptr(rope_table, torch.float32, "rope_table"),
+        0 if rope_table is None else rope_table.shape[0], rope_dim, _ptr(latent, torch.bfloat16, "latent"),
+        _ptr(k_codes, torch.uint8, "k_codes"), _ptr(k_scales, torch.uint8, "k_scales"),
+        _ptr(ring, torch.bfloat16, "ring"), _ptr(iq, torch.bfloat16, "iq"), _ptr(w, torch.float32, "w"), Hi, Di,
+        ratio, K, _ptr(q, torch.bfloat16, "q"), _ptr(sink, torch.float32, "sink"), float(scale), H, B, n_c, D, win,
+        start_pos, _ptr(idx, torch.int32, "idx"), _ptr(out, torch.bfloat16, "out"), _ptr(ws, None, "ws"),
+        ws.numel() * ws.element_size(), _stream(stream)))

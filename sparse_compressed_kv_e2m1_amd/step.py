@@ -38,9 +38,18 @@ def uses_decode_prepare(w, kcache: str) -> bool:
     return w.start_pos > 0 and w.m == 1 and bool(w.Hi) and kcache == "fp4" and w.n_c - w.first_new_row <= 1
 
 
-def step_call_names(w, kcache: str) -> list:
+def uses_decode_step(w, kcache: str, latent: str = "bf16", B: int = 1) -> bool:
+    """A decode step of at most 64 sequences in the shapes sckv_decode_step is
+    built for (it runs as that one launch when asked for)."""
+    return (uses_decode_prepare(w, kcache) and latent == "bf16" and w.Hi == 64 and w.Di == 128 and w.D == 512
+            and 33 <= w.H <= 64 and B <= 64 and w.n_c <= 32768 and w.T <= 4096)
+
+
+def step_call_names(w, kcache: str, latent: str = "bf16", B: int = 1, decode_launch: str = "separate") -> list:
     """Names of a step's library calls, in order (the names PathState.calls
     gives them)."""
+    if decode_launch == "one" and uses_decode_step(w, kcache, latent, B):
+        return ["decode_step"]
     if uses_decode_prepare(w, kcache):
         names = ["decode_prepare"]
     else:
@@ -58,19 +67,27 @@ class PathState:
     raw CPU inputs (see sckv_synth.make_inputs).  setup() round-trips the cache
     rows that existed before this step; step() runs the hot path."""
 
-    def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16", latent: str = "bf16"):
+    def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16", latent: str = "bf16",
+                 decode_launch: str = "separate"):
         """kcache: "bf16" keeps the indexer k cache as round-tripped bf16 rows
         (the pages' layout); "fp4" keeps it packed (4-bit codes + one E8M0 byte
         per 32 values) and scores it on the scaled fp4 matrix cores.
         latent: "bf16" keeps the latent cache as round-tripped bf16 rows (the
         pages' layout); "fp4" keeps it packed (4-bit codes + one e4m3 byte per
         16 values, 288 bytes a 512-wide row) and the attention expands the
-        rows it gathers on chip (D = 512)."""
+        rows it gathers on chip (D = 512).
+        decode_launch: "separate" (default) runs a decode step as its separate
+        calls; "one" runs a small-batch decode step as the one cooperative
+        launch sckv_decode_step when its shapes allow (the same results; on
+        MI355X its grid barriers cost more than the launch gaps they remove)."""
         if kcache not in ("bf16", "fp4"):
             raise ValueError(kcache)
         if latent not in ("bf16", "fp4") or (latent == "fp4" and w.D != 512):
             raise ValueError(f"latent={latent} (packed latent rows need D = 512)")
+        if decode_launch not in ("one", "separate"):
+            raise ValueError(decode_launch)
         self.w, self.B, self.device, self.kcache, self.latent_fmt = w, B, device, kcache, latent
+        self.decode_launch = decode_launch
         dev = lambda t: t.to(device).contiguous()  # noqa: E731
         self.q = dev(inputs["q"])
         self.sink = dev(inputs["sink"])
@@ -194,6 +211,18 @@ class PathState:
         """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
         m, win, D = w.m, w.win, w.D
+        if self.decode_launch == "one" and uses_decode_step(w, self.kcache, self.latent_fmt, B):
+            # the whole decode step in one launch (the same results as the calls below)
+            new = self.n_new == 1
+            if not hasattr(self, "ws_step"):
+                nb = sk.sckv_decode_step_workspace_bytes(B, w.H, D, w.n_c, self.T)
+                # zeroed: its first 256 bytes are the launch's barrier words
+                self.ws_step = torch.zeros(max(nb, 256), dtype=torch.uint8, device=self.device)
+            return [("decode_step", lambda: sk.sckv_decode_step(
+                self.latent_new if new else None, self.ik_new if new else None, self.kv_new, self.rope_table,
+                w.rope_dim, self.latent, self.ik_codes, self.ik_scales, self.ring, self.iq, self.iw, w.Hi, w.Di,
+                w.ratio, w.K, self.q, self.sink, w.scale, w.H, B, w.n_c, D, win, w.start_pos, self.idx, self.out,
+                ws=self.ws_step))]
         if uses_decode_prepare(w, self.kcache):
             # decode: the latent and k rows, the ring slot and the window
             # columns in one launch (the same results as the four calls below)
@@ -270,7 +299,8 @@ class PathState:
         """One pass of the hot path (steps 1-6 of the module doc)."""
         if not hasattr(self, "_calls"):
             self._calls = self.calls()
-            assert [n for n, _ in self._calls] == step_call_names(self.w, self.kcache)
+            assert [n for n, _ in self._calls] == step_call_names(self.w, self.kcache, self.latent_fmt, self.B,
+                                                                 self.decode_launch)
         for _, f in self._calls:
             f()
         return self.out

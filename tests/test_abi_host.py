@@ -21,7 +21,8 @@ def test_header_declares_the_calls():
     for n in ["sckv_quant", "sckv_quant_rows", "sckv_ring_write", "sckv_rows_a_len", "sckv_window_idx",
               "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
               "sckv_last_error", "sckv_abi_version", "sckv_quant_pack", "sckv_index_scores_topk_fp4",
-              "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows", "sckv_rope_quant_pack"]:
+              "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows", "sckv_rope_quant_pack",
+              "sckv_decode_step", "sckv_sparse_attn_sink_fp4"]:
         assert n in names
 
 
@@ -238,3 +239,32 @@ def test_rotation_table_matches_oracle():
                 (64, 4, 4096, 1e4, 0.0, 32.0, 1.0)):
         with pytest.raises(sk.SckvError):
             sk.sckv_yarn_freqs_cis(*bad)
+
+
+def test_decode_step_host_checks(L):
+    """sckv_decode_step refuses what it is not built for before enqueuing
+    anything (fake pointers are never dereferenced)."""
+    import sparse_compressed_kv_e2m1_amd as sk
+
+    f = ctypes.c_void_p(0x10000)
+
+    def ds(**kw):
+        a = dict(lat_new=f, k_new=f, n_pos=40000, rope_dim=64, Hi=64, Di=128, ratio=4, K=512, H=64, B=2, n_c=8192,
+                 D=512, win=128, start_pos=32767, ws_bytes=1 << 40)
+        a.update(kw)
+        return L.sckv_decode_step(a["lat_new"], a["k_new"], f, f, a["n_pos"], a["rope_dim"], f, f, f, f, f, f,
+                                  a["Hi"], a["Di"], a["ratio"], a["K"], f, f, ctypes.c_float(0.05), a["H"], a["B"],
+                                  a["n_c"], a["D"], a["win"], a["start_pos"], f, f, f, ctypes.c_size_t(a["ws_bytes"]),
+                                  None)
+
+    assert ds(B=65) == sk.SCKV_EUNSUPPORTED        # more than 64 sequences
+    assert ds(H=16) == sk.SCKV_EUNSUPPORTED        # head groups the step is not built for
+    assert ds(Hi=32) == sk.SCKV_EUNSUPPORTED
+    assert ds(n_c=40000, start_pos=159999) == sk.SCKV_EUNSUPPORTED
+    assert ds(K=5000) == sk.SCKV_EUNSUPPORTED      # win + K above 4096
+    assert ds(k_new=None) == sk.SCKV_EINVAL        # one new row without the other
+    assert ds(start_pos=32768, n_c=8192) == sk.SCKV_EINVAL  # no row completes at this step
+    assert ds(n_c=8193) == sk.SCKV_EINVAL          # rows not yet visible
+    assert ds(ws_bytes=100) == sk.SCKV_EWORKSPACE
+    assert ds(B=0) == sk.SCKV_OK
+    assert sk.sckv_decode_step_workspace_bytes(1, 64, 512, 8192, 640) >= 8192 * 2

@@ -946,6 +946,51 @@ def test_step_graph_replays_match_eager(sk, name, B):
     torch.cuda.empty_cache()
 
 
+DSTEP_CASES = [("decode", 1, True), ("decode", 3, True), ("decode", 13, True), ("decode", 64, True),
+               ("long_decode", 2, True), ("decode", 2, False), ("long_decode", 1, False)]
+
+
+@pytest.mark.parametrize("name,B,new", DSTEP_CASES, ids=lambda c: str(c))
+def test_decode_step_one_launch_matches_separate_calls(sk, name, B, new):
+    """sckv_decode_step (set-up, scores, top-K, attention, combine as phases
+    of one cooperative launch) against the separate calls on the same inputs:
+    index lists, outputs, ring, latent and packed k caches bit for bit, on two
+    launches in a row; sequence 0 against the oracle.  new=False: a step that
+    completes no compressed row."""
+    from sparse_compressed_kv_e2m1_amd.step import PathState, step_call_names
+
+    w = synth.WORKLOADS[name]
+    if not new:
+        w = w.with_(start_pos=w.start_pos - 1, n_c=w.start_pos // w.ratio)
+    assert step_call_names(w, "fp4", "bf16", B, "one") == ["decode_step"]
+    x = synth.make_inputs(w, B)
+    say(f"decode step in one launch: {name} B={B} new={new}")
+    states = {}
+    for mode in ("separate", "one"):
+        st = PathState(w, x, B, kcache="fp4", decode_launch=mode)
+        st.setup()
+        st.step()
+        states[mode] = st
+    torch.cuda.synchronize()
+    sep, one = states["separate"], states["one"]
+    for rep in range(2):
+        assert torch.equal(one.idx, sep.idx), (rep, "index lists")
+        assert torch.equal(one.out.view(torch.int16), sep.out.view(torch.int16)), (rep, "outputs")
+        assert torch.equal(one.ring.view(torch.int16), sep.ring.view(torch.int16)), (rep, "ring")
+        assert torch.equal(one.latent.view(torch.int16), sep.latent.view(torch.int16)), (rep, "latent cache")
+        assert torch.equal(one.ik_codes, sep.ik_codes) and torch.equal(one.ik_scales, sep.ik_scales), (rep, "k cache")
+        one.idx.fill_(-5)
+        one.out.zero_()
+        one.step()  # the step is idempotent: it rewrites the same slot and rows
+        torch.cuda.synchronize()
+    if B <= 3:
+        ref_idx, ref_out = oracle_step(w, {k: (v if k == "sink" else v[:1]) for k, v in x.items()}, 0)
+        assert np.array_equal(one.idx[0].cpu().numpy(), ref_idx)
+        ok, worst = attn_tolerance_ok(vals(bits(one.out[0])), ref_out)
+        assert ok, worst
+    del states, sep, one
+
+
 _ORACLE_STEPS = {}
 
 
