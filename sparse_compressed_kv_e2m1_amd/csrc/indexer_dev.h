@@ -167,10 +167,13 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t k, uint32_t
 // bytes (hist[0..256), built while the keys were produced): the K-th largest
 // key tau is the high-byte bin found there plus the low-byte bin found in a
 // second histogram (hist[256..512), zero on entry) over the keys of that bin
-// only; then the same ordered compaction.
+// only; then the same ordered compaction.  With `stage` (K free words of LDS)
+// the selected rows gather there first and leave with coalesced stores
+// instead of one scattered store per selected key.
 template <int KPT, int NWAVES>
 __device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int64_t s0, int K, int32_t offset,
-                                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* tot) {
+                                                 int32_t* __restrict__ out, uint32_t* hist, uint32_t* tot,
+                                                 int32_t* stage = nullptr) {
     uint32_t hi_bin, above_hi;
     find_bin(hist, (uint32_t)K, hi_bin, above_hi);
 #pragma unroll
@@ -192,6 +195,7 @@ __device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int
     take_eq = take_eq < eq ? take_eq : eq;
     uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
     uint32_t eq_seen = 0;
+    int32_t* dst = stage ? stage : out;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         const uint32_t k = key[j];
@@ -200,7 +204,11 @@ __device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int
             take = eq_seen < take_eq;
             ++eq_seen;
         }
-        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s0 + j);
+        if (take && pos < (uint32_t)K) dst[pos++] = (int32_t)(offset + s0 + j);
+    }
+    if (stage) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < K; i += NWAVES * 64) out[i] = stage[i];
     }
 }
 
@@ -319,23 +327,26 @@ __device__ __forceinline__ void index_score_body(
     int64_t row_end = row0 + rows_per_wg;
     row_end = row_end < vis ? row_end : vis;
 
-    // ---- this wave's rows: a contiguous run, streamed in 32-row tiles through
-    // a wave-private ring.  Lane i of copy j brings 16 bytes to tile byte
+    // ---- the workgroup's rows [row0, row_end) in 32-row tiles, each streamed
+    // through the ring of the wave that takes it.  The waves take tiles in the
+    // order they ask for them: wave w's first QD are w, w + NW, ...; after
+    // that each request claims the next unclaimed tile from an LDS counter, so
+    // that all waves run out of tiles together, however unevenly the memory
+    // system serves them.  Lane i of copy j brings 16 bytes to tile byte
     // j*1024 + 16 i; which 16-byte chunk of which row lands there is swizzled
     // so that the B-operand reads below (32 rows at one chunk) spread over all
     // banks.  FP4: the tile's scale bytes follow its codes.
     const int64_t nrows = row_end - row0;
-    const int64_t per_wave = (((nrows + S::NW - 1) / S::NW) + 31) / 32 * 32;
-    const int64_t w0 = row0 + (int64_t)wave * per_wave;
-    int64_t w1 = w0 + per_wave;
-    w1 = w1 < row_end ? w1 : row_end;
-    const int ntiles = (w0 < w1) ? (int)((w1 - w0 + 31) / 32) : 0;
+    const int ntiles_all = (int)((nrows + 31) / 32);
+    constexpr int QD = S::PD > 0 ? S::PD : 1;  // tiles a wave has asked for and not yet used
+    __shared__ uint32_t tile_ctr;
     const unsigned char* kb = reinterpret_cast<const unsigned char*>(k) + b * n_c * S::ROWB;
     const uint8_t* ksb = FP4 ? k_scales + b * n_c * S::SB : nullptr;
     const uint32_t ring = lds0 + (uint32_t)(wave * S::NST * S::TILE);
-    auto issue = [&](int tile) {
-        const int64_t s0 = w0 + (int64_t)tile * 32;
-        const uint32_t st = ring + (uint32_t)((tile % S::NST) * S::TILE);
+    // the wave's seq-th tile (ring stage seq % NST) is tile t
+    auto issue = [&](int seq, int t) {
+        const int64_t s0 = row0 + (int64_t)t * 32;
+        const uint32_t st = ring + (uint32_t)((seq % S::NST) * S::TILE);
 #pragma unroll
         for (int j = 0; j < S::CT / 1024; ++j) {
             const int slot = j * 64 + lane;  // 16-byte slot of the tile
@@ -369,16 +380,20 @@ __device__ __forceinline__ void index_score_body(
     for (int j = wave; j * 1024 < qbytes; j += S::NW)
         if (j * 1024 + lane * 16 < qbytes) dma16_s(qrow, (uint32_t)(j * 1024 + lane * 16), qdst + j * 1024);
     if (wave == 0 && lane < Hi) dma4_s(w + qi * (int64_t)Hi, (uint32_t)lane * 4u, lds0 + S::OFF_W);
+    int tq[QD];  // this wave's tiles in request order (>= ntiles_all: none left)
+#pragma unroll
+    for (int i = 0; i < QD; ++i) tq[i] = wave + i * S::NW;
+    if (threadIdx.x == 0) tile_ctr = (uint32_t)(S::NW * QD);  // read only after the barrier below
 #pragma unroll
     for (int i = 0; i < S::PD; ++i)
-        if (i < ntiles) issue(i);
+        if (tq[i] < ntiles_all) issue(i, tq[i]);
     // fused top-K: the high-byte histogram of the keys fills while they are
     // produced (hist[0..256)); hist[256..512) serves the second pass
     __shared__ uint32_t hist[KPT > 0 ? 512 : 1];
     if (KPT > 0)
         for (int i = threadIdx.x; i < 512; i += S::NW * 64) hist[i] = 0u;
     // q and w landed (only the tile copies may still be in flight), in every wave
-    if (ntiles >= S::PD)
+    if (S::PD == 0 || tq[S::PD > 0 ? S::PD - 1 : 0] < ntiles_all)
         wait_vmcnt<S::PD * S::NINST>();
     else
         wait_vmcnt<0>();
@@ -500,13 +515,26 @@ __device__ __forceinline__ void index_score_body(
         }
     __syncthreads();  // every wave holds q_hat and w before keys overwrite them
 
-    for (int tile = 0; tile < ntiles; ++tile) {
-        if (S::PD == 0) issue(tile);
-        // tiles tile+1 .. tile+PD-1 may still be in flight; tile itself must be done
-        const int ahead = (ntiles - 1 - tile) < (S::PD - 1) ? (ntiles - 1 - tile) : (S::PD - 1);
+    for (int seq = 0; tq[0] < ntiles_all; ++seq) {
+        const int tile = tq[0];
+        if (S::PD == 0) issue(seq, tile);
+        // the tiles asked for after this one may still be in flight; this one must be done
+        int ahead = 0;
+#pragma unroll
+        for (int i = 1; i < QD; ++i) ahead += tq[i] < ntiles_all ? 1 : 0;
         wait_tiles<S::NINST, (S::PD > 1 ? S::PD : 1)>(ahead);
-        if (S::PD > 0 && tile + S::PD < ntiles) issue(tile + S::PD);  // into the stage tile-1 used
-        const unsigned char* stp = lds + (wave * S::NST + tile % S::NST) * S::TILE;
+        // the next tile (none once a claim has run past the end)
+        int tn = ntiles_all;
+        if (tq[QD - 1] < ntiles_all) {
+            uint32_t v = 0;
+            if (lane == 0) v = atomicAdd(&tile_ctr, 1u);
+            tn = __builtin_amdgcn_readfirstlane((int)v);
+        }
+        if (S::PD > 0 && tn < ntiles_all) issue(seq + S::PD, tn);  // into the stage the last tile used
+#pragma unroll
+        for (int i = 0; i < QD - 1; ++i) tq[i] = tq[i + 1];
+        tq[QD - 1] = tn;
+        const unsigned char* stp = lds + (wave * S::NST + seq % S::NST) * S::TILE;
         const int r = lane & 31;
         f32x16 acc[MT];
 #pragma unroll
@@ -569,8 +597,8 @@ __device__ __forceinline__ void index_score_body(
             v[1] = v[1] + v[3];
         }
         if (Hi > 1) v[0] = v[0] + v[1];
-        const int64_t s = w0 + (int64_t)tile * 32 + r;
-        if (lane < 32 && s < w1) {
+        const int64_t s = row0 + (int64_t)tile * 32 + r;
+        if (lane < 32 && s < row_end) {
             const uint32_t bits = f32_to_bf16_bits(v[0]);
             const uint32_t key = score_key(bits);
             keys_l[s - row0] = (uint16_t)key;
@@ -605,7 +633,9 @@ __device__ __forceinline__ void index_score_body(
         }
 #pragma unroll
         for (int j = 0; j < KP; ++j) key[j] = (s0 + j < nrows) ? key[j] : 0u;
-        topk_select_hist<KP, S::NW>(key, s0, K, offset, idx + qi * ld + col0, hist, tot);
+        // the rings are idle now: they stage the selected rows when K fits
+        int32_t* stage = (size_t)K * 4 <= (size_t)S::NW * S::NST * S::TILE ? reinterpret_cast<int32_t*>(lds) : nullptr;
+        topk_select_hist<KP, S::NW>(key, s0, K, offset, idx + qi * ld + col0, hist, tot, stage);
     }
 }
 

@@ -499,6 +499,10 @@ FP4_CASES = [
     (192, 1, 32, 256, 1500, 1, 1499, 100, False),   # fused, head dim 256
     (1, 256, 8, 128, 64, 1, 0, 16, False),          # fused, queries that see <= K rows
     (192, 1, 64, 128, 32768, 4, 131071, 2048, False),  # fused, long decode shape (64 keys a thread)
+    # fused, 64 keys a thread: visible counts 19997 and 19998 end inside a
+    # 16-byte group of keys; n_c not a multiple of 8
+    (200, 2, 64, 128, 20000, 4, 79990, 1500, False),
+    (192, 1, 64, 128, 20004, 1, 20003, 700, False),
 ]
 
 
@@ -639,9 +643,11 @@ def test_index_fp4_q_packing_exhaustive(sk):
                                                       for i, j in bad[:6]])
 
 
-def test_index_topk_fp4_ties(sk):
-    """Forced ties at the K-th place through the fp4 path (fused and split)."""
-    n_c, Di, Hi, K = 500, 128, 4, 64
+@pytest.mark.parametrize("n_c,K", [(500, 64), (17000, 900)])
+def test_index_topk_fp4_ties(sk, n_c, K):
+    """Forced ties at the K-th place through the fp4 path (fused and split;
+    n_c = 17000: 64 keys a thread in the fused path)."""
+    Di, Hi = 128, 4
     rng = np.random.default_rng(97)
     base = bits(bf16_of(rng.standard_normal((8, Di))))
     kraw = base[rng.integers(0, 8, size=n_c)]
