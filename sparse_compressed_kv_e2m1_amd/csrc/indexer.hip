@@ -25,19 +25,48 @@
 // sum follows the fixed pairwise order (stride Hi/2 first): in the D tile
 // layout strides 32, 16, 8, 2 and 1 stay inside a lane and stride 4 is the
 // lane^32 exchange.  Ordered 16-bit keys collect in LDS and leave with
-// coalesced stores.
+// coalesced stores.  Waves take tiles as they ask for them (an LDS counter),
+// so they finish together.  Short fused lists (at most 2048 rows, fp4 k) run
+// in a persistent grid of 4-wave workgroups, four to a compute unit.
 #include "indexer_dev.h"
 
 namespace sckv {
 namespace {
 
-template <int MT, int DI, int KPT, bool FP4>
-__global__ __launch_bounds__(score_waves(FP4) * 64) void index_score_kernel(
+// NWV > 0: workgroups of NWV waves instead of score_waves(FP4), held to the
+// registers of four waves a SIMD (four such workgroups a compute unit)
+template <int MT, int DI, int KPT, bool FP4, int NWV = 0>
+__global__ __launch_bounds__((NWV > 0 ? NWV : score_waves(FP4)) * 64)
+__attribute__((amdgpu_waves_per_eu(NWV > 0 ? 4 : 1))) void index_score_kernel(
     const void* __restrict__ q, const void* __restrict__ k,
     const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
     int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
-    int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0) {
-    index_score_body<MT, DI, KPT, FP4>(q, k, k_scales, w, m, Hi, n_c, ratio, start_pos, rows_per_wg, nsplit, keys, scores, K, offset, idx, ld, col0, blockIdx.x);
+    int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0, uint32_t nwork) {
+    if constexpr (NWV > 0) {
+        // a persistent grid: workgroup g takes work items g, g + gridDim.x, ...
+        // (starting a workgroup costs more than a short query's scores)
+        for (uint32_t vb = blockIdx.x; vb < nwork; vb += gridDim.x) {
+            index_score_body<MT, DI, KPT, FP4, NWV>(q, k, k_scales, w, m, Hi, n_c, ratio, start_pos, rows_per_wg,
+                                                    nsplit, keys, scores, K, offset, idx, ld, col0, vb);
+            __syncthreads();  // the next item reuses the LDS
+        }
+    } else {
+        index_score_body<MT, DI, KPT, FP4, NWV>(q, k, k_scales, w, m, Hi, n_c, ratio, start_pos, rows_per_wg, nsplit,
+                                                keys, scores, K, offset, idx, ld, col0, blockIdx.x);
+    }
+}
+
+// Compute units of the current device (cached per device; 0 if unknown).
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 template <int KPT>
@@ -70,9 +99,9 @@ void launch_topk(const uint16_t* keys, int64_t nq, int64_t n_c, int64_t m, int r
 }
 
 // LDS bytes of a score launch (KPT as in index_score_kernel).
-template <int MT, int DI, int KPT, bool FP4>
+template <int MT, int DI, int KPT, bool FP4, int NWV = 0>
 size_t score_lds_bytes(int rows_per_wg, bool with_scores) {
-    using Sh = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4), FP4>;
+    using Sh = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4, NWV), FP4, NWV>;
     return Sh::lds_bytes(rows_per_wg, with_scores);
 }
 
@@ -96,19 +125,26 @@ struct IndexArgs {
     hipStream_t s;
 };
 
-template <int MT, int DI, int KPT, bool FP4>
+template <int MT, int DI, int KPT, bool FP4, int NWV = 0>
 int launch_scores(const IndexArgs& a, int rows_per_wg, int nsplit, uint16_t* keys) {
-    const size_t lds = score_lds_bytes<MT, DI, KPT, FP4>(rows_per_wg, a.scores != nullptr);
+    const size_t lds = score_lds_bytes<MT, DI, KPT, FP4, NWV>(rows_per_wg, a.scores != nullptr);
     if (lds + SCORE_STATIC_LDS > 160 * 1024)
         return fail(SCKV_EUNSUPPORTED, "sckv_index_scores_topk: score tile does not fit in LDS");
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI, KPT, FP4>,
+        hipError_t e = hipFuncSetAttribute((const void*)index_score_kernel<MT, DI, KPT, FP4, NWV>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_index_scores_topk: ") + hipGetErrorString(e));
     }
-    index_score_kernel<MT, DI, KPT, FP4><<<dim3((unsigned)(a.nq * nsplit)), dim3(score_waves(FP4) * 64), lds, a.s>>>(
+    constexpr int nw = NWV > 0 ? NWV : score_waves(FP4);
+    const int64_t nwork = a.nq * nsplit;
+    int64_t grid = nwork;
+    if (NWV > 0) {  // persistent: four workgroups a compute unit
+        const int64_t slots = 4 * (int64_t)device_cus();
+        if (slots > 0 && grid > slots) grid = slots;
+    }
+    index_score_kernel<MT, DI, KPT, FP4, NWV><<<dim3((unsigned)grid), dim3(nw * 64), lds, a.s>>>(
         a.q, a.k, a.k_scales, a.w, a.m, a.Hi, a.n_c, a.ratio, a.start_pos, rows_per_wg, nsplit, keys,
-        a.scores, a.K, a.offset, a.idx, a.ld, a.col0);
+        a.scores, a.K, a.offset, a.idx, a.ld, a.col0, (uint32_t)nwork);
     return SCKV_OK;
 }
 
@@ -122,6 +158,13 @@ int launch_fused(const IndexArgs& a) {
 #define SCKV_FUSED(KPT)                                                                           \
     (score_lds_bytes<MT, DI, KPT, FP4>(rows, false) + SCORE_STATIC_LDS > 160 * 1024 ? SCKV_EUNSUPPORTED \
                                                                   : launch_scores<MT, DI, KPT, FP4>(a, rows, 1, nullptr))
+    if constexpr (FP4 && DI == 128) {
+        // short lists (at most 8 keys a thread at 4 waves): 4-wave workgroups,
+        // four of which share a compute unit (LDS and registers allow it), so
+        // twice as many queries overlap their latency-bound start and top-K
+        if ((rows + 255) / 256 <= 8 && score_lds_bytes<MT, DI, 8, FP4, 4>(rows, false) + SCORE_STATIC_LDS <= 40 * 1024)
+            return launch_scores<MT, DI, 8, FP4, 4>(a, rows, 1, nullptr);
+    }
     if (need <= 8) return SCKV_FUSED(8);
     if (need <= 16) return SCKV_FUSED(16);
     if (need <= 32) return SCKV_FUSED(32);

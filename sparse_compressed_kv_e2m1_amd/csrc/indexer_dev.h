@@ -216,7 +216,7 @@ __device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int
 // sets the ring depth (tiles per wave) instead of the default.  FP4: the k
 // rows come packed (4-bit e2m1 codes, one E8M0 byte per 32 values) and the
 // contraction runs on the scaled fp4 matrix cores.
-template <int MT, int DI, int NST_ = 0, bool FP4 = false>
+template <int MT, int DI, int NST_ = 0, bool FP4 = false, int NW_ = 0>
 struct ScoreShape {
     static constexpr int HP = MT * 32;                 // padded heads
     static constexpr int KS = FP4 ? DI / 64 : DI / 16; // k-steps (64 fp4 or 16 bf16 values each)
@@ -231,7 +231,7 @@ struct ScoreShape {
     static constexpr int SWZ = (CPR < 8 ? CPR : 8) - 1;  // bf16 chunk swizzle mask
     static constexpr int RPS = 16 / (CPR < 16 ? CPR : 16);  // fp4: rows sharing one swizzle value
     static constexpr int QS = FP4 ? DI / 2 : DI * 2;   // bytes per q row in LDS (fp4: codes)
-    static constexpr int NW = score_waves(FP4);       // waves
+    static constexpr int NW = NW_ > 0 ? NW_ : score_waves(FP4);  // waves
     static constexpr int OFF_Q = NW * NST * TILE;
     static constexpr int OFF_QS = OFF_Q + HP * QS;     // fp4: q scale bytes [HP][SB]
     static constexpr int OFF_W = OFF_QS + HP * SB;     // 64 f32 head weights
@@ -264,7 +264,9 @@ __device__ __forceinline__ void wait_tiles(int ahead) {
 
 // Ring depth of the fused kernel: the keys of a whole query share the LDS
 // with the ring (KPT keys per thread, 256 threads).
-constexpr int fused_ring_depth(int DI, int KPT, bool FP4) {
+// (NWV = 4: 2 deep, so that four 4-wave workgroups share a compute unit)
+constexpr int fused_ring_depth(int DI, int KPT, bool FP4, int NWV = 0) {
+    if (NWV == 4) return 2;
     // fp4, up to 16 keys a thread (at most 8192 rows, 16 tiles a wave): a
     // shallow ring, so that two workgroups share a compute unit and one's
     // prologue and top-K overlap the other's stream
@@ -290,13 +292,13 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32
 // takes its round trip in LDS.  FP4: k arrives as codes [n_c][DI/2] and
 // scale bytes [n_c][DI/32], and q_hat is packed the same way in LDS;
 // otherwise k is bf16 [n_c][DI].
-template <int MT, int DI, int KPT, bool FP4>
+template <int MT, int DI, int KPT, bool FP4, int NWV = 0>
 __device__ __forceinline__ void index_score_body(
     const void* __restrict__ q, const void* __restrict__ k,
     const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
     int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
     int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0, const uint32_t vb) {
-    using S = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4), FP4>;
+    using S = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4, NWV), FP4, NWV>;
     constexpr int KS = S::KS;
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* qh_l = lds + S::OFF_Q;
@@ -304,8 +306,13 @@ __device__ __forceinline__ void index_score_body(
     uint16_t* sc_l = keys_l + rows_per_wg;
     const uint32_t lds0 = lds_offset(lds);
 
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // (the thread number through an opaque copy: the per-thread arithmetic
+    // derived from it then stays inside a caller's loop over work items
+    // instead of being hoisted and kept live across it)
+    int tidx;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tidx) : "v"((int)threadIdx.x));
+    const int lane = tidx & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tidx >> 6);
     const int64_t qi = vb / nsplit;
     const int split = (int)(vb - qi * nsplit);
     const int64_t b = qi / m;
@@ -316,7 +323,7 @@ __device__ __forceinline__ void index_score_body(
     if (KPT > 0 && vis <= K) {
         // every visible row is selected: no scores needed
         int32_t* out = idx + qi * ld + col0;
-        for (int j = threadIdx.x; j < K; j += S::NW * 64) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
+        for (int j = tidx; j < K; j += S::NW * 64) out[j] = (j < vis) ? (int32_t)(offset + j) : -1;
         return;
     }
     // (the split path leaves such queries to the top-k kernel; it still writes
@@ -383,7 +390,7 @@ __device__ __forceinline__ void index_score_body(
     int tq[QD];  // this wave's tiles in request order (>= ntiles_all: none left)
 #pragma unroll
     for (int i = 0; i < QD; ++i) tq[i] = wave + i * S::NW;
-    if (threadIdx.x == 0) tile_ctr = (uint32_t)(S::NW * QD);  // read only after the barrier below
+    if (tidx == 0) tile_ctr = (uint32_t)(S::NW * QD);  // read only after the barrier below
 #pragma unroll
     for (int i = 0; i < S::PD; ++i)
         if (tq[i] < ntiles_all) issue(i, tq[i]);
@@ -391,7 +398,7 @@ __device__ __forceinline__ void index_score_body(
     // produced (hist[0..256)); hist[256..512) serves the second pass
     __shared__ uint32_t hist[KPT > 0 ? 512 : 1];
     if (KPT > 0)
-        for (int i = threadIdx.x; i < 512; i += S::NW * 64) hist[i] = 0u;
+        for (int i = tidx; i < 512; i += S::NW * 64) hist[i] = 0u;
     // q and w landed (only the tile copies may still be in flight), in every wave
     if (S::PD == 0 || tq[S::PD > 0 ? S::PD - 1 : 0] < ntiles_all)
         wait_vmcnt<S::PD * S::NINST>();
@@ -406,7 +413,7 @@ __device__ __forceinline__ void index_score_body(
     if constexpr (!FP4) {
         // q_hat = E8M0_B32 round trip of the raw q, one 32-value block per thread
         // and step, in place; padded heads (h >= Hi) become zero rows
-        for (int blk = threadIdx.x; blk < S::HP * (DI / 32); blk += S::NW * 64) {
+        for (int blk = tidx; blk < S::HP * (DI / 32); blk += S::NW * 64) {
             const int h = blk / (DI / 32);
             const int c = blk - h * (DI / 32);
             u32x4* qb = reinterpret_cast<u32x4*>(qh_l + h * S::QS + c * 64);
@@ -447,7 +454,7 @@ __device__ __forceinline__ void index_score_body(
         // the block's E8M0 byte); padded heads (h >= Hi) are never read
         const unsigned char* qr_l = lds + S::OFF_QR;
         uint8_t* qs_w = lds + S::OFF_QS;
-        for (int blk = threadIdx.x; blk < Hi * (DI / 32); blk += S::NW * 64) {
+        for (int blk = tidx; blk < Hi * (DI / 32); blk += S::NW * 64) {
             const int h = blk / (DI / 32);
             const int c = blk - h * (DI / 32);
             const u32x4* qb = reinterpret_cast<const u32x4*>(qr_l + h * DI * 2 + c * 64);
@@ -610,16 +617,16 @@ __device__ __forceinline__ void index_score_body(
     if (KPT == 0) {
         // ---- flush this workgroup's keys (and scores) with coalesced stores
         uint16_t* kout = keys + qi * n_c + row0;
-        for (int64_t i = threadIdx.x; i < nrows; i += S::NW * 64) kout[i] = keys_l[i];
+        for (int64_t i = tidx; i < nrows; i += S::NW * 64) kout[i] = keys_l[i];
         if (scores) {
             uint16_t* sout = scores + qi * n_c + row0;
-            for (int64_t i = threadIdx.x; i < nrows; i += S::NW * 64) sout[i] = sc_l[i];
+            for (int64_t i = tidx; i < nrows; i += S::NW * 64) sout[i] = sc_l[i];
         }
     } else {
         // ---- fused top-K over the query's keys in LDS (row0 == 0, nrows == vis > K)
         constexpr int KP = KPT > 0 ? KPT : 8;
         __shared__ uint32_t tot[S::NW];
-        const int64_t s0 = (int64_t)threadIdx.x * KP;
+        const int64_t s0 = (int64_t)(uint32_t)(tidx * KP);  // (32-bit product: uniform operands stay scalar)
         uint32_t key[KP];
 #pragma unroll
         for (int j8 = 0; j8 < KP / 8; ++j8) {
