@@ -135,6 +135,62 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[KPT], int64_t 
     }
 }
 
+// topk_select with the keys packed two to a register (key 2i in the low half
+// of kp[i], key 2i + 1 in the high half): the same selection and compaction
+// in half the key registers, for 128 keys a thread.
+template <int KP2, int NWAVES>
+__device__ __forceinline__ void topk_select_packed(const uint32_t (&kp_in)[KP2], int64_t s0, int K, int32_t offset,
+                                                   int32_t* __restrict__ out, uint32_t (*red)[NWAVES], uint32_t* tot) {
+    uint32_t kp[KP2];
+#pragma unroll
+    for (int i = 0; i < KP2; ++i) kp[i] = kp_in[i];
+    uint32_t tau = 0;
+    int rb = 0;
+#pragma unroll 1
+    for (int bit = 15; bit >= 0; --bit) {
+        // (the words pass an empty asm each round, so that their halves are
+        // taken apart inside the round instead of being hoisted out of the
+        // loop into 2 KP2 registers)
+#pragma unroll
+        for (int i = 0; i < KP2; ++i) asm volatile("" : "+v"(kp[i]));
+        const uint32_t cand = tau | (1u << bit);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < KP2; ++i) c += ((kp[i] & 0xffffu) >= cand) + ((kp[i] >> 16) >= cand);
+        const uint32_t total = block_sum<NWAVES>(c, red[rb]);
+        rb ^= 1;
+        if (total >= (uint32_t)K) tau = cand;
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < KP2; ++i) asm volatile("" : "+v"(kp[i]));
+#pragma unroll
+    for (int i = 0; i < KP2; ++i) {
+        const uint32_t k0 = kp[i] & 0xffffu, k1 = kp[i] >> 16;
+        gt += (k0 > tau) + (k1 > tau);
+        eq += (k0 == tau) + (k1 == tau);
+    }
+    const uint32_t gt_total = block_sum<NWAVES>(gt, red[rb]);
+    const uint32_t need_eq = (uint32_t)K - gt_total;  // >= 1 by the choice of tau
+    const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
+    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
+    take_eq = take_eq < eq ? take_eq : eq;
+    uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
+    uint32_t eq_seen = 0;
+#pragma unroll
+    for (int i = 0; i < KP2; ++i) asm volatile("" : "+v"(kp[i]));
+#pragma unroll
+    for (int j = 0; j < 2 * KP2; ++j) {
+        const uint32_t k = (j & 1) ? (kp[j >> 1] >> 16) : (kp[j >> 1] & 0xffffu);
+        bool take = k > tau;
+        if (k == tau) {
+            take = eq_seen < take_eq;
+            ++eq_seen;
+        }
+        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s0 + j);
+    }
+}
+
 // The bin b of a 256-bin histogram with (keys in bins above b) < k <= (keys
 // in bins b and above), and the count of keys in bins above b; every wave
 // computes the same (uniform) answer from LDS.  Needs 1 <= k <= total.
@@ -665,6 +721,44 @@ __device__ __forceinline__ void topk_body(const uint16_t* __restrict__ keys, int
     }
     const uint16_t* kp = keys + qi * n_c;
     const int64_t s0 = (int64_t)tid * KPT;
+    if constexpr (KPT >= 128) {
+        // keys two to a register (128 keys a thread)
+        uint32_t kw[KPT / 2];
+        // groups of 8 keys: 16-byte loads when every query's keys start on a
+        // 16-byte boundary (n_c % 8 == 0), else 4-byte loads (n_c even) or
+        // 2-byte loads; only the group that crosses n_c is read key by key
+#pragma unroll
+        for (int j8 = 0; j8 < KPT / 8; ++j8) {
+            const int64_t g0 = s0 + 8 * j8;
+            u32x4 v = u32x4{0, 0, 0, 0};
+            if (g0 + 8 <= n_c) {
+                if ((n_c % 8) == 0) {
+                    v = load16(kp + g0);
+                } else if ((n_c % 2) == 0) {
+                    const uint32_t* p32 = reinterpret_cast<const uint32_t*>(kp + g0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = p32[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = (uint32_t)kp[g0 + 2 * e] | ((uint32_t)kp[g0 + 2 * e + 1] << 16);
+                }
+            } else if (g0 < n_c) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (g0 + e < n_c) v[e >> 1] |= (uint32_t)kp[g0 + e] << (16 * (e & 1));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kw[4 * j8 + e] = v[e];
+        }
+#pragma unroll
+        for (int i = 0; i < KPT / 2; ++i) {
+            const uint32_t lo = (s0 + 2 * i < vis) ? (kw[i] & 0xffffu) : 0u;
+            const uint32_t hi = (s0 + 2 * i + 1 < vis) ? (kw[i] & 0xffff0000u) : 0u;
+            kw[i] = lo | hi;
+        }
+        topk_select_packed<KPT / 2, TOPK_THREADS / 64>(kw, s0, K, offset, out, red, tot);
+        return;
+    }
     uint32_t key[KPT];
     if (KPT % 8 == 0 && (n_c % 8) == 0) {
         // whole 16-byte groups of 8 keys; groups past n_c are not read

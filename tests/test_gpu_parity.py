@@ -368,6 +368,8 @@ INDEXER_CASES = [
     (1, 6, 64, 128, 20, 4, 0, 8),            # early positions: 0, 1, 2 see nothing
     (3, 1, 64, 128, 3000, 4, 11999, 3000),   # K >= visible: all visible rows
     (1, 1, 4, 32, 65536, 1, 65535, 5000),    # largest supported n_c (128 keys per top-k thread)
+    (1, 3, 4, 32, 40001, 1, 40000, 3000),    # 128 keys a thread, odd n_c: 2-byte key loads
+    (2, 2, 4, 32, 40002, 1, 40000, 3000),    # n_c even, not a multiple of 8: 4-byte key loads
     (1, 2, 8, 64, 20000, 1, 19999, 777),     # 40 keys per thread, ragged
     (1, 1, 16, 32, 600, 1, 599, 599),        # K = V - 1
 ]
