@@ -351,11 +351,14 @@ __device__ __forceinline__ f32x16 mfma_fp4(u32x4 a, uint32_t sa, u32x4 b, uint32
 template <int MT, int DI, int KPT, bool FP4, int NWV = 0>
 __device__ __forceinline__ void index_score_body(
     const void* __restrict__ q, const void* __restrict__ k,
-    const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi, int64_t n_c, int ratio,
+    const uint8_t* __restrict__ k_scales, const float* __restrict__ w, int64_t m, int Hi_arg, int64_t n_c, int ratio,
     int64_t start_pos, int rows_per_wg, int nsplit, uint16_t* __restrict__ keys, uint16_t* __restrict__ scores, int K,
     int32_t offset, int32_t* __restrict__ idx, int64_t ld, int64_t col0, const uint32_t vb) {
     using S = ScoreShape<MT, DI, KPT == 0 ? 0 : fused_ring_depth(DI, KPT, FP4, NWV), FP4, NWV>;
     constexpr int KS = S::KS;
+    // two head tiles hold Hi in 33..64, and Hi is a power of two: Hi = 64,
+    // known at compile time (the head-sum steps below then need no selects)
+    const int Hi = MT == 2 ? 64 : Hi_arg;
     extern __shared__ __align__(16) unsigned char lds[];
     unsigned char* qh_l = lds + S::OFF_Q;
     uint16_t* keys_l = reinterpret_cast<uint16_t*>(lds + S::OFF_KEYS);
@@ -407,18 +410,29 @@ __device__ __forceinline__ void index_score_body(
     const uint8_t* ksb = FP4 ? k_scales + b * n_c * S::SB : nullptr;
     const uint32_t ring = lds0 + (uint32_t)(wave * S::NST * S::TILE);
     // the wave's seq-th tile (ring stage seq % NST) is tile t
+    // (a sequence's k rows span under 2^31 bytes: n_c <= 65536 rows of at most
+    // 512 bytes, so the copy offsets are 32-bit)
     auto issue = [&](int seq, int t) {
         const int64_t s0 = row0 + (int64_t)t * 32;
         const uint32_t st = ring + (uint32_t)((seq % S::NST) * S::TILE);
+        // a tile wholly inside the array (every one but possibly the last):
+        // the tile's offset plus the lane's, no clamp
+        const bool whole = s0 + 32 <= n_c;
 #pragma unroll
         for (int j = 0; j < S::CT / 1024; ++j) {
             const int slot = j * 64 + lane;  // 16-byte slot of the tile
             const int r = slot / S::CPR;
             const int cp = slot % S::CPR;
             const int ch = FP4 ? (cp ^ ((r / S::RPS) % S::CPR)) : (cp ^ (r & S::SWZ));
-            int64_t row = s0 + r;
-            row = row < n_c ? row : n_c - 1;  // tail rows re-read a real row; their results are dropped
-            dma16_s(kb, (uint32_t)(row * S::ROWB + ch * 16), st + (uint32_t)(j * 1024));
+            uint32_t off;
+            if (whole) {
+                off = (uint32_t)s0 * (uint32_t)S::ROWB + (uint32_t)(r * S::ROWB + ch * 16);
+            } else {
+                int64_t row = s0 + r;
+                row = row < n_c ? row : n_c - 1;  // tail rows re-read a real row; their results are dropped
+                off = (uint32_t)(row * S::ROWB + ch * 16);
+            }
+            dma16_s(kb, off, st + (uint32_t)(j * 1024));
         }
         if (FP4) {
             // scale bytes of the tile's 32 rows, 4 bytes a lane (SB = 2: 2 rows a lane)
@@ -426,10 +440,16 @@ __device__ __forceinline__ void index_score_body(
             const int rpl = S::SB >= 4 ? 1 : 4 / S::SB;      // rows per lane
             const int nl = 32 * per / rpl;
             if (lane < nl) {
-                int64_t row = s0 + (lane / per) * rpl;
-                const int64_t last = n_c - rpl;  // keep the 4-byte read inside the array
-                row = row < last ? row : (last > 0 ? last : 0);
-                dma4_s(ksb, (uint32_t)(row * S::SB + (lane % per) * 4), st + (uint32_t)(S::CT));
+                uint32_t off;
+                if (whole) {
+                    off = (uint32_t)s0 * (uint32_t)S::SB + (uint32_t)(((lane / per) * rpl) * S::SB + (lane % per) * 4);
+                } else {
+                    int64_t row = s0 + (lane / per) * rpl;
+                    const int64_t last = n_c - rpl;  // keep the 4-byte read inside the array
+                    row = row < last ? row : (last > 0 ? last : 0);
+                    off = (uint32_t)(row * S::SB + (lane % per) * 4);
+                }
+                dma4_s(ksb, off, st + (uint32_t)(S::CT));
             }
         }
     };
