@@ -22,9 +22,9 @@
 // 16-byte chunks swizzled by row so the B-operand reads hit every bank).  All
 // products are exact and, for round-tripped data, every partial sum is a
 // binary32 value, so the MFMA accumulation order does not matter.  The head
-// sum follows the fixed pairwise order (stride Hi/2 first): in the D tile
-// layout strides 32, 16, 8, 2 and 1 stay inside a lane and stride 4 is the
-// lane^32 exchange.  Ordered 16-bit keys collect in LDS and leave with
+// sum follows the fixed pairwise order (stride Hi/2 first); the q rows sit in
+// the MFMA rows so that strides 32, 16, 8, 4 and 2 stay inside a lane and only
+// stride 1 is the lane^32 exchange.  Ordered 16-bit keys collect in LDS and leave with
 // coalesced stores.  Waves take tiles as they ask for them (an LDS counter),
 // so they finish together.  Short fused lists (at most 2048 rows, fp4 k) run
 // in a persistent grid of 4-wave workgroups, four to a compute unit.

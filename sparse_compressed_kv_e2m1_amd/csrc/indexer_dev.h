@@ -330,6 +330,14 @@ constexpr int fused_ring_depth(int DI, int KPT, bool FP4, int NWV = 0) {
                : ((64 * DI >= 16384) ? 1 : (KPT >= 128 ? 2 : 4));
 }
 
+// The head that row r of a 32-head tile holds in the score products: the D
+// layout gives lane l, value i the row 8 (i / 4) + 4 (l / 32) + i % 4, so row r
+// holding head 2 (4 (r / 8) + r % 4) + (r / 4) % 2 puts head 2 i + l / 32 at
+// value i of lane l.  Every pair the fixed head-sum tree adds (h, h + stride)
+// for strides 32 (the other tile), 16, 8, 4, 2 then sits in one lane; only
+// stride 1 crosses to lane l ^ 32.
+__device__ __forceinline__ int head_of_row(int r) { return 2 * ((r >> 3) * 4 + (r & 3)) + ((r >> 2) & 1); }
+
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands e2m1 (format 4): lane l
 // holds, for row l%32, the 32 codes of k-block l/32 (16 bytes, in the low four
 // registers) and that block's E8M0 scale in the low byte of its scale word.
@@ -522,7 +530,7 @@ __device__ __forceinline__ void index_score_body(
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + (lane & 31)) * S::QS +
+                qa[mt][ks] = *reinterpret_cast<const bf16x8*>(qh_l + (mt * 32 + head_of_row(lane & 31)) * S::QS +
                                                               (ks * 16 + (lane >> 5) * 8) * 2);
     } else {
         // q_hat = E8M0_B32 round trip of the raw q, packed: one 32-value block per
@@ -577,7 +585,7 @@ __device__ __forceinline__ void index_score_body(
         const uint8_t* qs_l = lds + S::OFF_QS;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const int h = mt * 32 + (lane & 31);
+            const int h = mt * 32 + head_of_row(lane & 31);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int blk = 2 * ks + (lane >> 5);
@@ -586,14 +594,14 @@ __device__ __forceinline__ void index_score_body(
             }
         }
     }
-    // head weights in D layout: head mt*32 + d_row(i, lane)
+    // head weights in D layout: value i of lane l is head mt*32 + 2 i + l / 32
     const float* w_l = reinterpret_cast<const float*>(lds + S::OFF_W);
     float wd[MT][16];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int h = mt * 32 + d_row(i, lane);
+            const int h = mt * 32 + 2 * i + (lane >> 5);
             wd[mt][i] = (h < Hi) ? w_l[h] : 0.0f;
         }
     __syncthreads();  // every wave holds q_hat and w before keys overwrite them
@@ -666,20 +674,16 @@ __device__ __forceinline__ void index_score_body(
             for (int i = 0; i < 4; ++i) v[i] = v[i] + v[i + 4];
         }
         if (Hi > 4) {
-            // heads h and h + 4 sit in lanes l and l ^ 32: the lane swap hands
-            // both lanes (v of the lower lane, v of the upper lane)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i]), false,
-                                                                 false);
-                v[i] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-            }
-        }
-        if (Hi > 2) {
             v[0] = v[0] + v[2];
             v[1] = v[1] + v[3];
         }
-        if (Hi > 1) v[0] = v[0] + v[1];
+        if (Hi > 2) v[0] = v[0] + v[1];
+        if (Hi > 1) {
+            // heads h and h + 1 sit in lanes l and l ^ 32: the lane swap hands
+            // both lanes (v of the lower lane, v of the upper lane)
+            const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+            v[0] = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+        }
         const int64_t s = row0 + (int64_t)tile * 32 + r;
         if (lane < 32 && s < row_end) {
             const uint32_t bits = f32_to_bf16_bits(v[0]);
