@@ -546,8 +546,11 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # (the GPU's clocks settle over ~50-80 decode steps after idle time: a
+    # decode step measured 1.8 ms in its first 20 steps, 567 us in steps 20-40
+    # and 542 us from step 80 on; 60 warm-up steps reach that steady state)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=60)
     ap.add_argument("--workload", default="decode")
     ap.add_argument("--instances", type=int, default=None, help="B independent sequences per step")
     ap.add_argument("--kcache", choices=["fp4", "bf16"], default="fp4",
