@@ -207,6 +207,9 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16", latent="bf16"):
     1 GiB device copy reads and writes 1 GiB)."""
     tr = _steady_groups(_csv_rows(os.path.join(folder, "trace"), "kernel_trace.csv"),
                         lambda r: (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"]))
+    # durations after the warm-up launches (the first 40% of a kernel's
+    # dispatches: the GPU's clocks are still settling there)
+    tr = {k: sorted(v, key=lambda r: int(r["Start_Timestamp"]))[(len(v) * 2) // 5:] for k, v in tr.items()}
     dur = {k: sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in v) / len(v) / 1e3
            for k, v in tr.items()}
     calls = {k: len(v) for k, v in tr.items()}
@@ -231,7 +234,8 @@ def summarize_profiles(w, B, folder, commands, kcache="bf16", latent="bf16"):
     lines += ["# commands (repo root as working directory):"] + [f"#   {c}" for c in commands]
     lines += [f"# counter scale (1 GiB device copy): FETCH_SIZE x{scale.get('FETCH_SIZE', float('nan')):.3f}, "
               f"WRITE_SIZE x{scale.get('WRITE_SIZE', float('nan')):.3f}",
-              "# steady-state dispatches only (most frequent grid size per kernel)", "#",
+              "# steady-state dispatches only (most frequent grid size per kernel; durations after the first 40%"
+              " of its dispatches, the warm-up)", "#",
               f"{'kernel':<44} {'calls':>5} {'avg_us':>9} {'read_MB':>9} {'write_MB':>9}"]
     # only the kernels of the step's own calls (set-up launches are left out)
     from sparse_compressed_kv_e2m1_amd.step import step_call_names  # noqa: PLC0415
