@@ -241,7 +241,7 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
  * sckv_decode_step -- a whole decode step (m = 1 at start_pos > 0) of B <= 64
  * sequences in ONE launch (forward.rs AttnV41::forward: ring copy, window
  * list, indexer, merge, attend_and_project; compress.rs: the round trips, the
- * rotation, attention_any).  The results are bit for bit those of
+ * rotation, attention_any).  It computes the same as
  *   sckv_decode_prepare(lat_new, D, latent row n_c-1, n_c*D, k_new, Di, k_codes
  *       row n_c-1, n_c*Di/2, k_scales row n_c-1, n_c*Di/32, Di, kv_new, D, ring,
  *       win*D, B, D, win, start_pos, idx, win+K, rope_table, n_pos, rope_dim,
@@ -251,11 +251,17 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
  *   sckv_sparse_attn_sink(q, ring, win, latent, n_c, idx, win+K, sink, scale,
  *       B, 1, H, D, out, ...)
  * run as phases of one cooperative launch with grid-wide barriers between
- * them (the keys, index lists and split partials pass through ws).  For
+ * them (the keys, index lists and split partials pass through ws): the ring,
+ * caches and index lists bit for bit; the outputs to rounding, as its
+ * attention phase splits each query's list into 64-head work items where
+ * sckv_sparse_attn_sink at B <= 64 uses 16-head workgroups (the two sum the
+ * split partials in different groupings; both within the attention
+ * tolerance of the exact result).  For
  * callers that need a step as a single launch: on MI355X each grid barrier
  * (device-scope atomics across the eight XCDs' L2s) costs a few microseconds,
  * more than the launch gaps of the separate calls, so those are faster at
- * every batch size measured (B = 1: 73 against 40 us at n_c = 8192).
+ * every batch size measured (B = 1: 73 against 35 us at n_c = 8192, the
+ * separate calls replayed from a HIP graph).
  *   lat_new, k_new  [B] new raw latent rows (D bf16) and raw indexer k rows (Di
  *                   bf16), contiguous, or both NULL when no compressed row
  *                   completes at this step (else (start_pos+1) % ratio == 0 and

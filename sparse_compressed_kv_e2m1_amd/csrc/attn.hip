@@ -58,7 +58,7 @@ __global__ __launch_bounds__(NS * NHW * 64) __attribute__((amdgpu_waves_per_eu(2
     const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
     uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
     const uint8_t* __restrict__ rb_scales) {
-    sparse_attn_body<D, NHW, CPS, NS, CS, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, chunks_per_split, nsplit, out, part_o, part_ml, rb_scales, blockIdx.x);
+    sparse_attn_body<D, NHW, CPS, NS, CS, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, chunks_per_split, nsplit, out, part_o, part_ml, rb_scales, blockIdx.x, (int)blockIdx.y * 16 * NHW);
 }
 
 __global__ __launch_bounds__(COMBINE_THREADS) void combine_kernel(const float* __restrict__ part_o,
@@ -85,14 +85,14 @@ template <int D, int NHW, int CPS, int NS = 2, bool CS = false, bool PK = false>
 int launch_attn(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                 const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                 int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
-                const uint8_t* rb_scales) {
+                const uint8_t* rb_scales, int hgroups = 1) {
     using Sh = AttnShape<D, NHW, CPS, NS, CS>;
     if (Sh::LDS_BYTES > 65536) {
         hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<D, NHW, CPS, NS, CS, PK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)Sh::LDS_BYTES);
         if (e != hipSuccess) return fail(SCKV_EHIP, std::string("sckv_sparse_attn_sink: ") + hipGetErrorString(e));
     }
-    sparse_attn_kernel<D, NHW, CPS, NS, CS, PK><<<dim3((unsigned)(nq * nsplit)), dim3(Sh::WAVES * 64), Sh::LDS_BYTES,
+    sparse_attn_kernel<D, NHW, CPS, NS, CS, PK><<<dim3((unsigned)(nq * nsplit), (unsigned)hgroups), dim3(Sh::WAVES * 64), Sh::LDS_BYTES,
                                                  s>>>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, m, H, cps,
                                                       nsplit, out, part_o, part_ml, rb_scales);
     return check_launch("sckv_sparse_attn_sink");
@@ -102,7 +102,7 @@ template <int D, int NHW, bool PK = false>
 int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                   int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
-                  const uint8_t* rb_scales) {
+                  const uint8_t* rb_scales, int hgroups = 1) {
     if constexpr (D == 512 && NHW == 4) {
         // unsplit lists of up to 64 chunks and at least two queries per
         // compute unit: one set of 4 waves (76 KB of LDS), so that two
@@ -122,16 +122,20 @@ int launch_attn_c(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
     }
     if (cps <= 64)
         return launch_attn<D, NHW, 64, 2, false, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
-                                                     cps, nsplit, out, part_o, part_ml, s, rb_scales);
+                                                     cps, nsplit, out, part_o, part_ml, s, rb_scales, hgroups);
     return launch_attn<D, NHW, MAX_CPS, 2, false, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H,
-                                                      cps, nsplit, out, part_o, part_ml, s, rb_scales);
+                                                      cps, nsplit, out, part_o, part_ml, s, rb_scales, hgroups);
 }
 
 template <int D, bool PK = false>
 int launch_attn_d(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const uint16_t* rows_b, int64_t rb,
                   const int32_t* idx, int T, const float* sink, float scale_log2, int64_t nq, int64_t m, int H,
                   int cps, int nsplit, uint16_t* out, float* part_o, float* part_ml, hipStream_t s,
-                  const uint8_t* rb_scales) {
+                  const uint8_t* rb_scales, int hgroups = 1) {
+    // head groups of 16: one 16-head wave per set
+    if (H <= 16 || hgroups > 1)
+        return launch_attn_c<D, 1, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
+                                       out, part_o, part_ml, s, rb_scales, hgroups);
     if (H <= 16)
         return launch_attn_c<D, 1, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
                                        out, part_o, part_ml, s, rb_scales);
@@ -145,14 +149,9 @@ int launch_attn_d(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
 }  // namespace
 
 size_t attn_workspace_bytes(int B, int64_t m, int H, int D, int64_t T) {
-    int cps, nsplit;
-    attn_split((int64_t)B * m, (int)T, &cps, &nsplit);
-    if (nsplit == 1) return 0;
-    const size_t nq = (size_t)B * (size_t)m;
-    size_t bytes = nq * (size_t)nsplit * (size_t)H * (size_t)D * 4u;
-    bytes = (bytes + 255u) & ~(size_t)255u;
-    bytes += nq * (size_t)nsplit * (size_t)H * 2u * 4u;
-    return (bytes + 255u) & ~(size_t)255u;
+    int cps, nsplit, hgroups;
+    attn_split_groups((int64_t)B * m, (int)T, H, &cps, &nsplit, &hgroups);
+    return attn_partials_bytes((int64_t)B * m, nsplit, H, D);
 }
 
 }  // namespace sckv
@@ -188,8 +187,8 @@ int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, co
             return fail(SCKV_EINVAL, std::string(name) + ": packed rows_b scale bytes must be 16-byte aligned");
     }
     const int64_t nq = (int64_t)B * m;
-    int cps, nsplit;
-    attn_split(nq, T, &cps, &nsplit);
+    int cps, nsplit, hgroups;
+    attn_split_groups(nq, T, H, &cps, &nsplit, &hgroups);
     if (nq * nsplit > 0x7fffffffLL) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": grid too large");
     const size_t need = attn_workspace_bytes(B, m, H, D, T);
     if (need && (!ws || ws_bytes < need)) return fail(SCKV_EWORKSPACE, std::string(name) + ": workspace too small");
@@ -209,11 +208,12 @@ int attn_run(const char* name, const void* q, const void* rows_a, int64_t ra, co
     uint16_t* oo = (uint16_t*)out;
     int rc;
     const uint8_t* sc = (const uint8_t*)rb_scales;
-#define SCKV_ATTN(D) \
-    launch_attn_d<D>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s, sc)
+#define SCKV_ATTN(D)                                                                                              \
+    launch_attn_d<D>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o, part_ml, s, sc, \
+                     hgroups)
     if (rb_scales) {
         rc = launch_attn_d<512, true>(qq, aa, ra, bb, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit, oo, part_o,
-                                      part_ml, s, sc);
+                                      part_ml, s, sc, hgroups);
     } else {
         switch (D) {
             case 64: rc = SCKV_ATTN(64); break;

@@ -107,10 +107,14 @@ template <int D, int NHW, int CPS, int NS, bool CS, bool PK>
 __device__ __forceinline__ void sparse_attn_body(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ rows_a, int64_t ra,
     const uint16_t* __restrict__ rows_b, int64_t rb, const int32_t* __restrict__ idx, int T,
-    const float* __restrict__ sink, float scale_log2, int64_t m, int H, int chunks_per_split, int nsplit,
-    uint16_t* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
-    const uint8_t* __restrict__ rb_scales, const uint32_t vb) {
+    const float* __restrict__ sink_all, float scale_log2, int64_t m, int HS, int chunks_per_split, int nsplit,
+    uint16_t* __restrict__ out_all, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const uint8_t* __restrict__ rb_scales, const uint32_t vb, const int h0 = 0) {
     using S = AttnShape<D, NHW, CPS, NS, CS>;
+    // this workgroup's heads: h0 .. h0 + H - 1 of the query's HS (at most 16 NHW)
+    const int H = (HS - h0) < 16 * NHW ? (HS - h0) : 16 * NHW;
+    const float* __restrict__ sink = sink_all + h0;
+    uint16_t* __restrict__ out = out_all + (int64_t)h0 * D;  // row (qi, h0 + r) at out + (qi HS + r) D
     static_assert(!PK || D == 512, "packed rows_b at D = 512 only");
     constexpr int PKB = D / 2 + D / 16;  // packed bytes of a row (codes, then scale bytes)
     constexpr int PKO = S::RS - PKB;     // where they land in the row's stage slot
@@ -133,7 +137,7 @@ __device__ __forceinline__ void sparse_attn_body(
     const uint8_t* codes_b = PK ? reinterpret_cast<const uint8_t*>(rows_b) + b * rb * (D / 2) : nullptr;
     const uint8_t* scl_b = PK ? rb_scales + b * rb * (D / 16) : nullptr;
     const int32_t* idx_q = idx + qi * (int64_t)T;
-    const uint16_t* qrow = q + qi * (int64_t)H * D;
+    const uint16_t* qrow = q + (qi * (int64_t)HS + h0) * D;
 
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int c_begin = split * chunks_per_split;
@@ -570,7 +574,7 @@ __device__ __forceinline__ void sparse_attn_body(
             const int r = piece / NPC, c = piece % NPC;
             if (r < H) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PR + ((c ^ (r % NPC)) << 4));
-                store16(reinterpret_cast<unsigned char*>(out + (qi * H + r) * (int64_t)D + hw * (D / NHW)) + c * 16, v);
+                store16(reinterpret_cast<unsigned char*>(out + (qi * HS + r) * (int64_t)D + hw * (D / NHW)) + c * 16, v);
             }
         }
         return;
@@ -608,7 +612,7 @@ __device__ __forceinline__ void sparse_attn_body(
             const int r = piece / CPR, c = piece % CPR;
             if (r < nrow1) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * PF + c * 16);
-                store16(reinterpret_cast<unsigned char*>(out + (qi * H + 16 * hw + r) * (int64_t)D) + c * 16, v);
+                store16(reinterpret_cast<unsigned char*>(out + (qi * HS + 16 * hw + r) * (int64_t)D) + c * 16, v);
             }
         }
         return;
@@ -691,7 +695,7 @@ __device__ __forceinline__ void sparse_attn_body(
             const int r = piece / CPRW, c = piece % CPRW;
             if (r < nrow) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(stg + r * P + c * 16);
-                store16(reinterpret_cast<unsigned char*>(out + (qi * H + 16 * hw + r) * (int64_t)D + col0) + c * 16, v);
+                store16(reinterpret_cast<unsigned char*>(out + (qi * HS + 16 * hw + r) * (int64_t)D + col0) + c * 16, v);
             }
         }
     } else {
@@ -708,7 +712,7 @@ __device__ __forceinline__ void sparse_attn_body(
                 *reinterpret_cast<float*>(stg + r * (2 * D) + (((c >> 2) ^ (r % SWR)) << 4) + (c & 3) * 4) = fo[k][i];
             }
         wave_lds_sync();
-        const int64_t pbase = (qi * nsplit + split) * (int64_t)H + 16 * hw;
+        const int64_t pbase = (qi * nsplit + split) * (int64_t)HS + h0 + 16 * hw;
 #pragma unroll
         for (int k = 0; k < 16 * CPRW / 64; ++k) {
             const int piece = k * 64 + lane;
@@ -811,6 +815,43 @@ void attn_split(int64_t nq, int T, int* chunks_per_split, int* nsplit) {
     // workgroup cost more than the chunk itself (measured, decode at B = 1)
     if (cps < MIN_SPLIT_CHUNKS) cps = nchunks < MIN_SPLIT_CHUNKS ? nchunks : MIN_SPLIT_CHUNKS;
     if (cps > MAX_CPS) cps = MAX_CPS;
+    *chunks_per_split = cps;
+    *nsplit = (nchunks + cps - 1) / cps;
+}
+
+// Bytes of the split partials: [nq][nsplit][H][D] f32 O, then [nq][nsplit][H]
+// (max, sum) pairs, each part 256-byte aligned; 0 without a split.
+size_t attn_partials_bytes(int64_t nq, int nsplit, int H, int D) {
+    if (nsplit <= 1) return 0;
+    size_t bytes = (size_t)nq * (size_t)nsplit * (size_t)H * (size_t)D * 4u;
+    bytes = (bytes + 255u) & ~(size_t)255u;
+    bytes += (size_t)nq * (size_t)nsplit * (size_t)H * 2u * 4u;
+    return (bytes + 255u) & ~(size_t)255u;
+}
+
+// Split of the attention call when the queries alone do not give a quarter of
+// a workgroup per compute unit: the heads go to ceil(H / 16) workgroups of 16
+// heads each (two waves, one chunk a set at a time), and the chunks to ranges
+// of at least 2 (one per set), so that a query's work spreads over about 256
+// workgroups with short chains of dependent copies.  hgroups = 1 when no split
+// is needed.
+void attn_split_groups(int64_t nq, int T, int H, int* chunks_per_split, int* nsplit, int* hgroups) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int64_t want = (256 + nq - 1) / nq;  // workgroups per query
+    // (from two to three workgroups a query the 64-head split is faster:
+    // 16-head workgroups take 135 KB of LDS for 2 waves, one per compute unit)
+    if (want < 4 || H <= 16) {
+        *hgroups = 1;
+        attn_split(nq, T, chunks_per_split, nsplit);
+        return;
+    }
+    const int G = (H + 15) / 16;
+    int64_t splits = (want + G - 1) / G;
+    if (splits > nchunks) splits = nchunks;
+    int cps = (int)((nchunks + splits - 1) / splits);
+    if (cps < 2) cps = nchunks < 2 ? nchunks : 2;
+    if (cps > MAX_CPS) cps = MAX_CPS;
+    *hgroups = G;
     *chunks_per_split = cps;
     *nsplit = (nchunks + cps - 1) / cps;
 }

@@ -215,7 +215,9 @@ int launch_step(StepArgs& a, hipStream_t s, const char* name) {
 extern "C" size_t sckv_decode_step_workspace_bytes(int B, int H, int D, int64_t n_c, int T) {
     using namespace sckv;
     if (B < 0 || H <= 0 || D <= 0 || n_c < 0 || T <= 0) return (size_t)-1;
-    return STEP_SYNC_BYTES + step_keys_bytes(B, n_c) + align256(attn_workspace_bytes(B, 1, H, D, T));
+    int cps, nsplit;
+    attn_split(B, T, &cps, &nsplit);
+    return STEP_SYNC_BYTES + step_keys_bytes(B, n_c) + align256(attn_partials_bytes(B, nsplit, H, D));
 }
 
 extern "C" int sckv_decode_step(const void* lat_new, const void* k_new, const void* kv_new, const float* rope_table,

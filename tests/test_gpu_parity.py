@@ -962,9 +962,12 @@ DSTEP_CASES = [("decode", 1, True), ("decode", 3, True), ("decode", 13, True), (
 def test_decode_step_one_launch_matches_separate_calls(sk, name, B, new):
     """sckv_decode_step (set-up, scores, top-K, attention, combine as phases
     of one cooperative launch) against the separate calls on the same inputs:
-    index lists, outputs, ring, latent and packed k caches bit for bit, on two
-    launches in a row; sequence 0 against the oracle.  new=False: a step that
-    completes no compressed row."""
+    index lists, ring, latent and packed k caches bit for bit, outputs within
+    the attention tolerance of each other (the separate attention call splits
+    small batches into 16-head workgroups, the one launch into 64-head work
+    items, so the split partials are summed in other groupings), on two
+    launches in a row, the second repeating the first bit for bit; sequence 0
+    against the oracle.  new=False: a step that completes no compressed row."""
     from sparse_compressed_kv_e2m1_amd.step import PathState, step_call_names
 
     w = synth.WORKLOADS[name]
@@ -981,9 +984,13 @@ def test_decode_step_one_launch_matches_separate_calls(sk, name, B, new):
         states[mode] = st
     torch.cuda.synchronize()
     sep, one = states["separate"], states["one"]
+    first = one.out.clone()
+    sep_out = vals(bits(sep.out))
     for rep in range(2):
         assert torch.equal(one.idx, sep.idx), (rep, "index lists")
-        assert torch.equal(one.out.view(torch.int16), sep.out.view(torch.int16)), (rep, "outputs")
+        ok, worst = attn_tolerance_ok(vals(bits(one.out)), sep_out)
+        assert ok, (rep, "outputs", worst)
+        assert torch.equal(one.out.view(torch.int16), first.view(torch.int16)), (rep, "repeat")
         assert torch.equal(one.ring.view(torch.int16), sep.ring.view(torch.int16)), (rep, "ring")
         assert torch.equal(one.latent.view(torch.int16), sep.latent.view(torch.int16)), (rep, "latent cache")
         assert torch.equal(one.ik_codes, sep.ik_codes) and torch.equal(one.ik_scales, sep.ik_scales), (rep, "k cache")
