@@ -28,12 +28,13 @@ __device__ __forceinline__ uint32_t score_key(uint32_t b) {
 // ---- top-k: one block per query, keys held in registers
 //
 // Thread t owns the KPT consecutive rows [t*KPT, t*KPT + KPT).  The K-th
-// largest key tau is built bit by bit (16 rounds: keep bit b when at least K
-// keys are >= the candidate), counting in registers and summing over the
-// block; then the rows with key > tau and the first (K - #greater) rows with
-// key == tau (lowest rows first) are written in ascending row order with two
-// block prefix sums.  No atomics; missing rows hold key 0, below every real
-// key (finite scores have keys >= 0x007f).
+// largest key tau is found with counts in registers summed over the block
+// (its high byte) and an LDS histogram (its low byte; topk_select), or bit by
+// bit in 16 rounds of counts (keys two to a register, topk_select_packed);
+// then the rows with key > tau and the first (K - #greater) rows with key ==
+// tau (lowest rows first) are written in ascending row order with two block
+// prefix sums.  Missing rows hold key 0, below every real key (finite scores
+// have keys >= 0x007f).
 
 // DPP helpers (no LDS round trip).  update_dpp(old, src, ctrl, row_mask,
 // bank_mask, bound_ctrl): lanes outside row_mask keep `old`.
@@ -88,39 +89,135 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tot) {
     return before + incl - x;
 }
 
+// The bin b of a 256-bin histogram with (keys in bins above b) < k <= (keys
+// in bins b and above), and the count of keys in bins above b; every wave
+// computes the same (uniform) answer from LDS.  Needs 1 <= k <= total.
+__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t k, uint32_t& bin, uint32_t& above) {
+    const int lane = threadIdx.x & 63;
+    const u32x4 c = *reinterpret_cast<const u32x4*>(h + 4 * lane);  // bins 4 lane .. 4 lane + 3
+    const uint32_t s = c[0] + c[1] + c[2] + c[3];
+    const uint32_t incl = wave_incl_scan(s);                       // keys in bins < 4 (lane + 1)
+    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    const uint32_t ge = total - incl + s;                           // keys in bins >= 4 lane
+    const uint32_t gt = ge - s;                                     // keys in bins >= 4 (lane + 1)
+    const bool mine = gt < k && ge >= k;                            // exactly one lane
+    const int L = __builtin_ctzll(__ballot(mine));
+    uint32_t b = 4 * lane, run = gt;
+    if (mine) {
+#pragma unroll
+        for (int i = 3; i >= 1; --i) {
+            if (run + c[i] >= k) {
+                b = 4 * lane + i;
+                break;
+            }
+            run += c[i];
+        }
+    }
+    bin = (uint32_t)__builtin_amdgcn_readlane((int)b, L);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)run, L);
+}
+
+// Max of x over the wave (uniform result), the same butterfly as wave_sum.
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+    x = max(x, SCKV_DPP(x, 0xb1, 0xf, false));
+    x = max(x, SCKV_DPP(x, 0x4e, 0xf, false));
+    x = max(x, SCKV_DPP(x, 0x141, 0xf, false));
+    x = max(x, SCKV_DPP(x, 0x140, 0xf, false));
+    return max(max((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
+}
+
+// Max over the block of NWAVES waves (buf as in block_sum).
+template <int NWAVES>
+__device__ __forceinline__ uint32_t block_max(uint32_t x, uint32_t* buf) {
+    const uint32_t w = wave_max(x);
+    if ((threadIdx.x & 63) == 0) buf[threadIdx.x >> 6] = w;
+    __syncthreads();
+    uint32_t t = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) t = max(t, buf[i]);
+    return t;
+}
+
 // Top-K of the keys held by the block: thread t owns key[0..KPT) of rows
 // s0 .. s0+KPT-1 (rows at or past the visible count hold key 0).  Writes
 // offset + s of the K selected rows in ascending s to out[0..K).  Needs
 // V > K visible rows (so tau ends up >= 1 and every missing key is below it).
-// (Measured against a wave-ballot count and against starting below the high
-// bits the smallest and largest keys share: neither was faster, as scores of
-// both signs leave no shared bits and the 16 block sums set the time.)
+// The K-th largest key tau: its high byte h is the largest with at least K
+// keys whose high byte is >= h, searched downwards from the high byte of the
+// largest key (the top keys of a score list share one or two high bytes:
+// typically one or two block counts) and, after four steps, by bisection;
+// its low byte comes from a histogram (hist: 256 words of LDS) of the low
+// bytes of the keys in that high byte.  About 5 block-wide barriers instead
+// of 16 for a bit-by-bit search (measured: the 16 rounds of block sums set
+// the time of one query's top-K, 6-7 us at 8192 keys).
 template <int KPT, int NWAVES>
 __device__ __forceinline__ void topk_select(const uint32_t (&key)[KPT], int64_t s0, int K, int32_t offset,
-                                            int32_t* __restrict__ out, uint32_t (*red)[NWAVES], uint32_t* tot) {
-    uint32_t tau = 0;
+                                            int32_t* __restrict__ out, uint32_t (*red)[NWAVES], uint32_t* tot,
+                                            uint32_t* hist) {
+    for (int i = threadIdx.x; i < 256; i += NWAVES * 64) hist[i] = 0u;  // ordered by the next barrier
     int rb = 0;
-#pragma unroll 1
-    for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t cand = tau | (1u << bit);
+    uint32_t kmax = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) kmax = max(kmax, key[j]);
+    kmax = block_max<NWAVES>(kmax, red[rb]);
+    rb ^= 1;
+    // count of keys whose high byte is >= g (uniform)
+    auto count_ge = [&](uint32_t g) {
         uint32_t c = 0;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) c += key[j] >= cand;
-        const uint32_t total = block_sum<NWAVES>(c, red[rb]);
+        for (int j = 0; j < KPT; ++j) c += (key[j] >> 8) >= g;
+        const uint32_t t = block_sum<NWAVES>(c, red[rb]);
         rb ^= 1;
-        if (total >= (uint32_t)K) tau = cand;
+        return t;
+    };
+    uint32_t h = kmax >> 8;
+    uint32_t above = 0;  // keys whose high byte is > h
+    bool found = false;
+#pragma unroll 1
+    for (int step = 0; step < 4; ++step) {
+        const uint32_t c = count_ge(h);
+        if (c >= (uint32_t)K) {
+            found = true;
+            break;
+        }
+        above = c;
+        --h;  // h >= 1 here: count_ge(0) counts every key, which is >= K
     }
-    uint32_t gt = 0, eq = 0;
+    if (!found) {
+        // the largest g in [0, h] with count_ge(g) >= K; `above` stays the
+        // count for hi + 1
+        uint32_t lo = 0, hi = h;
+#pragma unroll 1
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            const uint32_t c = count_ge(mid);
+            if (c >= (uint32_t)K) {
+                lo = mid;
+            } else {
+                hi = mid - 1;
+                above = c;
+            }
+        }
+        h = lo;
+    }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        gt += key[j] > tau;
-        eq += key[j] == tau;
-    }
-    const uint32_t gt_total = block_sum<NWAVES>(gt, red[rb]);
-    const uint32_t need_eq = (uint32_t)K - gt_total;  // >= 1 by the choice of tau
+    for (int j = 0; j < KPT; ++j)
+        if ((key[j] >> 8) == h) atomicAdd(&hist[key[j] & 0xffu], 1u);
+    __syncthreads();
+    uint32_t lo_bin, above_lo;
+    find_bin(hist, (uint32_t)K - above, lo_bin, above_lo);
+    const uint32_t tau = (h << 8) | lo_bin;
+    uint32_t eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) eq += key[j] == tau;
+    const uint32_t need_eq = (uint32_t)K - (above + above_lo);  // keys == tau to take, >= 1
     const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
     uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
     take_eq = take_eq < eq ? take_eq : eq;
+    uint32_t gt = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) gt += key[j] > tau;
     uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
     uint32_t eq_seen = 0;
 #pragma unroll
@@ -191,33 +288,6 @@ __device__ __forceinline__ void topk_select_packed(const uint32_t (&kp_in)[KP2],
     }
 }
 
-// The bin b of a 256-bin histogram with (keys in bins above b) < k <= (keys
-// in bins b and above), and the count of keys in bins above b; every wave
-// computes the same (uniform) answer from LDS.  Needs 1 <= k <= total.
-__device__ __forceinline__ void find_bin(const uint32_t* h, uint32_t k, uint32_t& bin, uint32_t& above) {
-    const int lane = threadIdx.x & 63;
-    const u32x4 c = *reinterpret_cast<const u32x4*>(h + 4 * lane);  // bins 4 lane .. 4 lane + 3
-    const uint32_t s = c[0] + c[1] + c[2] + c[3];
-    const uint32_t incl = wave_incl_scan(s);                       // keys in bins < 4 (lane + 1)
-    const uint32_t total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    const uint32_t ge = total - incl + s;                           // keys in bins >= 4 lane
-    const uint32_t gt = ge - s;                                     // keys in bins >= 4 (lane + 1)
-    const bool mine = gt < k && ge >= k;                            // exactly one lane
-    const int L = __builtin_ctzll(__ballot(mine));
-    uint32_t b = 4 * lane, run = gt;
-    if (mine) {
-#pragma unroll
-        for (int i = 3; i >= 1; --i) {
-            if (run + c[i] >= k) {
-                b = 4 * lane + i;
-                break;
-            }
-            run += c[i];
-        }
-    }
-    bin = (uint32_t)__builtin_amdgcn_readlane((int)b, L);
-    above = (uint32_t)__builtin_amdgcn_readlane((int)run, L);
-}
 
 // topk_select for a block that already holds the histogram of its keys' high
 // bytes (hist[0..256), built while the keys were produced): the K-th largest
@@ -733,6 +803,7 @@ __device__ __forceinline__ void topk_body(const uint16_t* __restrict__ keys, int
                                                             int64_t col0, const uint32_t vb) {
     __shared__ uint32_t red[2][TOPK_THREADS / 64];
     __shared__ uint32_t tot[TOPK_THREADS / 64];
+    __shared__ uint32_t hist[256];
     const int tid = threadIdx.x;
     const int64_t qi = vb;
     const int64_t t = qi % m;
@@ -803,7 +874,7 @@ __device__ __forceinline__ void topk_body(const uint16_t* __restrict__ keys, int
         for (int j = 0; j < KPT; ++j) key[j] = (s0 + j < vis) ? (uint32_t)kp[s0 + j] : 0u;
     }
 
-    topk_select<KPT, TOPK_THREADS / 64>(key, s0, K, offset, out, red, tot);
+    topk_select<KPT, TOPK_THREADS / 64>(key, s0, K, offset, out, red, tot, hist);
 }
 
 // (host)
