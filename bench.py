@@ -374,6 +374,7 @@ def peak_lib():
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.sckv_peak_copy.argtypes = [vp, vp, i64, i32, i32, vp]
     L.sckv_peak_read.argtypes = [vp, i64, vp, i32, i32, vp]
+    L.sckv_peak_gather.argtypes = [vp, i64, vp, i64, vp, i32, i32, vp]
     L.sckv_peak_mfma.argtypes = [i32, i64, i32, vp, vp]
     L.sckv_peak_mfma_flops.argtypes = [i32, i64, i32]
     L.sckv_peak_mfma_flops.restype = ctypes.c_double
@@ -415,9 +416,19 @@ def measure_peaks():
     shapes = [(ncu * wpc, depth) for wpc in (4, 8, 16, 32) for depth in (4, 8, 16)]
     t_copy = min(best(lambda: L.sckv_peak_copy(src.data_ptr(), dst.data_ptr(), n, g, d, sp), 3) for g, d in shapes)
     t_read = min(best(lambda: L.sckv_peak_read(src.data_ptr(), 2 * n, out.data_ptr(), g, d, sp), 3) for g, d in shapes)
-    del src, dst
+    # 1 KiB rows of the 4 GiB buffer named by a seeded uniform index list of
+    # one decode step's size (2048 queries x 640 rows)
+    n_rows = 2 * n // 1024
+    n_idx = 2048 * 640
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    gidx = torch.randint(0, n_rows, (n_idx,), generator=gen, dtype=torch.int32, device="cuda")
+    t_gather = min(best(lambda: L.sckv_peak_gather(src.data_ptr(), n_rows, gidx.data_ptr(), n_idx, out.data_ptr(),
+                                                   g, d, sp), 3) for g, d in shapes)
+    del src, dst, gidx
     res = {"hbm_copy_GBs": round(2 * n / t_copy / 1e9, 1), "hbm_read_GBs": round(2 * n / t_read / 1e9, 1),
-           "copy_bytes": n, "read_bytes": 2 * n}
+           "hbm_gather_1KiB_GBs": round(n_idx * 1024 / t_gather / 1e9, 1),
+           "copy_bytes": n, "read_bytes": 2 * n, "gather_rows": n_idx}
     fo = torch.empty(ncu * 4 * 256, dtype=torch.float32, device="cuda")
     iters = 512
     for kind, name in ((0, "bf16_mfma_TFLOPs"), (1, "fp4_mfma_TFLOPs")):
@@ -428,10 +439,12 @@ def measure_peaks():
     return res
 
 
-def roofline_of(cnt, ms, peaks=None, dtype=None):
+def roofline_of(cnt, ms, peaks=None, dtype=None, gather=False):
     """Achieved rate of a call against the datasheet peak (and the measured
     one when given) of its bound: HBM bytes, or matrix-core flops of its
-    contraction's dtype (bf16, or fp4 for the packed indexer)."""
+    contraction's dtype (bf16, or fp4 for the packed indexer).  gather: the
+    call reads its rows through an index list, so it is also put against the
+    measured rate of 1 KiB row gathers."""
     if cnt["bound"] == "hbm":
         achieved = cnt["bytes"] / (ms / 1e3) / 1e9
         r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -439,6 +452,9 @@ def roofline_of(cnt, ms, peaks=None, dtype=None):
         if peaks:
             r["measured_peak"] = peaks["hbm_read_GBs"]
             r["frac_measured"] = round(achieved / peaks["hbm_read_GBs"], 4)
+            if gather and "hbm_gather_1KiB_GBs" in peaks:
+                r["measured_gather_peak"] = peaks["hbm_gather_1KiB_GBs"]
+                r["frac_of_gather_peak"] = round(achieved / peaks["hbm_gather_1KiB_GBs"], 4)
         return r
     achieved = cnt["flops"] / (ms / 1e3) / 1e12
     pk = FP4_PEAK_TFLOPS if dtype == "fp4" else BF16_PEAK_TFLOPS
@@ -548,7 +564,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
     call_info = {}
     for name, t in per_ms.items():
         cnt = counts(w, B, name, kcache, latent)
-        r = roofline_of(cnt, t, peaks, dtypes.get(name))
+        r = roofline_of(cnt, t, peaks, dtypes.get(name), gather=name.startswith("sparse_attn"))
         r.update({"ms_per_launch": round(t, 5), "algorithmic_bytes": cnt["bytes"], "algorithmic_flops": cnt["flops"],
                   "traffic": traffic_for(w.name, B, name, kc, latent)})
         if "flops_all_visible" in cnt:

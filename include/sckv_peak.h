@@ -5,7 +5,8 @@
  * Not part of the hot path: these calls re-measure, on the GPU at hand, the
  * quantities the hot path's kernels are judged against -- streaming HBM
  * bandwidth (a copy and a read-only pass over buffers far larger than the
- * last-level cache) and the dense matrix-core rate for the two contractions the
+ * last-level cache), the rate of 1 KiB row gathers (the attention's access
+ * pattern) and the dense matrix-core rate for the two contractions the
  * library runs (bf16 products, and e2m1 x e2m1 products with power-of-two block
  * scales).  The caller times them (e.g. with HIP events on `stream`).
  *
@@ -39,6 +40,18 @@ int sckv_peak_copy(const void* src, void* dst, int64_t bytes, int blocks, int de
  * dropped.  bytes a multiple of 64, src 16-byte aligned.
  */
 int sckv_peak_read(const void* src, int64_t bytes, uint32_t* out, int blocks, int depth, void* stream);
+
+/*
+ * sckv_peak_gather -- reads the 1 KiB rows rows[idx[i]] for i in [0, n_idx)
+ * (rows [n_rows][1024 bytes], 16-byte aligned; every idx[i] in [0, n_rows),
+ * which the caller guarantees: it is not checked on the device) with one
+ * 16-byte load a lane per row, each wave keeping `depth` (4, 8 or 16) rows in
+ * flight, `blocks` workgroups of 256 threads striding over the list; XOR
+ * folded per thread into out [blocks * 256].  Moves n_idx KiB from HBM when
+ * the rows are spread over far more than the last-level cache.
+ */
+int sckv_peak_gather(const void* rows, int64_t n_rows, const int32_t* idx, int64_t n_idx, uint32_t* out, int blocks,
+                     int depth, void* stream);
 
 /* Matrix-core loop kinds. */
 enum sckv_peak_mfma_kind {

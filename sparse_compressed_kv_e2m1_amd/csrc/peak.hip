@@ -1,5 +1,6 @@
 // peak.hip -- measurement kernels for the roofline denominators (C ABI in
-// include/sckv_peak.h): a streaming HBM copy, a streaming HBM read, and dense
+// include/sckv_peak.h): a streaming HBM copy, a streaming HBM read, a gather
+// of 1 KiB rows through an index list (the attention's access pattern), and dense
 // matrix-core loops for the two contractions of the hot path (bf16 products;
 // e2m1 x e2m1 products with power-of-two block scales).  Not part of the hot
 // path; built into libsckv_peak.so.
@@ -63,6 +64,30 @@ __global__ __launch_bounds__(THREADS) void peak_read_kernel(const u32x4* __restr
         for (int j = 0; j < DEPTH; ++j) x ^= v[j];
     }
     for (; i < n16; i += nt) x ^= src[i];
+    out[(int64_t)blockIdx.x * THREADS + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+// Gather of 1 KiB rows named by an index list: each wave takes DEPTH
+// consecutive list entries at a time (grid-strided) and reads those rows with
+// one 16-byte load a lane per row, XOR folded per thread.
+template <int DEPTH>
+__global__ __launch_bounds__(THREADS) void peak_gather_kernel(const u32x4* __restrict__ rows,
+                                                              const int32_t* __restrict__ idx, int64_t n_idx,
+                                                              uint32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t nw = (int64_t)gridDim.x * (THREADS / 64);
+    int64_t e = ((int64_t)blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6)) * DEPTH;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    for (; e < n_idx; e += nw * DEPTH) {
+        u32x4 v[DEPTH];
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) {
+            const int64_t r = e + j < n_idx ? idx[e + j] : idx[e];
+            v[j] = rows[r * 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < DEPTH; ++j) x ^= v[j];
+    }
     out[(int64_t)blockIdx.x * THREADS + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
@@ -143,6 +168,21 @@ extern "C" int sckv_peak_read(const void* src, int64_t bytes, uint32_t* out, int
     else if (depth == 8) peak_read_kernel<8><<<g, t, 0, s>>>(a, bytes / 16, out);
     else peak_read_kernel<16><<<g, t, 0, s>>>(a, bytes / 16, out);
     return launched("sckv_peak_read");
+}
+
+extern "C" int sckv_peak_gather(const void* rows, int64_t n_rows, const int32_t* idx, int64_t n_idx, uint32_t* out,
+                                int blocks, int depth, void* stream) {
+    if (n_rows <= 0 || n_idx < 0 || blocks <= 0 || !rows || !idx || !out || (uintptr_t)rows % 16 ||
+        (uintptr_t)idx % 4 || (uintptr_t)out % 4 || (depth != 4 && depth != 8 && depth != 16))
+        return fail(SCKV_EINVAL, "sckv_peak_gather: bad arguments");
+    if (n_idx == 0) return SCKV_OK;
+    const dim3 g((unsigned)blocks), t(THREADS);
+    hipStream_t s = (hipStream_t)stream;
+    const u32x4* a = (const u32x4*)rows;
+    if (depth == 4) peak_gather_kernel<4><<<g, t, 0, s>>>(a, idx, n_idx, out);
+    else if (depth == 8) peak_gather_kernel<8><<<g, t, 0, s>>>(a, idx, n_idx, out);
+    else peak_gather_kernel<16><<<g, t, 0, s>>>(a, idx, n_idx, out);
+    return launched("sckv_peak_gather");
 }
 
 extern "C" double sckv_peak_mfma_flops(int kind, int64_t iters, int blocks) {

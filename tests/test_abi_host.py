@@ -42,7 +42,8 @@ def test_peak_library_exports_every_declared_call():
     their own, declared in include/sckv_peak.h."""
     peak = ctypes.CDLL(os.path.join(ROOT, "sparse_compressed_kv_e2m1_amd", "libsckv_peak.so"))
     names = declared_calls("sckv_peak.h")
-    assert {"sckv_peak_copy", "sckv_peak_read", "sckv_peak_mfma", "sckv_peak_mfma_flops"} <= set(names)
+    assert {"sckv_peak_copy", "sckv_peak_read", "sckv_peak_gather", "sckv_peak_mfma",
+            "sckv_peak_mfma_flops"} <= set(names)
     for n in names:
         assert hasattr(peak, n), n
     peak.sckv_peak_mfma_flops.restype = ctypes.c_double
@@ -53,6 +54,12 @@ def test_peak_library_exports_every_declared_call():
                                     ctypes.c_void_p]
     assert peak.sckv_peak_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 63, 1, 4, None) == -1  # size
     assert peak.sckv_peak_copy(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), 64, 1, 5, None) == -1  # depth
+    peak.sckv_peak_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                                      ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    a, i, o = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000), ctypes.c_void_p(0x3000)
+    assert peak.sckv_peak_gather(a, 0, i, 8, o, 1, 4, None) == -1  # no rows
+    assert peak.sckv_peak_gather(a, 16, i, 8, o, 1, 3, None) == -1  # depth
+    assert peak.sckv_peak_gather(ctypes.c_void_p(0x1008), 16, i, 8, o, 1, 4, None) == -1  # misaligned rows
 
 
 def test_header_compiles_as_c():
