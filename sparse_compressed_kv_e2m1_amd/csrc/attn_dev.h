@@ -67,9 +67,16 @@ struct AttnShape {
 // v_permlane32_swap: with both operands v, the pair returned is (v of the
 // lower lane, v of the upper lane) of {l, l^16} or {l, l^32}), so every lane
 // of a group adds the same two values in the same order
+// (v_max_f32 written out: the values are never NaN, and fmaxf would first
+// canonicalize both operands, two more instructions)
+__device__ __forceinline__ float max_nn(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 __device__ __forceinline__ float pair_max16(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum16(float v) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -77,7 +84,7 @@ __device__ __forceinline__ float pair_sum16(float v) {
 }
 __device__ __forceinline__ float pair_max32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_nn(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum32(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -421,30 +428,36 @@ __device__ __forceinline__ void sparse_attn_body(
                         __builtin_amdgcn_sched_group_barrier(0x008, SA, 0);
                     }
                     float x[8];
+#pragma unroll
+                    for (int k8 = 0; k8 < 8; ++k8) x[k8] = sp[k8 >> 2][k8 & 3] * scale_log2;
+                    if (mask != 0xffffffffu) {
+                        // rows that name no valid entry (chunks at the ends of a
+                        // list only) drop out of the softmax
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (!((mask >> (mt * 16 + g * 4 + i)) & 1u)) x[mt * 4 + i] = -INFINITY;
+                    }
                     float cmax = -INFINITY;
 #pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int r = mt * 16 + g * 4 + i;
-                            const float v = ((mask >> r) & 1u) ? sp[mt][i] * scale_log2 : -INFINITY;
-                            x[mt * 4 + i] = v;
-                            cmax = fmaxf(cmax, v);
-                        }
+                    for (int k8 = 0; k8 < 8; ++k8) cmax = fmaxf(cmax, x[k8]);
                     cmax = max4x16(cmax);
                     const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
                     alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     float psum = 0.0f;
                     uint32_t pk[4];
+                    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
                     for (int j2 = 0; j2 < 4; ++j2) {
                         // hardware exp2 (v_exp_f32) and round-to-nearest-even pack to
-                        // bf16 (v_cvt_pk_bf16_f32); the sum uses the rounded weights
+                        // bf16 (v_cvt_pk_bf16_f32); the sum uses the rounded weights,
+                        // two at a time through the bf16 dot product with (1, 1)
                         const f32x2 pf = {__builtin_amdgcn_exp2f(x[2 * j2] - m_new),
                                           __builtin_amdgcn_exp2f(x[2 * j2 + 1] - m_new)};
-                        const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pf, bf16x2));
-                        psum += __uint_as_float(pb << 16) + __uint_as_float(pb & 0xffff0000u);
-                        pk[j2] = pb;
+                        const bf16x2 pbv = __builtin_convertvector(pf, bf16x2);
+                        psum = __builtin_amdgcn_fdot2_f32_bf16(pbv, ones, psum, false);
+                        pk[j2] = __builtin_bit_cast(uint32_t, pbv);
                     }
                     l_run = l_run * alpha + sum4x16(psum);
                     const bool moved = __ballot(m_new != m_run) != 0;
