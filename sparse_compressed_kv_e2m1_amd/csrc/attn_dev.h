@@ -481,8 +481,10 @@ __device__ __forceinline__ void sparse_attn_body(
             if (CS && it < n_own) {
                 // column split: after every wave has published its
                 // probabilities, wave hw accumulates O for all 64 heads over
-                // columns 128 hw .. 128 hw + 127 (accumulator 8 hg + ct: heads
-                // 16 hg + g*4 + i, columns 128 hw + 16 ct + l16)
+                // columns 128 hw .. 128 hw + 127, transposed (O^T = R^T . P^T,
+                // the same operand registers in swapped roles): accumulator
+                // 8 hg + ct holds head 16 hg + l16, columns 128 hw + 16 ct +
+                // g*4 + i, four consecutive columns of one head a lane
                 __syncthreads();
                 const uint32_t mv = *reinterpret_cast<const uint32_t*>(lds + S::OFF_MOVED);
                 if (mv) {  // rare: rescale the head groups whose running max moved
@@ -490,13 +492,11 @@ __device__ __forceinline__ void sparse_attn_body(
 #pragma unroll
                     for (int hg = 0; hg < NHW; ++hg) {
                         if (((mv >> (8 * hg)) & 0xffu) == 0) continue;
-                        float a4[4];
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) a4[i] = al[16 * hg + g * 4 + i];
+                        const float a1 = al[16 * hg + l16];
 #pragma unroll
                         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) o[hg * 8 + ct][i] *= a4[i];
+                            for (int i = 0; i < 4; ++i) o[hg * 8 + ct][i] *= a1;
                     }
                 }
                 bf16x8 pall[NHW];
@@ -513,7 +513,7 @@ __device__ __forceinline__ void sparse_attn_body(
                     const bf16x8 bv =
                         __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-                    for (int hg = 0; hg < NHW; ++hg) o[hg * 8 + ct] = mfma16x16x32(pall[hg], bv, o[hg * 8 + ct]);
+                    for (int hg = 0; hg < NHW; ++hg) o[hg * 8 + ct] = mfma16x16x32(bv, pall[hg], o[hg * 8 + ct]);
                 }
             } else if (it < n_own) {
                 // O[heads, :] += P . R: k = g*8 + 0..3 are rows g*4 + 0..3, k = g*8 + 4..7
@@ -550,9 +550,10 @@ __device__ __forceinline__ void sparse_attn_body(
 
     if constexpr (CS) {
         // ---- epilogue, column split: 1/sum of each head from its owner
-        // wave, then each wave normalizes its 64 heads x 128 columns and
-        // writes them through its own staging rows (bf16, 256 bytes a row,
-        // 16-byte pieces swizzled by the row) as 16-byte pieces
+        // wave, then each wave normalizes its 64 heads x 128 columns into
+        // its own staging rows (bf16, 256 bytes a row, 16-byte pieces
+        // swizzled by the row; a lane's four columns of one head as 8
+        // bytes) and writes them out as 16-byte pieces
         __syncthreads();  // all stages idle
         float* il = reinterpret_cast<float*>(lds + S::OFF_ALPHA);
         if (g == 0) il[16 * hw + l16] = 1.0f / l_run;
@@ -560,25 +561,19 @@ __device__ __forceinline__ void sparse_attn_body(
         constexpr int PR = (D / NHW) * 2;  // bytes of a staged row (128 columns)
         constexpr int NPC = PR / 16;       // 16-byte pieces a row
         unsigned char* stg = lds + (size_t)wave * (S::HP * PR);
-        const bool odd = (l16 & 1) != 0;
 #pragma unroll
         for (int hg = 0; hg < NHW; ++hg) {
-            float fin[4];
+            const int r = 16 * hg + l16;
+            const float fin = il[r];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fin[i] = il[16 * hg + g * 4 + i];
-#pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; i += 2) {
-                    const float a = o[hg * 8 + ct][i] * fin[i], b2 = o[hg * 8 + ct][i + 1] * fin[i + 1];
-                    const float other = lane_xor1(odd ? a : b2);
-                    const f32x2 pr = odd ? f32x2{other, b2} : f32x2{a, other};
-                    const uint32_t pb = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-                    const int r = 16 * hg + g * 4 + i + (odd ? 1 : 0);
-                    const int c = ct * 16 + (l16 & ~1);  // column within the wave's 128
-                    const int pc = (c >> 3) ^ (r % NPC);
-                    *reinterpret_cast<uint32_t*>(stg + r * PR + pc * 16 + (c & 7) * 2) = pb;
-                }
+            for (int ct = 0; ct < 8; ++ct) {
+                const f32x4 v = o[hg * 8 + ct];
+                const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[0] * fin, v[1] * fin}, bf16x2));
+                const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2] * fin, v[3] * fin}, bf16x2));
+                const int c = ct * 16 + g * 4;  // column within the wave's 128
+                const int pc = (c >> 3) ^ (r % NPC);
+                *reinterpret_cast<uint2*>(stg + r * PR + pc * 16 + (c & 7) * 2) = uint2{lo, hi};
+            }
         }
         wave_lds_sync();
 #pragma unroll
