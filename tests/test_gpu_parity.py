@@ -685,6 +685,10 @@ ATTN_CASES = [
     (300, 1, 64, 512, 128, 200, 64, 0.1),    # many queries: no split
     (2, 2, 40, 512, 60, 90, 200, 0.2),       # 33..63 heads at D = 512: padded second head group
     (260, 1, 48, 512, 128, 300, 130, 0.1),   # the same, unsplit
+    # at 64 queries or fewer the heads split into 16-head workgroups
+    (1, 1, 64, 128, 64, 500, 300, 0.1),      # four head groups, D = 128
+    (3, 1, 64, 64, 32, 100, 96, 0.0),        # D = 64, three chunks
+    (1, 1, 56, 512, 128, 2000, 1000, 0.2),   # last group of 8 heads, 32 chunks
 ]
 
 
