@@ -505,6 +505,8 @@ FP4_CASES = [
     # 16-byte group of keys; n_c not a multiple of 8
     (200, 2, 64, 128, 20000, 4, 79990, 1500, False),
     (192, 1, 64, 128, 20004, 1, 20003, 700, False),
+    # fused, 64 keys a thread, keys in the workspace at an odd row stride
+    (192, 1, 64, 128, 20001, 1, 20000, 900, False),
 ]
 
 
