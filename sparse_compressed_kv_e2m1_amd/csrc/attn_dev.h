@@ -429,7 +429,7 @@ __device__ __forceinline__ void sparse_attn_body(
                     }
                     float x[8];
 #pragma unroll
-                    for (int k8 = 0; k8 < 8; ++k8) x[k8] = sp[k8 >> 2][k8 & 3] * scale_log2;
+                    for (int k8 = 0; k8 < 8; ++k8) x[k8] = sp[k8 >> 2][k8 & 3];  // raw products
                     if (mask != 0xffffffffu) {
                         // rows that name no valid entry (chunks at the ends of a
                         // list only) drop out of the softmax
@@ -442,7 +442,9 @@ __device__ __forceinline__ void sparse_attn_body(
                     float cmax = -INFINITY;
 #pragma unroll
                     for (int k8 = 0; k8 < 8; ++k8) cmax = fmaxf(cmax, x[k8]);
-                    cmax = max4x16(cmax);
+                    // (the scale is positive and rounding is monotone, so this is
+                    // exactly the largest scaled logit)
+                    cmax = max4x16(cmax) * scale_log2;
                     const float m_new = (cmax > m_run + STALE_MAX) ? cmax : m_run;
                     alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                     float psum = 0.0f;
@@ -453,8 +455,9 @@ __device__ __forceinline__ void sparse_attn_body(
                         // hardware exp2 (v_exp_f32) and round-to-nearest-even pack to
                         // bf16 (v_cvt_pk_bf16_f32); the sum uses the rounded weights,
                         // two at a time through the bf16 dot product with (1, 1)
-                        const f32x2 pf = {__builtin_amdgcn_exp2f(x[2 * j2] - m_new),
-                                          __builtin_amdgcn_exp2f(x[2 * j2 + 1] - m_new)};
+                        // (the logit scale and the max in one multiply-add)
+                        const f32x2 pf = {__builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j2], scale_log2, -m_new)),
+                                          __builtin_amdgcn_exp2f(__builtin_fmaf(x[2 * j2 + 1], scale_log2, -m_new))};
                         const bf16x2 pbv = __builtin_convertvector(pf, bf16x2);
                         psum = __builtin_amdgcn_fdot2_f32_bf16(pbv, ones, psum, false);
                         pk[j2] = __builtin_bit_cast(uint32_t, pbv);
