@@ -42,7 +42,13 @@
 // its 16 heads' probabilities (and, when its running max moved, the rescale
 // factors) in LDS, and after one more barrier every wave accumulates O for
 // all 64 heads over its own 128 columns, which reads each row byte once per
-// wave instead of once per head group.
+// wave instead of once per head group.  It accumulates O transposed (the
+// same operands in swapped roles), so a lane ends with four consecutive
+// columns of one head and packs them without lane shuffles.
+//
+// Few queries (at most 64): the heads split too, into workgroups of 16 heads
+// (grid y), over chunk ranges of at least two chunks, so that one sequence's
+// attention spreads over ~40 workgroups with one round of row copies each.
 #include <mutex>
 #include <string>
 
