@@ -766,6 +766,21 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
     float* colsum = red + 2 * (NTH / 64);       // [groups][D]
     colsum = reinterpret_cast<float*>((reinterpret_cast<uintptr_t>(colsum) + 15) & ~(uintptr_t)15);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    static_assert(NTH >= 256 && NTH % 64 == 0, "combine workgroup");
+    const int per = D / 4;            // threads of a split group (4 columns each)
+    const int groups = 1024 / D;      // split groups
+    const int grp = tid / per, c4 = tid - grp * per;
+    // this thread's splits are grp, grp + groups, ...: the first PRE of them
+    // are requested before the weights are known (one memory round trip
+    // instead of two), the rest where they are summed
+    constexpr int PRE = 8;
+    const int n_own = grp < groups && grp < nsplit ? (nsplit - grp + groups - 1) / groups : 0;
+    const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (qi * nsplit * H + h) * (int64_t)D) + c4;
+    const int64_t stride4 = (int64_t)H * D / 4;  // one split further
+    f32x4 pv[PRE];
+#pragma unroll
+    for (int kk = 0; kk < PRE; ++kk)
+        pv[kk] = kk < n_own ? po[(grp + kk * groups) * stride4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const float s2 = sink[h] * LOG2E;
     const float* ml = part_ml + (qi * nsplit * H + h) * 2;  // split j at ml[j * H * 2]
     float mx = s2;
@@ -786,15 +801,27 @@ __device__ __forceinline__ void combine_body(const float* __restrict__ part_o, c
     __syncthreads();
     float Z = exp2f(s2 - M);
     for (int i = 0; i < NTH / 64; ++i) Z += red[NTH / 64 + i];
-    static_assert(NTH >= 256 && NTH % 64 == 0, "combine workgroup");
-    const int per = D / 4;            // threads of a split group (4 columns each)
-    const int groups = 1024 / D;      // split groups
-    const int grp = tid / per, c4 = tid - grp * per;
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     if (grp < groups) {
-        const f32x4* po = reinterpret_cast<const f32x4*>(part_o + (qi * nsplit * H + h) * (int64_t)D) + c4;
-        const int64_t stride4 = (int64_t)H * D / 4;  // one split further
-        int j = grp;
+        // the sums in a fixed order: fours of splits while four remain, then
+        // one at a time (the preloaded ones first, in the same order)
+        int k = 0;
+#pragma unroll
+        for (int qd = 0; qd < PRE / 4; ++qd) {
+            if (k == 4 * qd && 4 * qd + 3 < n_own) {
+                const int j = grp + 4 * qd * groups;
+                acc += pv[4 * qd] * wj[j] + pv[4 * qd + 1] * wj[j + groups] + pv[4 * qd + 2] * wj[j + 2 * groups] +
+                       pv[4 * qd + 3] * wj[j + 3 * groups];
+                k += 4;
+            }
+        }
+        if (k < PRE) {  // the fours ended inside the preloaded splits: so do all of them
+#pragma unroll
+            for (int kk = 0; kk < PRE; ++kk)
+                if (kk >= k && kk < n_own) acc += pv[kk] * wj[grp + kk * groups];
+            k = n_own;
+        }
+        int j = grp + k * groups;
         for (; j + 3 * groups < nsplit; j += 4 * groups) {  // four loads in flight
             const f32x4 v0 = po[j * stride4], v1 = po[(j + groups) * stride4];
             const f32x4 v2 = po[(j + 2 * groups) * stride4], v3 = po[(j + 3 * groups) * stride4];
