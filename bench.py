@@ -83,6 +83,10 @@ def counts(w, B, call, kcache="bf16", latent="bf16"):
                 "flops": 0, "bound": "hbm"}
     if call == "visible_idx":
         return {"bytes": B * m * w.K * 4, "flops": 0, "bound": "hbm"}
+    if call == "prefill_prepare":  # the set-up calls of a step that is not a decode step, in one launch
+        parts = ["quant_latent"] + (["quant_index_k", "window_idx"] if w.Hi else ["window_idx", "visible_idx"])
+        parts += ["ring_write"] if w.start_pos == 0 else []
+        return {"bytes": sum(counts(w, B, c, kcache, latent)["bytes"] for c in parts), "flops": 0, "bound": "hbm"}
     if call == "index_scores_topk":
         # flops: only queries that see more than K rows need scores (a query
         # seeing V <= K rows selects all of them); the all-visible-pairs count
@@ -135,9 +139,10 @@ def traffic_for(workload, B, call, kcache, latent="bf16"):
 # Library call -> the kernels it launches (demangled-name prefixes).
 CALL_KERNELS = {
     "quant_latent": ["quant_rows_kernel<0,", "quant_pack_kernel<0,"],
-    "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1>"],
+    "quant_index_k": ["quant_rows_kernel<1,", "quant_pack_kernel<1,"],
     "ring_write": ["ring_write_kernel"],
     "decode_prepare": ["decode_prepare_kernel"],
+    "prefill_prepare": ["prefill_prepare_kernel"],
     "decode_step": ["decode_step_kernel"],
     "window_idx": ["window_idx_kernel"],
     "visible_idx": ["visible_idx_kernel"],
@@ -470,7 +475,7 @@ def roofline_of(cnt, ms, peaks=None, dtype=None, gather=False):
 
 
 def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, latent="bf16",
-            decode_launch="separate"):
+            decode_launch="separate", prepare="one"):
     """Time whole steps of workload w over B sequences (inputs drawn on the
     device, resident before the timed region), then each library call with
     events around it on the same stream; optionally the B = 1 latency."""
@@ -485,7 +490,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
     stream = torch.cuda.current_stream()
     if single and B > 1:
         x1 = synth.make_inputs(w, 1, device="cuda")
-        s1 = PathState(w, x1, 1, kcache=kcache, latent=latent, decode_launch=decode_launch)
+        s1 = PathState(w, x1, 1, kcache=kcache, latent=latent, decode_launch=decode_launch, prepare=prepare)
         s1.setup()
         for _ in range(warmup):
             s1.step()
@@ -517,7 +522,7 @@ def run_leg(w, B, kcache, steps, warmup, single=True, graph=False, peaks=None, l
 
     log(f"bench: workload {w.name} B={B}: generating inputs on the device")
     x = synth.make_inputs(w, B, device="cuda")
-    st = PathState(w, x, B, kcache=kcache, latent=latent, decode_launch=decode_launch)
+    st = PathState(w, x, B, kcache=kcache, latent=latent, decode_launch=decode_launch, prepare=prepare)
     del x
     st.setup()
     calls = st.calls()
@@ -597,6 +602,9 @@ def main():
     ap.add_argument("--decode-launch", choices=["separate", "one"], default="separate",
                     help="decode steps: the separate calls (default), or the one cooperative launch "
                          "sckv_decode_step for small batches")
+    ap.add_argument("--prepare", choices=["one", "separate"], default="one",
+                    help="set-up of steps that are not decode steps: the one launch sckv_prefill_prepare "
+                         "(default) or its separate calls")
     ap.add_argument("--legs", default="long_decode,causal_prefill,chunked_prefill",
                     help="other workloads timed in the same run and reported under 'legs' (comma list; '' = none)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per thread count")
@@ -649,12 +657,13 @@ def main():
     w = synth.WORKLOADS[args.workload]
     B = args.instances or DEFAULT_B[args.workload]
     head = run_leg(w, B, args.kcache, args.steps, args.warmup, single=not args.no_single, graph=args.graph,
-                   peaks=peaks, latent=args.latent, decode_launch=args.decode_launch)
+                   peaks=peaks, latent=args.latent, decode_launch=args.decode_launch, prepare=args.prepare)
     legs = {}
     for name in [n for n in args.legs.split(",") if n and n != w.name]:
         lw = synth.WORKLOADS[name]
         legs[name] = run_leg(lw, DEFAULT_B[name], args.kcache, args.steps, args.warmup, single=False,
-                             graph=args.graph, peaks=peaks, latent=args.latent, decode_launch=args.decode_launch)
+                             graph=args.graph, peaks=peaks, latent=args.latent, decode_launch=args.decode_launch,
+                             prepare=args.prepare)
 
     line = {
         "metric": "sparse-attn tokens/s (decode & prefill) + % of HBM/MFMA roofline, 1 MI355X",

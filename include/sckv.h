@@ -238,6 +238,56 @@ int sckv_decode_prepare(const void* lat_new, int64_t ld_lat_new, void* lat_dst, 
                         int64_t ld_lat_codes, void* lat_scales, int64_t ld_lat_scales, void* stream);
 
 /*
+ * sckv_prefill_prepare -- the set-up calls of a step of m >= 1 queries for B
+ * sequences in one launch (forward.rs AttnV41::forward: the fp4 round trip of
+ * the completed latent groups before their cache copy, window_topk_idxs,
+ * compress_len = (start_pos + m) / ratio, the ring's stream-ordered copies;
+ * compress.rs fp4_quant_e4m3_inplace, fp4_quant_e8m0_inplace and the rotation
+ * of a new latent group before its round trip).  The result is exactly that
+ * of, in any order (the parts read only these inputs and write disjoint
+ * memory), for every sequence b (X_b = X + b * bs_X):
+ *   sckv_rope_quant_rows(lat_new_b, D, lat_dst_b, D, n_new, D, rope_table,
+ *       n_pos, rope_dim, pos0, pos_step)           (latent rows, bf16 out)
+ *     or sckv_rope_quant_pack(lat_new_b, D, lat_codes_b, D/2, lat_scales_b,
+ *       D/16, n_new, D, ...)                        (latent rows, packed)
+ *     (sckv_quant_rows / sckv_quant_pack in SCKV_FP4_E4M3_B16 when
+ *     rope_table is NULL)
+ *   sckv_quant_rows(k_new_b, Di, k_dst_b, Di, n_new, Di, SCKV_FP4_E8M0_B32)
+ *     or sckv_quant_pack(k_new_b, Di, k_codes_b, Di/2, k_scales_b, Di/32,
+ *       n_new, Di, SCKV_FP4_E8M0_B32)
+ *   sckv_window_idx(B, m, start_pos, win, idx, ld_idx)
+ *   sckv_visible_idx(B, m, start_pos, ratio, n_c, K, offset, idx, ld_idx, win)
+ *     (only when K > 0)
+ *   sckv_ring_write(ring_src, bs_ring_src, ring, bs_ring, B, m, start_pos,
+ *       win, D)                                      (only when ring_src is given)
+ * Every row set is contiguous within a sequence (row stride = row length);
+ * the batch strides bs_* count elements for bf16 rows and bytes for codes
+ * and scales.
+ *   lat_new    [B, n_new, D] raw latent rows, or NULL (or n_new = 0): no
+ *              latent part; give lat_dst ([B] x n_new bf16 rows, e.g. the
+ *              cache's first new row) or lat_codes + lat_scales, not both
+ *   k_new      [B, n_new, Di] raw indexer k rows, or NULL: no k part; give
+ *              k_dst or k_codes + k_scales, not both
+ *   ring_src   [B, m, D] the step's kv rows, or NULL: no ring write.  The
+ *              ring is written in this launch, so give it only when nothing
+ *              later in the step reads the ring's earlier rows (a step from
+ *              position 0); a chunk's ring write follows its attention
+ *   idx        [B, m, ld_idx] int32, ld_idx >= win + K
+ * Sources and destinations must not overlap (no in-place round trip).
+ * D % 16 == 0, Di % 32 == 0; bf16 rows and k codes 16-byte aligned, latent
+ * codes 8-byte aligned, batch strides multiples of 16 bytes (8 for latent
+ * codes, scales any), else SCKV_EINVAL; the checks of the separate calls
+ * (rotation table, K >= every visible count) apply.
+ */
+int sckv_prefill_prepare(int B, int64_t m, int64_t start_pos, int win, int D, int64_t n_new, const void* lat_new,
+                         int64_t bs_lat_new, void* lat_dst, int64_t bs_lat_dst, void* lat_codes, int64_t bs_lat_codes,
+                         void* lat_scales, int64_t bs_lat_scales, const float* rope_table, int64_t n_pos,
+                         int rope_dim, int64_t pos0, int64_t pos_step, const void* k_new, int64_t bs_k_new, int Di,
+                         void* k_dst, int64_t bs_k_dst, void* k_codes, int64_t bs_k_codes, void* k_scales,
+                         int64_t bs_k_scales, const void* ring_src, int64_t bs_ring_src, void* ring, int64_t bs_ring,
+                         int32_t* idx, int64_t ld_idx, int ratio, int64_t n_c, int K, int32_t offset, void* stream);
+
+/*
  * sckv_decode_step -- a whole decode step (m = 1 at start_pos > 0) of B <= 64
  * sequences in ONE launch (forward.rs AttnV41::forward: ring copy, window
  * list, indexer, merge, attend_and_project; compress.rs: the round trips, the

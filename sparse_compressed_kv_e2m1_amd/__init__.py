@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     sckv_index_scores_topk,
     sckv_index_scores_topk_fp4,
     sckv_last_error,
+    sckv_prefill_prepare,
     sckv_quant,
     sckv_quant_pack,
     sckv_quant_rows,

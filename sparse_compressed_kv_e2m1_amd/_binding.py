@@ -46,6 +46,9 @@ def _load():
     L.sckv_ring_write.argtypes = [vp, i64, vp, i64, i32, i64, i64, i32, i32, vp]
     L.sckv_decode_prepare.argtypes = [vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32, vp, i64, vp, i64, i32, i32,
                                       i32, i64, vp, i64, vp, i64, i32, i64, vp, i64, vp, i64, vp]
+    L.sckv_prefill_prepare.argtypes = [i32, i64, i64, i32, i32, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, i32,
+                                       i64, i64, vp, i64, i32, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64,
+                                       i32, i64, i32, ctypes.c_int32, vp]
     L.sckv_rope_quant_pack.argtypes = [vp, i64, vp, i64, vp, i64, i64, i64, vp, i64, i32, i64, i64, vp]
     L.sckv_yarn_freqs_cis.argtypes = [vp, i32, i64, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                       ctypes.c_float]
@@ -76,6 +79,7 @@ def _load():
     L.sckv_last_error.restype = ctypes.c_char_p
     L.sckv_abi_version.argtypes = []
     for name in ("sckv_quant", "sckv_quant_rows", "sckv_quant_pack", "sckv_ring_write", "sckv_decode_prepare",
+                 "sckv_prefill_prepare",
                  "sckv_window_idx",
                  "sckv_visible_idx", "sckv_index_scores_topk", "sckv_index_scores_topk_fp4", "sckv_sparse_attn_sink",
                  "sckv_abi_version"):
@@ -191,6 +195,31 @@ def sckv_decode_prepare(lat_new, ld_lat_new: int, lat_dst, ld_lat_dst: int, k_ne
         p(rope_table, torch.float32, "rope_table"), 0 if rope_table is None else rope_table.shape[0], rope_dim,
         lat_pos, p(lat_codes, torch.uint8, "lat_codes"), ld_lat_codes, p(lat_scales, torch.uint8, "lat_scales"),
         ld_lat_scales, _stream(stream)))
+
+
+def sckv_prefill_prepare(B: int, m: int, start_pos: int, win: int, D: int, n_new: int, lat_new, bs_lat_new: int,
+                         lat_dst, bs_lat_dst: int, lat_codes, bs_lat_codes: int, lat_scales, bs_lat_scales: int,
+                         rope_table, rope_dim: int, pos0: int, pos_step: int, k_new, bs_k_new: int, Di: int, k_dst,
+                         bs_k_dst: int, k_codes, bs_k_codes: int, k_scales, bs_k_scales: int, ring_src,
+                         bs_ring_src: int, ring, bs_ring: int, idx: torch.Tensor, ld_idx: int, ratio: int = 1,
+                         n_c: int = 0, K: int = 0, offset: int = 0, stream=None):
+    """Row arguments: device tensors whose data pointers start sequence 0's
+    first row (any of the optional parts may be None); rope_table is the
+    [n_pos, rope_dim/2, 2] f32 device table or None."""
+    def p(t, dtype, name):
+        if t is None:
+            return None
+        if not t.is_cuda or t.dtype != dtype:
+            raise ValueError(f"{name}: expected a {dtype} device tensor")
+        return t.data_ptr()
+    bf, u8 = torch.bfloat16, torch.uint8
+    _check("sckv_prefill_prepare", lib.sckv_prefill_prepare(
+        B, m, start_pos, win, D, n_new, p(lat_new, bf, "lat_new"), bs_lat_new, p(lat_dst, bf, "lat_dst"), bs_lat_dst,
+        p(lat_codes, u8, "lat_codes"), bs_lat_codes, p(lat_scales, u8, "lat_scales"), bs_lat_scales,
+        p(rope_table, torch.float32, "rope_table"), 0 if rope_table is None else rope_table.shape[0], rope_dim, pos0,
+        pos_step, p(k_new, bf, "k_new"), bs_k_new, Di, p(k_dst, bf, "k_dst"), bs_k_dst, p(k_codes, u8, "k_codes"),
+        bs_k_codes, p(k_scales, u8, "k_scales"), bs_k_scales, p(ring_src, bf, "ring_src"), bs_ring_src,
+        p(ring, bf, "ring"), bs_ring, p(idx, torch.int32, "idx"), ld_idx, ratio, n_c, K, offset, _stream(stream)))
 
 
 def sckv_yarn_freqs_cis(dim: int, seqlen: int, original_seq_len: int, base: float, factor: float, beta_fast: float,

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsckv.so")
-SOURCES = ["abi.hip", "quant.hip", "rope.hip", "window.hip", "decode.hip", "indexer.hip", "attn.hip", "decode_step.hip"]
+SOURCES = ["abi.hip", "quant.hip", "rope.hip", "window.hip", "decode.hip", "prefill.hip", "indexer.hip", "attn.hip", "decode_step.hip"]
 # measurement kernels for the roofline denominators (not the hot path): a library of their own
 PEAK_LIB = os.path.join(HERE, "libsckv_peak.so")
 PEAK_SOURCES = ["peak.hip"]

@@ -115,11 +115,8 @@ __device__ __forceinline__ void decode_prepare_body(const PrepArgs& a, const int
     // window columns of the query at p = start_pos: the n_w = min(win, p + 1)
     // newest positions, oldest first, then -1
     {
-        const int64_t p = a.start_pos;
-        const int64_t n_w = (p + 1 < a.win) ? (p + 1) : a.win;
         int32_t* row = a.idx + b * a.ld_idx;
-        for (int j = t; j < a.win; j += PREP_THREADS)
-            row[j] = (j < n_w) ? (int32_t)window_row(a.win, 1, p, p - n_w + 1 + j) : -1;
+        for (int j = t; j < a.win; j += PREP_THREADS) row[j] = window_col(a.win, 1, a.start_pos, 0, j);
     }
 }
 

@@ -224,6 +224,25 @@ __device__ __forceinline__ int64_t window_row(int win, int64_t m, int64_t start_
     return (q < start_pos) ? (q % win) : (win + (q - start_pos));
 }
 
+// Column j of query t's window part of the index list: the j-th oldest of the
+// n_w = min(win, p + 1) positions ending at p = start_pos + t, as its row in
+// rows_a, then -1 (forward.rs window_topk_idxs; reading in sckv_window_idx).
+__device__ __forceinline__ int32_t window_col(int win, int64_t m, int64_t start_pos, int64_t t, int j) {
+    const int64_t p = start_pos + t;
+    const int64_t n_w = (p + 1 < win) ? (p + 1) : win;
+    return (j < n_w) ? (int32_t)window_row(win, m, start_pos, p - n_w + 1 + j) : -1;
+}
+
+// Column j of query t's compressed part on a layer without an indexer:
+// offset + j for the V_p = min(n_c, (p + 1) / ratio) visible compressed rows,
+// then -1.
+__device__ __forceinline__ int32_t visible_col(int64_t start_pos, int ratio, int64_t n_c, int32_t offset, int64_t t,
+                                               int j) {
+    int64_t v = (start_pos + t + 1) / ratio;
+    v = v < n_c ? v : n_c;
+    return (j < v) ? (int32_t)(offset + j) : -1;
+}
+
 // ---------------------------------------------------------------- host side
 
 void set_error(const std::string& msg);

@@ -34,23 +34,17 @@ __global__ __launch_bounds__(RING_THREADS) void ring_write_kernel(const uint16_t
     (void)m;
 }
 
-// idx[b, t, j] for j < win: the j-th oldest of the n_w = min(win, p + 1)
-// positions ending at p = start_pos + t, then -1.
+// idx[b, t, j] for j < win: window_col.
 __global__ __launch_bounds__(IDX_THREADS) void window_idx_kernel(int64_t m, int64_t start_pos, int win,
                                                                  int32_t* __restrict__ idx, int64_t ld) {
     const int64_t gid = (int64_t)blockIdx.x * IDX_THREADS + threadIdx.x;
     const int64_t t = gid / win;
     const int j = (int)(gid - t * win);
     if (t >= m) return;
-    const int64_t p = start_pos + t;
-    const int64_t n_w = (p + 1 < win) ? (p + 1) : win;
-    int32_t v = -1;
-    if (j < n_w) v = (int32_t)window_row(win, m, start_pos, p - n_w + 1 + j);
-    idx[(int64_t)blockIdx.y * m * ld + t * ld + j] = v;
+    idx[(int64_t)blockIdx.y * m * ld + t * ld + j] = window_col(win, m, start_pos, t, j);
 }
 
-// idx[b, t, col0 + j] = offset + j for j < V_p, else -1;
-// V_p = min(n_c, (p + 1) / ratio).
+// idx[b, t, col0 + j] for j < K: visible_col.
 __global__ __launch_bounds__(IDX_THREADS) void visible_idx_kernel(int64_t m, int64_t start_pos, int ratio,
                                                                   int64_t n_c, int K, int32_t offset,
                                                                   int32_t* __restrict__ idx, int64_t ld,
@@ -59,10 +53,7 @@ __global__ __launch_bounds__(IDX_THREADS) void visible_idx_kernel(int64_t m, int
     const int64_t t = gid / K;
     const int j = (int)(gid - t * K);
     if (t >= m) return;
-    const int64_t p = start_pos + t;
-    int64_t v = (p + 1) / ratio;
-    v = v < n_c ? v : n_c;
-    idx[(int64_t)blockIdx.y * m * ld + t * ld + col0 + j] = (j < v) ? (int32_t)(offset + j) : -1;
+    idx[(int64_t)blockIdx.y * m * ld + t * ld + col0 + j] = visible_col(start_pos, ratio, n_c, offset, t, j);
 }
 
 }  // namespace

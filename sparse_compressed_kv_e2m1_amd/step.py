@@ -45,19 +45,32 @@ def uses_decode_step(w, kcache: str, latent: str = "bf16", B: int = 1) -> bool:
             and 33 <= w.H <= 64 and B <= 64 and w.n_c <= 32768 and w.T <= 4096)
 
 
-def step_call_names(w, kcache: str, latent: str = "bf16", B: int = 1, decode_launch: str = "separate") -> list:
+def uses_prefill_prepare(w, prepare: str = "one") -> bool:
+    """A step that is not a decode step sets up with the one-launch
+    sckv_prefill_prepare (unless asked for the separate calls)."""
+    return prepare == "one" and not (w.start_pos > 0 and w.m == 1)
+
+
+def step_call_names(w, kcache: str, latent: str = "bf16", B: int = 1, decode_launch: str = "separate",
+                    prepare: str = "one") -> list:
     """Names of a step's library calls, in order (the names PathState.calls
     gives them)."""
     if decode_launch == "one" and uses_decode_step(w, kcache, latent, B):
         return ["decode_step"]
+    one = uses_prefill_prepare(w, prepare)
     if uses_decode_prepare(w, kcache):
         names = ["decode_prepare"]
+    elif one:
+        names = ["prefill_prepare"]
     else:
         names = ["quant_latent"] + (["quant_index_k"] if w.Hi else [])
         names += (["ring_write"] if (w.start_pos > 0 and w.m == 1) else []) + ["window_idx"]
-    names += ["index_scores_topk"] if w.Hi else ["visible_idx"]
+    if w.Hi:
+        names += ["index_scores_topk"]
+    elif not one:
+        names += ["visible_idx"]
     names += ["sparse_attn_sink"]
-    if not (w.start_pos > 0 and w.m == 1):
+    if w.start_pos > 0 and w.m > 1 or (w.start_pos == 0 and not one):
         names += ["ring_write"]
     return names
 
@@ -68,7 +81,7 @@ class PathState:
     rows that existed before this step; step() runs the hot path."""
 
     def __init__(self, w, inputs: dict, B: int = 1, device="cuda", kcache: str = "bf16", latent: str = "bf16",
-                 decode_launch: str = "separate"):
+                 decode_launch: str = "separate", prepare: str = "one"):
         """kcache: "bf16" keeps the indexer k cache as round-tripped bf16 rows
         (the pages' layout); "fp4" keeps it packed (4-bit codes + one E8M0 byte
         per 32 values) and scores it on the scaled fp4 matrix cores.
@@ -79,13 +92,20 @@ class PathState:
         decode_launch: "separate" (default) runs a decode step as its separate
         calls; "one" runs a small-batch decode step as the one cooperative
         launch sckv_decode_step when its shapes allow (the same results; on
-        MI355X its grid barriers cost more than the launch gaps they remove)."""
+        MI355X its grid barriers cost more than the launch gaps they remove).
+        prepare: "one" (default) sets up a step that is not a decode step
+        (the new rows' round trips, the index columns that need no scores and
+        a fresh step's ring write) with the one launch sckv_prefill_prepare;
+        "separate" runs those as their separate calls (the same results)."""
         if kcache not in ("bf16", "fp4"):
             raise ValueError(kcache)
         if latent not in ("bf16", "fp4") or (latent == "fp4" and w.D != 512):
             raise ValueError(f"latent={latent} (packed latent rows need D = 512)")
         if decode_launch not in ("one", "separate"):
             raise ValueError(decode_launch)
+        if prepare not in ("one", "separate"):
+            raise ValueError(prepare)
+        self.prepare = prepare
         self.w, self.B, self.device, self.kcache, self.latent_fmt = w, B, device, kcache, latent
         self.decode_launch = decode_launch
         dev = lambda t: t.to(device).contiguous()  # noqa: E731
@@ -207,6 +227,29 @@ class PathState:
                 sk.sckv_quant_pack(self.ik_new[b], Di, self.ik_codes[b, f], Di // 2, self.ik_scales[b, f], Di // 32,
                                    self.n_new, Di, sk.SCKV_FP4_E8M0_B32)
 
+    def _prefill_prepare(self):
+        """Step 1, step 3, step 4 without an indexer and, from position 0,
+        step 6 of the module doc in one launch."""
+        w, B = self.w, self.B
+        m, win, D, Di = w.m, w.win, w.D, w.Di
+        f, nn = self.first_new, self.n_new
+        pk = self.latent_fmt == "fp4"
+        kp = bool(w.Hi) and self.kcache == "fp4"
+        kb = bool(w.Hi) and self.kcache != "fp4"
+        fresh = self.mode == "fresh"
+        sk.sckv_prefill_prepare(
+            B, m, w.start_pos, win, D, nn, self.latent_new if nn else None, nn * D,
+            self.latent[:, f] if (nn and not pk) else None, w.n_c * D,
+            self.lat_codes[:, f] if (nn and pk) else None, w.n_c * D // 2,
+            self.lat_scales[:, f] if (nn and pk) else None, w.n_c * D // 16,
+            self.rope_table, w.rope_dim, f * w.ratio, w.ratio,
+            self.ik_new if (nn and w.Hi) else None, nn * Di, Di,
+            self.ik[:, f] if (nn and kb) else None, w.n_c * Di,
+            self.ik_codes[:, f] if (nn and kp) else None, w.n_c * Di // 2,
+            self.ik_scales[:, f] if (nn and kp) else None, w.n_c * Di // 32,
+            self.rows_a if fresh else None, m * D, self.ring if fresh else None, win * D,
+            self.idx, self.T, w.ratio, w.n_c, 0 if w.Hi else w.K, self.ra)
+
     def calls(self):
         """The step's library calls in order, as (name, thunk) pairs."""
         w, B = self.w, self.B
@@ -237,6 +280,8 @@ class PathState:
                 self.lat_codes[:, f] if (new and pk) else None, w.n_c * D // 2,
                 self.lat_scales[:, f] if (new and pk) else None, w.n_c * D // 16))]
             return out + self._score_and_attend_calls()
+        if uses_prefill_prepare(w, self.prepare):
+            return [("prefill_prepare", self._prefill_prepare)] + self._score_and_attend_calls()
         out = [("quant_latent", lambda: self._quant_new(self.latent_new, self.latent, D, sk.SCKV_FP4_E4M3_B16))]
         if w.Hi and self.kcache == "fp4":
             out.append(("quant_index_k", self._pack_new_k))
@@ -261,7 +306,7 @@ class PathState:
             out.append(("index_scores_topk", lambda: sk.sckv_index_scores_topk(
                 self.iq, self.ik, self.iw, B, m, w.Hi, w.Di, w.n_c, w.ratio, w.start_pos, w.K, self.ra, self.idx,
                 self.T, win, ws=self.ws_index)))
-        else:
+        elif not uses_prefill_prepare(w, self.prepare):
             out.append(("visible_idx", lambda: sk.sckv_visible_idx(B, m, w.start_pos, w.ratio, w.n_c, w.K, self.ra,
                                                                    self.idx, self.T, win)))
         if self.latent_fmt == "fp4":
@@ -272,7 +317,7 @@ class PathState:
             out.append(("sparse_attn_sink", lambda: sk.sckv_sparse_attn_sink(
                 self.q, self.rows_a, self.ra, self.latent, w.n_c, self.idx, self.T, self.sink, w.scale, B, m, w.H, D,
                 self.out, ws=self.ws_attn)))
-        if self.mode == "fresh":
+        if self.mode == "fresh" and not uses_prefill_prepare(w, self.prepare):
             out.append(("ring_write", lambda: sk.sckv_ring_write(self.rows_a, m * D, self.ring, win * D, B, m,
                                                                  w.start_pos, win, D)))
         elif self.mode == "chunk":
@@ -300,7 +345,7 @@ class PathState:
         if not hasattr(self, "_calls"):
             self._calls = self.calls()
             assert [n for n, _ in self._calls] == step_call_names(self.w, self.kcache, self.latent_fmt, self.B,
-                                                                 self.decode_launch)
+                                                                 self.decode_launch, self.prepare)
         for _, f in self._calls:
             f()
         return self.out

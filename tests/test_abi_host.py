@@ -22,7 +22,7 @@ def test_header_declares_the_calls():
               "sckv_visible_idx", "sckv_index_scores_topk", "sckv_sparse_attn_sink", "sckv_workspace_bytes",
               "sckv_last_error", "sckv_abi_version", "sckv_quant_pack", "sckv_index_scores_topk_fp4",
               "sckv_decode_prepare", "sckv_yarn_freqs_cis", "sckv_rope_quant_rows", "sckv_rope_quant_pack",
-              "sckv_decode_step", "sckv_sparse_attn_sink_fp4"]:
+              "sckv_decode_step", "sckv_sparse_attn_sink_fp4", "sckv_prefill_prepare"]:
         assert n in names
 
 
@@ -177,6 +177,50 @@ def test_error_paths(L):
     assert dp(lat_codes=fake, lat_scales=fake) == sk.SCKV_EINVAL      # packed and bf16 destinations at once
     assert dp(lat_dst=None, lat_codes=fake) == sk.SCKV_EINVAL         # packed codes without scale bytes
     assert dp(lat_dst=None, lat_codes=fake, lat_scales=fake, ld_lat_codes=200) == sk.SCKV_EINVAL  # short stride
+
+    # set-up of a step that is not a decode step: sizes, strides, alignment,
+    # destinations, overlap, the visible-count and rotation checks
+    def pp(**kw):
+        P = lambda v: ctypes.c_void_p(v)  # noqa: E731
+        a = dict(B=1, m=4096, start_pos=0, win=128, D=512, n_new=1024, bs_lat_new=1024 * 512,
+                 bs_lat_dst=1024 * 512, bs_lat_codes=1024 * 256, bs_lat_scales=1024 * 32, n_pos=4096, rope_dim=64,
+                 pos0=0, pos_step=4, bs_k_new=1024 * 128, Di=128, bs_k_dst=0, bs_k_codes=1024 * 64,
+                 bs_k_scales=1024 * 4, bs_ring_src=4096 * 512, bs_ring=128 * 512, ld_idx=640, ratio=4, n_c=1024,
+                 K=0, offset=4096)
+        a.update({k: v for k, v in kw.items() if k in a})
+        ptr = dict(lat_new=P(0x10000000), lat_dst=P(0x20000000), lat_codes=None, lat_scales=None,
+                   rope_table=P(0x30000000), k_new=P(0x40000000), k_dst=None, k_codes=P(0x50000000),
+                   k_scales=P(0x60000000), ring_src=P(0x70000000), ring=P(0x80000000), idx=P(0x90000000))
+        ptr.update({k: v for k, v in kw.items() if k in ptr})
+        return L.sckv_prefill_prepare(
+            a["B"], a["m"], a["start_pos"], a["win"], a["D"], a["n_new"], ptr["lat_new"], a["bs_lat_new"],
+            ptr["lat_dst"], a["bs_lat_dst"], ptr["lat_codes"], a["bs_lat_codes"], ptr["lat_scales"],
+            a["bs_lat_scales"], ptr["rope_table"], a["n_pos"], a["rope_dim"], a["pos0"], a["pos_step"], ptr["k_new"],
+            a["bs_k_new"], a["Di"], ptr["k_dst"], a["bs_k_dst"], ptr["k_codes"], a["bs_k_codes"], ptr["k_scales"],
+            a["bs_k_scales"], ptr["ring_src"], a["bs_ring_src"], ptr["ring"], a["bs_ring"], ptr["idx"], a["ld_idx"],
+            a["ratio"], a["n_c"], a["K"], a["offset"], None)
+
+    assert pp(B=0) == sk.SCKV_OK                                  # nothing to do (valid arguments)
+    assert pp(D=520) == sk.SCKV_EINVAL                            # not a multiple of 16
+    assert pp(Di=100) == sk.SCKV_EINVAL                           # not a multiple of 32
+    assert pp(idx=None) == sk.SCKV_EINVAL
+    assert pp(ld_idx=100) == sk.SCKV_EINVAL                       # shorter than win + K
+    assert pp(lat_dst=None) == sk.SCKV_EINVAL                     # no latent destination
+    assert pp(lat_codes=ctypes.c_void_p(0xA0000000), lat_scales=ctypes.c_void_p(0xB0000000)) == sk.SCKV_EINVAL
+    assert pp(k_codes=None) == sk.SCKV_EINVAL                     # scale bytes without codes
+    assert pp(bs_lat_dst=1000) == sk.SCKV_EINVAL                  # batch stride shorter than the rows
+    assert pp(lat_new=ctypes.c_void_p(0x10000008)) == sk.SCKV_EINVAL  # not 16-byte aligned
+    assert pp(lat_dst=ctypes.c_void_p(0x10000100)) == sk.SCKV_EINVAL  # overlaps its source
+    assert pp(k_codes=ctypes.c_void_p(0x40000100)) == sk.SCKV_EINVAL  # overlaps its source
+    assert pp(rope_dim=63) == sk.SCKV_EINVAL                      # odd rotation width
+    assert pp(pos0=4, n_pos=4096) == sk.SCKV_EINVAL               # last row at 4 + 1023 * 4 = 4096: outside
+    assert pp(rope_table=ctypes.c_void_p(0x30000004)) == sk.SCKV_EINVAL  # table not 8-byte aligned
+    assert pp(K=400, ld_idx=528) == sk.SCKV_EINVAL                # fewer columns than visible rows (1024)
+    assert pp(ring=None) == sk.SCKV_EINVAL                        # a ring source without a ring
+    assert pp(bs_ring=1000) == sk.SCKV_EINVAL                     # shorter than win * D
+    assert pp(ring=ctypes.c_void_p(0x70000100)) == sk.SCKV_EINVAL  # rows and ring overlap
+    assert pp(B=70000) == sk.SCKV_EUNSUPPORTED
+    assert pp(start_pos=-1) == sk.SCKV_EINVAL
 
     def rq(**kw):
         a = dict(ldx=512, ldy=512, rows=4, cols=512, n_pos=100, rope_dim=64, pos0=0, pos_step=4)

@@ -353,6 +353,106 @@ def test_decode_prepare_bit_exact(sk, B, D, Di, win, start_pos, new, rope_dim, p
         assert np.array_equal(got_idx[b, :, :win], want_idx) and np.all(got_idx[b, :, win:] == 77)
 
 
+PREFILL_PREPARE_CASES = [
+    # B, m, start_pos, win, D, Di, n_new, rope_dim, lat_packed, k (None / "bf16" / "fp4"), K, ring
+    (1, 4096, 0, 128, 512, 128, 1024, 64, False, "fp4", 0, True),      # causal prefill, packed k cache
+    (1, 2048, 63488, 128, 512, 0, 16, 64, False, None, 512, False),    # chunked prefill, no indexer
+    (2, 300, 0, 16, 64, 32, 75, 8, True, "bf16", 0, True),             # packed latent, bf16 k, m > win
+    (3, 7, 60, 8, 64, 64, 2, 0, False, "fp4", 0, False),               # no rotation table, a chunk
+    (2, 20, 0, 6, 32, 32, 5, 32, True, None, 8, True),                 # win % 4 != 0: one column a lane
+    (2, 5, 0, 8, 64, 32, 0, 8, False, "fp4", 0, True),                 # no completed group yet
+    (1, 1, 0, 4, 64, 32, 0, 8, False, "bf16", 0, True),                # one query from position 0
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_PREPARE_CASES,
+                         ids=lambda c: "B{}m{}sp{}win{}D{}Di{}new{}".format(*c[:7]))
+def test_prefill_prepare_bit_exact(sk, case):
+    """The one-launch set-up of a step against the oracle: the new latent
+    rows turned at j * ratio and round-tripped (bf16 or packed), the new k
+    rows round-tripped (bf16) or packed, the window and visible columns, the
+    ring write of a step from position 0; nothing else in the buffers
+    changes."""
+    B, m, sp, win, D, Di, n_new, rd, lat_packed, kfmt, K, with_ring = case
+    ratio = 4 if sp == 0 else 128
+    n_c = (sp + m) // ratio if K else n_new + 3
+    f = n_c - n_new  # first new cache row
+    rng = np.random.default_rng(m * 7 + sp)
+    lat_new = bits(bf16_of(rng.standard_normal((B, n_new, D))))
+    latent = rng.integers(0, 65535, size=(B, n_c, D)).astype(np.uint16)
+    lc = rng.integers(0, 255, size=(B, n_c, D // 2)).astype(np.uint8)
+    ls = rng.integers(0, 255, size=(B, n_c, D // 16)).astype(np.uint8)
+    pos0 = f * ratio
+    table = oracle.yarn_freqs_cis(rd, pos0 + max(n_new, 1) * ratio, 4096, 10000.0, 40.0, 32.0, 1.0) if rd else None
+    lat_d, lc_d, ls_d = from_bits(latent, "cuda"), torch.from_numpy(lc).cuda(), torch.from_numpy(ls).cuda()
+    kw = {}
+    if kfmt:
+        k_new = bits(bf16_of(rng.standard_normal((B, n_new, Di))))
+        ik = rng.integers(0, 65535, size=(B, n_c, Di)).astype(np.uint16)
+        kc = rng.integers(0, 255, size=(B, n_c, Di // 2)).astype(np.uint8)
+        ks = rng.integers(0, 255, size=(B, n_c, Di // 32)).astype(np.uint8)
+        ik_d, kc_d, ks_d = from_bits(ik, "cuda"), torch.from_numpy(kc).cuda(), torch.from_numpy(ks).cuda()
+        kw = dict(k_new=from_bits(k_new, "cuda") if n_new else None, bs_k_new=n_new * Di, Di=Di,
+                  k_dst=ik_d[:, f] if (kfmt == "bf16" and n_new) else None, bs_k_dst=n_c * Di,
+                  k_codes=kc_d[:, f] if (kfmt == "fp4" and n_new) else None, bs_k_codes=n_c * Di // 2,
+                  k_scales=ks_d[:, f] if (kfmt == "fp4" and n_new) else None, bs_k_scales=n_c * Di // 32)
+    else:
+        kw = dict(k_new=None, bs_k_new=0, Di=0, k_dst=None, bs_k_dst=0, k_codes=None, bs_k_codes=0, k_scales=None,
+                  bs_k_scales=0)
+    rows = rng.integers(0, 65535, size=(B, m, D)).astype(np.uint16)
+    ring = rng.integers(0, 65535, size=(B, win, D)).astype(np.uint16)
+    rows_d, ring_d = from_bits(rows, "cuda"), from_bits(ring, "cuda")
+    ld_idx = win + K + 4
+    idx = torch.full((B, m, ld_idx), 77, dtype=torch.int32, device="cuda")
+    off = 2176
+    say(f"prefill prepare {case}")
+    sk.sckv_prefill_prepare(
+        B, m, sp, win, D, n_new, from_bits(lat_new, "cuda") if n_new else None, n_new * D,
+        lat_d[:, f] if (n_new and not lat_packed) else None, n_c * D,
+        lc_d[:, f] if (n_new and lat_packed) else None, n_c * D // 2,
+        ls_d[:, f] if (n_new and lat_packed) else None, n_c * D // 16,
+        torch.from_numpy(table).cuda() if rd else None, rd, pos0, ratio, ring_src=rows_d if with_ring else None,
+        bs_ring_src=m * D, ring=ring_d if with_ring else None, bs_ring=win * D, idx=idx, ld_idx=ld_idx, ratio=ratio,
+        n_c=n_c, K=K, offset=off, **kw)
+    torch.cuda.synchronize()
+    want_lat, want_lc, want_ls = latent.copy(), lc.copy(), ls.copy()
+    positions = [pos0 + j * ratio for j in range(n_new)]
+    for b in range(B):
+        if not n_new:
+            break
+        r = oracle.rope_rows(lat_new[b], rd, table, positions) if rd else lat_new[b]
+        if lat_packed:
+            c, sc = oracle.pack(r.reshape(-1), oracle.E4M3_B16)
+            want_lc[b, f:], want_ls[b, f:] = c.reshape(n_new, D // 2), sc.reshape(n_new, D // 16)
+        else:
+            want_lat[b, f:] = oracle.quant(r.reshape(-1), oracle.E4M3_B16).reshape(n_new, D)
+    assert np.array_equal(bits(lat_d), want_lat)
+    assert np.array_equal(lc_d.cpu().numpy(), want_lc) and np.array_equal(ls_d.cpu().numpy(), want_ls)
+    if kfmt:
+        want_ik, want_kc, want_ks = ik.copy(), kc.copy(), ks.copy()
+        for b in range(B):
+            if not n_new:
+                break
+            if kfmt == "bf16":
+                want_ik[b, f:] = oracle.quant(k_new[b].reshape(-1), oracle.E8M0_B32).reshape(n_new, Di)
+            else:
+                c, sc = oracle.pack(k_new[b].reshape(-1), oracle.E8M0_B32)
+                want_kc[b, f:], want_ks[b, f:] = c.reshape(n_new, Di // 2), sc.reshape(n_new, Di // 32)
+        assert np.array_equal(bits(ik_d), want_ik)
+        assert np.array_equal(kc_d.cpu().numpy(), want_kc) and np.array_equal(ks_d.cpu().numpy(), want_ks)
+    got_ring = bits(ring_d)
+    for b in range(B):
+        assert np.array_equal(got_ring[b], oracle.ring_write(ring[b], rows[b], sp) if with_ring else ring[b])
+    assert np.array_equal(bits(rows_d), rows)
+    want_w, _ = oracle.window_idx(win, m, sp)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert np.array_equal(got[b, :, :win], want_w)
+        if K:
+            assert np.array_equal(got[b, :, win:win + K], oracle.visible_idx(m, sp, ratio, n_c, K, off))
+        assert np.all(got[b, :, win + K:] == 77)
+
+
 # --------------------------------------------------------------------- indexer
 
 INDEXER_CASES = [
@@ -958,6 +1058,43 @@ def test_step_graph_replays_match_eager(sk, name, B):
         torch.cuda.synchronize()
     del graph, st, x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name,B,kcache,latent", [("causal_prefill", 1, "fp4", "bf16"),
+                                                  ("causal_prefill", 2, "bf16", "fp4"),
+                                                  ("chunked_prefill", 2, "bf16", "bf16"),
+                                                  ("chunked_prefill", 1, "bf16", "fp4")])
+def test_step_prefill_prepare_matches_separate_calls(sk, name, B, kcache, latent):
+    """A step set up by the one launch sckv_prefill_prepare against the same
+    step set up by its separate calls, from the same inputs: index lists,
+    outputs, caches and the ring (or the [ring | chunk] buffer) bit for bit."""
+    from sparse_compressed_kv_e2m1_amd.step import PathState, step_call_names
+
+    w = synth.WORKLOADS[name]
+    assert step_call_names(w, kcache, latent, B)[0] == "prefill_prepare"
+    assert "prefill_prepare" not in step_call_names(w, kcache, latent, B, prepare="separate")
+    res = {}
+    for mode in ("one", "separate"):
+        say(f"prefill prepare step {name} B={B} ({kcache} k, {latent} latent): prepare={mode}")
+        # the same seeded draw for both (the step writes its caches in place)
+        x = synth.make_inputs(w, B, device="cuda")
+        st = PathState(w, x, B, kcache=kcache, latent=latent, prepare=mode)
+        st.setup()
+        st.step()
+        torch.cuda.synchronize()
+        bufs = {"idx": st.idx, "out": st.out.view(torch.int16), "rows_a": st.rows_a.view(torch.int16)}
+        if hasattr(st, "ring"):  # (a chunk's ring is the front of rows_a)
+            bufs["ring"] = st.ring.view(torch.int16)
+        bufs.update({"lat_codes": st.lat_codes, "lat_scales": st.lat_scales} if latent == "fp4" else
+                    {"latent": st.latent.view(torch.int16)})
+        if w.Hi:
+            bufs.update({"ik_codes": st.ik_codes, "ik_scales": st.ik_scales} if kcache == "fp4" else
+                        {"ik": st.ik.view(torch.int16)})
+        res[mode] = {k: v.cpu() for k, v in bufs.items()}
+        del st, x, bufs
+        torch.cuda.empty_cache()
+    for k in res["one"]:
+        assert torch.equal(res["one"][k], res["separate"][k]), (name, B, k)
 
 
 DSTEP_CASES = [("decode", 1, True), ("decode", 3, True), ("decode", 13, True), ("decode", 64, True),
