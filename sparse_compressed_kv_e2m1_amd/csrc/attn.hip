@@ -142,9 +142,6 @@ int launch_attn_d(const uint16_t* q, const uint16_t* rows_a, int64_t ra, const u
     if (H <= 16 || hgroups > 1)
         return launch_attn_c<D, 1, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
                                        out, part_o, part_ml, s, rb_scales, hgroups);
-    if (H <= 16)
-        return launch_attn_c<D, 1, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
-                                       out, part_o, part_ml, s, rb_scales);
     if (H <= 32)
         return launch_attn_c<D, 2, PK>(q, rows_a, ra, rows_b, rb, idx, T, sink, scale_log2, nq, m, H, cps, nsplit,
                                        out, part_o, part_ml, s, rb_scales);
