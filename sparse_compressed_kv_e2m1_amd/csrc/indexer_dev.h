@@ -139,6 +139,66 @@ __device__ __forceinline__ uint32_t block_max(uint32_t x, uint32_t* buf) {
     return t;
 }
 
+// The ordered compaction that ends a selection: of thread t's rows s0 ..
+// s0 + KPT - 1, those with key > tau and, over the block, the first need_eq
+// rows (lowest first) with key == tau, written in ascending row order to
+// dst[0 .. K).  The thread's matches are kept as bit masks; one block scan of
+// its two counts packed in one word (greater in the high half, equal in the
+// low half: with at most 2^15 keys a block the halves cannot carry) gives
+// both prefix counts, and the thread then walks only its selected bits.
+template <int KPT, int NWAVES>
+__device__ __forceinline__ void compact_selected(const uint32_t (&key)[KPT], uint32_t tau, uint32_t need_eq,
+                                                 int64_t s0, int K, int32_t offset, int32_t* __restrict__ dst,
+                                                 uint32_t* tot) {
+    constexpr int NM = (KPT + 31) / 32;
+    uint32_t gtm[NM], eqm[NM];
+#pragma unroll
+    for (int i = 0; i < NM; ++i) gtm[i] = eqm[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+        gtm[j / 32] |= (key[j] > tau ? 1u : 0u) << (j % 32);
+        eqm[j / 32] |= (key[j] == tau ? 1u : 0u) << (j % 32);
+    }
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        gt += (uint32_t)__builtin_popcount(gtm[i]);
+        eq += (uint32_t)__builtin_popcount(eqm[i]);
+    }
+    uint32_t eq_before, pos;
+    if constexpr (KPT * NWAVES * 64 <= 32768) {
+        const uint32_t before = block_excl_scan<NWAVES>((gt << 16) | eq, tot);
+        eq_before = before & 0xffffu;
+        pos = (before >> 16) + (need_eq < eq_before ? need_eq : eq_before);
+    } else {  // (more keys than the packed halves hold: two scans)
+        eq_before = block_excl_scan<NWAVES>(eq, tot);
+        const uint32_t t = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
+        pos = block_excl_scan<NWAVES>(gt + (t < eq ? t : eq), tot);
+    }
+    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;  // this thread's equal keys to take
+    take_eq = take_eq < eq ? take_eq : eq;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        uint32_t e = eqm[i];
+        while (take_eq > 0u && e != 0u) {  // the lowest equal rows first
+            const uint32_t low = e & (0u - e);
+            gtm[i] |= low;
+            e ^= low;
+            --take_eq;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        uint32_t sel = gtm[i];
+        while (sel != 0u) {
+            const int j = __builtin_ctz(sel);
+            sel &= sel - 1u;
+            if (pos < (uint32_t)K) dst[pos] = (int32_t)(offset + s0 + 32 * i + j);
+            ++pos;
+        }
+    }
+}
+
 // Top-K of the keys held by the block: thread t owns key[0..KPT) of rows
 // s0 .. s0+KPT-1 (rows at or past the visible count hold key 0).  Writes
 // offset + s of the K selected rows in ascending s to out[0..K).  Needs
@@ -208,28 +268,8 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[KPT], int64_t 
     uint32_t lo_bin, above_lo;
     find_bin(hist, (uint32_t)K - above, lo_bin, above_lo);
     const uint32_t tau = (h << 8) | lo_bin;
-    uint32_t eq = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) eq += key[j] == tau;
     const uint32_t need_eq = (uint32_t)K - (above + above_lo);  // keys == tau to take, >= 1
-    const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
-    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
-    take_eq = take_eq < eq ? take_eq : eq;
-    uint32_t gt = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) gt += key[j] > tau;
-    uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
-    uint32_t eq_seen = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const uint32_t k = key[j];
-        bool take = k > tau;
-        if (k == tau) {
-            take = eq_seen < take_eq;
-            ++eq_seen;
-        }
-        if (take && pos < (uint32_t)K) out[pos++] = (int32_t)(offset + s0 + j);
-    }
+    compact_selected<KPT, NWAVES>(key, tau, need_eq, s0, K, offset, out, tot);
 }
 
 // topk_select with the keys packed two to a register (key 2i in the low half
@@ -309,29 +349,8 @@ __device__ __forceinline__ void topk_select_hist(const uint32_t (&key)[KPT], int
     uint32_t lo_bin, above_lo;
     find_bin(hist + 256, (uint32_t)K - above_hi, lo_bin, above_lo);
     const uint32_t tau = (hi_bin << 8) | lo_bin;
-    uint32_t gt = 0, eq = 0;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        gt += key[j] > tau;
-        eq += key[j] == tau;
-    }
     const uint32_t need_eq = (uint32_t)K - (above_hi + above_lo);  // keys == tau to take, >= 1
-    const uint32_t eq_before = block_excl_scan<NWAVES>(eq, tot);
-    uint32_t take_eq = (need_eq > eq_before) ? (need_eq - eq_before) : 0u;
-    take_eq = take_eq < eq ? take_eq : eq;
-    uint32_t pos = block_excl_scan<NWAVES>(gt + take_eq, tot);
-    uint32_t eq_seen = 0;
-    int32_t* dst = stage ? stage : out;
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-        const uint32_t k = key[j];
-        bool take = k > tau;
-        if (k == tau) {
-            take = eq_seen < take_eq;
-            ++eq_seen;
-        }
-        if (take && pos < (uint32_t)K) dst[pos++] = (int32_t)(offset + s0 + j);
-    }
+    compact_selected<KPT, NWAVES>(key, tau, need_eq, s0, K, offset, stage ? stage : out, tot);
     if (stage) {
         __syncthreads();
         for (int i = threadIdx.x; i < K; i += NWAVES * 64) out[i] = stage[i];
