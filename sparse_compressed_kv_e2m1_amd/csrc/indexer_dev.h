@@ -32,9 +32,10 @@ __device__ __forceinline__ uint32_t score_key(uint32_t b) {
 // (its high byte) and an LDS histogram (its low byte; topk_select), or bit by
 // bit in 16 rounds of counts (keys two to a register, topk_select_packed);
 // then the rows with key > tau and the first (K - #greater) rows with key ==
-// tau (lowest rows first) are written in ascending row order with two block
-// prefix sums.  Missing rows hold key 0, below every real key (finite scores
-// have keys >= 0x007f).
+// tau (lowest rows first) are written in ascending row order after block
+// prefix sums of the two counts (compact_selected; the bit-by-bit form keeps
+// its own compaction).  Missing rows hold key 0, below every real key (finite
+// scores have keys >= 0x007f).
 
 // DPP helpers (no LDS round trip).  update_dpp(old, src, ctrl, row_mask,
 // bank_mask, bound_ctrl): lanes outside row_mask keep `old`.
