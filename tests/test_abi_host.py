@@ -319,3 +319,39 @@ def test_decode_step_host_checks(L):
     assert ds(ws_bytes=100) == sk.SCKV_EWORKSPACE
     assert ds(B=0) == sk.SCKV_OK
     assert sk.sckv_decode_step_workspace_bytes(1, 64, 512, 8192, 640) >= 8192 * 2
+
+
+def test_step_call_composition():
+    """The calls a step is made of (host logic only): decode steps set up with
+    sckv_decode_prepare (packed k cache) or the separate calls; every other
+    step with sckv_prefill_prepare, or its separate calls when asked; a
+    chunk's ring write follows its attention.  The one-launch set-up's
+    algorithmic bytes are those of the calls it replaces."""
+    import importlib.util
+
+    import sckv_synth as synth
+    from sparse_compressed_kv_e2m1_amd.step import step_call_names
+
+    W = synth.WORKLOADS
+    assert step_call_names(W["decode"], "fp4") == ["decode_prepare", "index_scores_topk", "sparse_attn_sink"]
+    assert step_call_names(W["decode"], "bf16") == ["quant_latent", "quant_index_k", "ring_write", "window_idx",
+                                                    "index_scores_topk", "sparse_attn_sink"]
+    assert step_call_names(W["causal_prefill"], "fp4") == ["prefill_prepare", "index_scores_topk",
+                                                           "sparse_attn_sink"]
+    assert step_call_names(W["causal_prefill"], "fp4", prepare="separate") == [
+        "quant_latent", "quant_index_k", "window_idx", "index_scores_topk", "sparse_attn_sink", "ring_write"]
+    assert step_call_names(W["chunked_prefill"], "bf16") == ["prefill_prepare", "sparse_attn_sink", "ring_write"]
+    assert step_call_names(W["chunked_prefill"], "bf16", prepare="separate") == [
+        "quant_latent", "window_idx", "visible_idx", "sparse_attn_sink", "ring_write"]
+
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    for name, kc in (("causal_prefill", "fp4"), ("chunked_prefill", "bf16")):
+        w = W[name]
+        parts = [c for c in step_call_names(w, kc, prepare="separate") if c not in ("index_scores_topk",
+                                                                                    "sparse_attn_sink")]
+        if w.start_pos > 0:
+            parts.remove("ring_write")  # a chunk's ring write stays a call of its own
+        assert bench.counts(w, 1, "prefill_prepare", kc)["bytes"] == sum(bench.counts(w, 1, c, kc)["bytes"]
+                                                                       for c in parts)
