@@ -34,7 +34,7 @@ extern "C" {
 enum sckv_status {
     SCKV_OK = 0,
     SCKV_EINVAL = -1,       /* bad shape, null pointer, bad mode, misaligned pointer */
-    SCKV_EUNSUPPORTED = -2, /* a valid shape this build has no kernel for (see each call) */
+    SCKV_EUNSUPPORTED = -2, /* a valid shape the library has no kernel for (see each call) */
     SCKV_EHIP = -3,         /* the HIP runtime refused a launch */
     SCKV_EWORKSPACE = -4    /* workspace pointer NULL or smaller than sckv_workspace_bytes() */
 };
