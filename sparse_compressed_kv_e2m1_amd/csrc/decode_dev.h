@@ -59,20 +59,34 @@ __device__ __forceinline__ float group_max(float v, int lanes) {
 // sckv_quant_pack.
 __device__ __forceinline__ void decode_prepare_body(const PrepArgs& a, const int64_t b) {
     const int t = threadIdx.x;
+    const uint32_t* lsrc = a.lat_new ? reinterpret_cast<const uint32_t*>(a.lat_new + b * a.ld_lat_new) : nullptr;
+    const int rope_first = (a.D - a.rope_dim) / 2;  // first pair of the rope slice
+    const float2* rt = (a.lat_new && a.rope_table)
+                           ? reinterpret_cast<const float2*>(a.rope_table) + a.lat_pos * (a.rope_dim / 2)
+                           : nullptr;
+    const uint32_t* ksrc = a.k_new ? reinterpret_cast<const uint32_t*>(a.k_new + b * a.ld_k_new) : nullptr;
+    const uint4* kvsrc = reinterpret_cast<const uint4*>(a.kv_new + b * a.ld_kv_new);
+    // the loads of every part's first pass come first, at addresses clamped
+    // into their rows (no per-lane branches), so that their latencies overlap
+    // instead of following one another part by part
+    uint32_t lat0 = 0u, k0 = 0u;
+    float2 cs0 = make_float2(1.0f, 0.0f);
+    {
+        const int tl = t < a.D / 2 ? t : a.D / 2 - 1;
+        int tr = t - rope_first;
+        tr = tr < 0 ? 0 : (tr < a.rope_dim / 2 ? tr : a.rope_dim / 2 - 1);
+        if (lsrc) lat0 = lsrc[tl];
+        if (rt) cs0 = rt[tr];
+        if (ksrc) k0 = ksrc[t < a.Di / 2 ? t : a.Di / 2 - 1];
+    }
+    const uint4 kv0 = kvsrc[t < a.D / 8 ? t : a.D / 8 - 1];
+
     // latent row: values 2p, 2p + 1 in lane p (E4M3_B16 round trip, bf16 out)
-    if (a.lat_new) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.lat_new + b * a.ld_lat_new);
+    if (lsrc) {
         uint32_t* dst = a.lat_dst ? reinterpret_cast<uint32_t*>(a.lat_dst + b * a.ld_lat_dst) : nullptr;
-        const int rope_first = (a.D - a.rope_dim) / 2;  // first pair of the rope slice
-        const float2* rt = a.rope_table ? reinterpret_cast<const float2*>(a.rope_table) + a.lat_pos * (a.rope_dim / 2)
-                                        : nullptr;
-        for (int p = t; p < a.D / 2; p += PREP_THREADS) {
-            uint32_t w = src[p];
-            if (rt && p >= rope_first) {
-                // the rotary turn of pair p before the round trip (sckv_rope_quant_rows)
-                const float2 cs = rt[p - rope_first];
-                w = rope_pair_bits(w, cs.x, cs.y);
-            }
+        auto pair = [&](int p, uint32_t w, float2 cs) {
+            // the rotary turn of pair p before the round trip (sckv_rope_quant_rows)
+            if (rt && p >= rope_first) w = rope_pair_bits(w, cs.x, cs.y);
             const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
             const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 8);
             const float s = block_scale<SCKV_FP4_E4M3_B16>(amax);
@@ -86,16 +100,18 @@ __device__ __forceinline__ void decode_prepare_body(const PrepArgs& a, const int
             } else {
                 dst[p] = fp4_value<SCKV_FP4_E4M3_B16>(lo, s, 0.0f) | (fp4_value<SCKV_FP4_E4M3_B16>(hi, s, 0.0f) << 16);
             }
-        }
+        };
+        // (a block's 8 lanes are all below D / 2 or all past it: D % 16 == 0)
+        if (t < a.D / 2) pair(t, lat0, cs0);
+        for (int p = t + PREP_THREADS; p < a.D / 2; p += PREP_THREADS)
+            pair(p, lsrc[p], (rt && p >= rope_first) ? rt[p - rope_first] : make_float2(1.0f, 0.0f));
     }
     // indexer k row: values 2p, 2p + 1 in lane p (E8M0_B32, packed: one code
     // byte a lane, the scale byte from the block's first lane)
-    if (a.k_new) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.k_new + b * a.ld_k_new);
+    if (ksrc) {
         uint8_t* codes = a.k_codes + b * a.ld_codes;
         uint8_t* scales = a.k_scales + b * a.ld_scales;
-        for (int p = t; p < a.Di / 2; p += PREP_THREADS) {
-            const uint32_t w = src[p];
+        auto pair = [&](int p, uint32_t w) {
             const float lo = bf16_bits_to_f32(w & 0xffffu), hi = bf16_bits_to_f32(w >> 16);
             const float amax = group_max(fmaxf(fabsf(lo), fabsf(hi)), 16);
             const float s = block_scale<SCKV_FP4_E8M0_B32>(amax);
@@ -104,13 +120,16 @@ __device__ __forceinline__ void decode_prepare_body(const PrepArgs& a, const int
             const uint32_t chi = e2m1_code(e2m1_round_mag(fminf(fabsf(hi) * inv_s, 6.0f)), hi);
             codes[p] = (uint8_t)(clo | (chi << 4));
             if ((p & 15) == 0) scales[p / 16] = (uint8_t)scale_byte<SCKV_FP4_E8M0_B32>(s);
-        }
+        };
+        // (a block's 16 lanes are all below Di / 2 or all past it: Di % 32 == 0)
+        if (t < a.Di / 2) pair(t, k0);
+        for (int p = t + PREP_THREADS; p < a.Di / 2; p += PREP_THREADS) pair(p, ksrc[p]);
     }
     // the new kv row into ring slot start_pos mod win
     {
-        const uint4* src = reinterpret_cast<const uint4*>(a.kv_new + b * a.ld_kv_new);
         uint4* dst = reinterpret_cast<uint4*>(a.ring + b * a.ld_ring + (a.start_pos % a.win) * a.D);
-        for (int i = t; i < a.D / 8; i += PREP_THREADS) dst[i] = src[i];
+        if (t < a.D / 8) dst[t] = kv0;
+        for (int i = t + PREP_THREADS; i < a.D / 8; i += PREP_THREADS) dst[i] = kvsrc[i];
     }
     // window columns of the query at p = start_pos: the n_w = min(win, p + 1)
     // newest positions, oldest first, then -1
