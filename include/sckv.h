@@ -310,8 +310,8 @@ int sckv_prefill_prepare(int B, int64_t m, int64_t start_pos, int win, int D, in
  * callers that need a step as a single launch: on MI355X each grid barrier
  * (device-scope atomics across the eight XCDs' L2s) costs a few microseconds,
  * more than the launch gaps of the separate calls, so those are faster at
- * every batch size measured (B = 1: 73 against 35 us at n_c = 8192, the
- * separate calls replayed from a HIP graph).
+ * every batch size measured (B = 1 at n_c = 8192: 69 us launched, 74 us
+ * replayed from a HIP graph, against 44 and 30 us for the separate calls).
  *   lat_new, k_new  [B] new raw latent rows (D bf16) and raw indexer k rows (Di
  *                   bf16), contiguous, or both NULL when no compressed row
  *                   completes at this step (else (start_pos+1) % ratio == 0 and

@@ -873,7 +873,7 @@ size_t attn_partials_bytes(int64_t nq, int nsplit, int H, int D) {
 // of at least 2 (one per set), so that a query's work spreads over about 256
 // workgroups with short chains of dependent copies.  hgroups = 1 when no split
 // is needed.
-void attn_split_groups(int64_t nq, int T, int H, int* chunks_per_split, int* nsplit, int* hgroups) {
+inline void attn_split_groups(int64_t nq, int T, int H, int* chunks_per_split, int* nsplit, int* hgroups) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int64_t want = (256 + nq - 1) / nq;  // workgroups per query
     // (from two to three workgroups a query the 64-head split is faster:

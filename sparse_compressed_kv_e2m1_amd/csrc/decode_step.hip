@@ -23,6 +23,7 @@
 // gridDim.x, ...; the grid is at most one workgroup per compute unit, all
 // resident (cooperative launch), so every barrier is reached by every
 // workgroup.  The barriers are the library's own (grid_barrier below).
+#include <mutex>
 #include <string>
 
 #include "attn_dev.h"
@@ -177,6 +178,52 @@ size_t step_keys_bytes(int B, int64_t n_c) { return align256((size_t)B * (size_t
 
 // One launch of the cooperative kernel with the largest grid the work needs
 // and the device keeps resident.
+constexpr size_t STEP_LDS_MAX = 160 * 1024;  // a compute unit's LDS
+
+// Set-up of the kernel instance on the current device, once per device: the
+// compute-unit count, the cooperative-launch check, the dynamic LDS limit
+// raised to what a compute unit has beside the kernel's static LDS, and the
+// check that one workgroup with that much fits a compute unit (so does every
+// smaller request).  Each call then only reads the cached values.
+template <int KPT>
+int step_device(int& ncu, size_t& lds_max, const char* name) {
+    static std::mutex mu;
+    static int cus[64] = {0};  // 0: not set up; -1: no cooperative launch
+    static size_t dyn[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return fail(SCKV_EHIP, std::string(name) + ": device query failed");
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0, coop = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || n <= 0)
+            return fail(SCKV_EHIP, std::string(name) + ": device query failed");
+        if (!coop) {
+            cus[dev] = -1;
+        } else {
+            const void* fn = (const void*)decode_step_kernel<KPT>;
+            hipFuncAttributes fa;
+            hipError_t e = hipFuncGetAttributes(&fa, fn);
+            if (e != hipSuccess) return fail(SCKV_EHIP, std::string(name) + ": " + hipGetErrorString(e));
+            if (fa.sharedSizeBytes >= STEP_LDS_MAX)
+                return fail(SCKV_EUNSUPPORTED, std::string(name) + ": no LDS left beside the static LDS");
+            const size_t d = STEP_LDS_MAX - fa.sharedSizeBytes;
+            e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)d);
+            if (e != hipSuccess) return fail(SCKV_EHIP, std::string(name) + ": " + hipGetErrorString(e));
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, STEP_THREADS, d);
+            if (e != hipSuccess || per_cu < 1)
+                return fail(SCKV_EUNSUPPORTED, std::string(name) + ": the step's workgroup does not fit a compute unit");
+            cus[dev] = n;
+            dyn[dev] = d;
+        }
+    }
+    if (cus[dev] < 0) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": no cooperative launch on this device");
+    ncu = cus[dev];
+    lds_max = dyn[dev];
+    return SCKV_OK;
+}
+
 template <int KPT>
 int launch_step(StepArgs& a, hipStream_t s, const char* name) {
     using SA = AttnShape<512, 4, STEP_CPS, 2, false>;
@@ -184,17 +231,11 @@ int launch_step(StepArgs& a, hipStream_t s, const char* name) {
     const size_t lds_s = SS::lds_bytes(a.rows_per_wg, false);
     const size_t lds = lds_s > SA::LDS_BYTES ? lds_s : (size_t)SA::LDS_BYTES;
     const void* fn = (const void*)decode_step_kernel<KPT>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return fail(SCKV_EHIP, std::string(name) + ": " + hipGetErrorString(e));
-    int dev = 0, ncu = 0, coop = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess)
-        return fail(SCKV_EHIP, std::string(name) + ": device query failed");
-    if (!coop) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": no cooperative launch on this device");
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, STEP_THREADS, lds);
-    if (e != hipSuccess || per_cu < 1)
-        return fail(SCKV_EUNSUPPORTED, std::string(name) + ": the step's workgroup does not fit a compute unit");
+    int ncu = 0;
+    size_t lds_max = 0;
+    if (const int rc = step_device<KPT>(ncu, lds_max, name)) return rc;
+    if (lds > lds_max) return fail(SCKV_EUNSUPPORTED, std::string(name) + ": the step needs more LDS than a compute unit has");
+    hipError_t e;
     int64_t work = a.B;
     work = work > (int64_t)a.B * a.nsplit_s ? work : (int64_t)a.B * a.nsplit_s;
     work = work > (int64_t)a.B * a.nsplit_a ? work : (int64_t)a.B * a.nsplit_a;
